@@ -1,0 +1,198 @@
+"""Pins for the INT8 quantizer, the witness bound and RoPE (oracle/int8.py,
+oracle/rope.py, oracle/decoder.expected_int8_store).
+
+What pins it:
+* the block scale against exact rational arithmetic rounded to the nearest
+  float32 by brute force (fractions.Fraction), not numpy;
+* each code against a brute-force nearest-integer search with ties to even;
+* the absmax element maps to +-127; all-zero blocks give scale 0 and codes 0;
+* the bound is sound for every token (Cauchy-Schwarz) and exactly tight for
+  adversarial queries aligned band by band with the residual ([WitCert]
+  "频带酉性与双层证书": the bound must hold per query, never on averages);
+* RoPE band unitarity for interleaved pairs, its failure for half-split
+  pairs, and the textbook relative-position property of rotary embeddings;
+* exactly quantizable data (zero residual) reduces INT8 attention to the
+  plain masked attention;
+* the storage format printed on the page (16 bands, 32 B per token-head).
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import attention as att
+from oracle import decoder, int8, rope
+
+
+def nearest_f32(x: Fraction) -> np.float32:
+    """Round an exact rational to the nearest float32, ties to even (brute force)."""
+    f = np.float32(float(x))
+    cands = {f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))}
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - x),
+                                     int(np.array(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def brute_code(x32: np.float32, s: np.float32) -> int:
+    quot = Fraction(float(np.float32(x32 / s)))  # the float32 quotient the method fixes
+    best = min(range(-127, 128), key=lambda c: (abs(quot - c), c & 1))
+    return best
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_block_scale_and_codes_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((16, 8)) * (10.0 ** rng.uniform(-3, 3))).astype(np.float32)
+    if seed == 1:
+        x[3, 5] = np.float32(127.5) * np.float32(0.5)  # exercise ties
+    s, codes = int8.quantize_block(x)
+    a = Fraction(float(np.max(np.abs(x))))
+    assert s == nearest_f32(a / 127)
+    for idx in np.ndindex(x.shape):
+        assert codes[idx] == brute_code(x[idx], s), idx
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert abs(int(codes[i])) == 127
+    err = np.abs(x.astype(np.float64) - int8.dequantize(codes, s))
+    assert np.all(err <= float(s) / 2 * (1 + 2.0 ** -20))
+
+
+def test_zero_block():
+    s, codes = int8.quantize_block(np.zeros((16, 128), dtype=np.float32))
+    assert s == 0 and not codes.any()
+
+
+def test_round_half_even_ties():
+    s = np.float32(1.0)
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, 126.5, -126.5, 127.0], dtype=np.float32)
+    assert list(int8.block_codes(x, s)) == [0, 2, 2, 0, -2, 126, -126, 127]
+
+
+def residuals(rng, n, d):
+    k = rng.standard_normal((n, d))
+    blocks = n // 16
+    s, c = int8.quantize_history(k.astype(np.float32), blocks)
+    khat = np.concatenate([int8.dequantize(c[i * 16:(i + 1) * 16], s[i]) for i in range(blocks)])
+    return k.astype(np.float32).astype(np.float64) - khat
+
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_bound_sound_random_queries(d):
+    rng = np.random.default_rng(d)
+    r = residuals(rng, 64, d)
+    wit = int8.band_norms(r)
+    for _ in range(50):
+        q = rng.standard_normal(d) * rng.uniform(0.1, 10)
+        c = int8.witness_bound(q, wit)
+        e = int8.logit_error(q, r)
+        assert np.all(c >= e * (1 - 1e-12)), "bound must hold for every token"
+
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_bound_tight_for_aligned_queries(d):
+    """q_b = lambda_b * r_b with lambda_b > 0 makes every Cauchy-Schwarz and the
+    triangle inequality tight: c_t equals the true error for that token."""
+    rng = np.random.default_rng(100 + d)
+    r = residuals(rng, 32, d)
+    wit = int8.band_norms(r)
+    for t in range(32):
+        lam = np.repeat(rng.uniform(0.5, 3.0, d // 8), 8)
+        q = lam * r[t]
+        c = int8.witness_bound(q, wit[t:t + 1])[0]
+        e = int8.logit_error(q, r[t:t + 1])[0]
+        assert c == pytest.approx(e, rel=1e-12)
+        # flipping the sign of one band breaks the triangle-inequality tightness
+        q2 = q.copy()
+        q2[:8] *= -1
+        assert int8.witness_bound(q2, wit[t:t + 1])[0] > int8.logit_error(q2, r[t:t + 1])[0] * (1 + 1e-9)
+
+
+def test_band_grouping_is_contiguous():
+    x = np.zeros(128)
+    x[8:16] = 1.0  # band 1 only
+    n = int8.band_norms(x)
+    assert n[1] == pytest.approx(np.sqrt(8)) and np.count_nonzero(n) == 1
+
+
+def test_rope_band_unitarity():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 128))
+    for pos in [0, 1, 17, 4095, 32767, 131071]:
+        y = rope.rope_interleaved(x, pos)
+        np.testing.assert_allclose(int8.band_norms(y), int8.band_norms(x), rtol=0, atol=1e-13)
+    y = rope.rope_half_split(x, 17)
+    assert np.max(np.abs(int8.band_norms(y) - int8.band_norms(x))) > 1e-3
+
+
+def test_rope_is_a_rotation_by_relative_position():
+    """(R_m q) . (R_n k) = (R_{m-n} q) . k, and R_0 is the identity."""
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    np.testing.assert_allclose(rope.rope_interleaved(q, 0), q, atol=0)
+    for m, n in [(5, 2), (300, 17), (9000, 8999)]:
+        lhs = rope.rope_interleaved(q, m) @ rope.rope_interleaved(k, n)
+        rhs = rope.rope_interleaved(q, m - n) @ k
+        assert lhs == pytest.approx(rhs, abs=1e-10)
+
+
+def test_exactly_quantizable_history_reduces_to_plain_attention():
+    """Keys/values that are exact multiples of a power-of-two scale with the
+    block absmax at +-127 quantize with zero residual: INT8 attention must then
+    equal the masked float64 attention, with c = e = 0."""
+    rng = np.random.default_rng(9)
+    n, d, w = 16 * 5 + 7, 128, 48
+    scale = 2.0 ** -5
+    k = rng.integers(-127, 128, (n, d)).astype(np.float64)
+    v = rng.integers(-127, 128, (n, d)).astype(np.float64)
+    k[::16, 0], v[::16, 0] = 127, -127
+    k, v = k * scale, v * scale
+    q = rng.standard_normal(d)
+    res = int8.int8_decode(q, k, v, n, w)
+    ref = att.masked_attention(q, np.arange(n), k, v, n - 1, w)
+    np.testing.assert_allclose(res["out"], ref, atol=1e-13)
+    assert not np.any(res["c"]) and not np.any(res["e"])
+    assert list(res["positions"]) == list(range(n - w, n))
+
+
+def test_int8_decode_staging_and_window():
+    rng = np.random.default_rng(10)
+    d, w = 128, 64
+    for n in [1, 15, 16, 17, 63, 64, 65, 80, 100, 129]:
+        k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+        q = rng.standard_normal(d)
+        res = int8.int8_decode(q, k, v, n, w)
+        ln = min(w, n)
+        assert list(res["positions"]) == list(range(n - ln, n))
+        exact = res["positions"] >= 16 * (n // 16)
+        assert not np.any(res["c"][exact])
+        assert np.all(res["c"] >= res["e"] * (1 - 1e-12))
+        ref = att.masked_attention(q, np.arange(n), k, v, n - 1, w)
+        assert np.max(np.abs(res["out"] - ref)) < 0.05  # quantization error, loose
+
+
+def test_expected_store_consistent():
+    rng = np.random.default_rng(12)
+    d, w = 128, 64
+    n = 16 * 9 + 5
+    k, v = rng.standard_normal((n, d)).astype(np.float32), rng.standard_normal((n, d)).astype(np.float32)
+    st = decoder.expected_int8_store(k, v, n, w)
+    assert st["staged_positions"] == list(range(144, 149))
+    # ring holds the last w/16 complete blocks: positions 80..143
+    assert sorted(st["slot_pos"]) == list(range(80, 144))
+    for s in range(w):
+        p = st["slot_pos"][s]
+        assert p % w == s
+        blk = p // 16
+        sc, codes = int8.quantize_block(k[blk * 16:(blk + 1) * 16])
+        assert st["k_scale"][s // 16] == sc
+        np.testing.assert_array_equal(st["k_codes"][s], codes[p % 16])
+
+
+def test_storage_format(golden):
+    g = golden("witcert_witness_format.json")
+    d = g["head_dim"]
+    nb = d // int8.BAND
+    assert nb == g["bands"]
+    assert nb * 2 == g["witness_bytes_per_token_head"]  # fp16 per band
+    per_token_head = 2 * d * 1 + nb * 2 + 2 * 4 / int8.BLOCK  # codes K+V, witness, scales
+    assert per_token_head == 288.5
