@@ -1,0 +1,150 @@
+/*
+ * swa.h -- C ABI of the sliding-window ring-buffer KV cache and its decode
+ * step, built as hand-written HIP for AMD gfx950 (MI355X).
+ *
+ * The cache follows the record described on the page "LLM 機制實驗（五）"
+ * (huhohoo.com, section 哪些東西必須一起裁剪): keys, values, the absolute
+ * position of every stored row, and next_position, the position the next
+ * token receives.  Its physical form is the fixed array of W slots of the page
+ * "用Lean4形式化验证滑动窗口KV Cache的正确性" (framerc.cn, §3.4): the token at
+ * absolute position p lives in slot p mod W and overwrites the oldest.  The
+ * decode query of step t attends to exactly the positions [t-len+1, t],
+ * len = min(W, t+1) (same page, §2.1 window and causal masks; §2.4 goal 3).
+ *
+ * Conventions shared by every entry point
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or synchronizes; every call only enqueues kernels
+ *   on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ * - Layouts are dense row-major, innermost dimension last, as written next
+ *   to each field.  K/V, q, out, staging and workspace pointers must be
+ *   16-byte aligned.
+ * - Return value: SWA_OK (0) or a negative SWA_E* code for a condition the
+ *   host can check (bad sizes, NULL, misalignment, unsupported shape, small
+ *   workspace, launch failure).  On error nothing has been enqueued.
+ *   Device-side preconditions (next_position >= 0, next_position + T <
+ *   2^31) are not checked on the hot path; swa_validate checks the cache.
+ * - Positions are 0-based int32.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SWA_OK = 0,
+  SWA_EINVAL = -1,       /* B, H, W < 1, T < 0, W*D*elem >= 2^32, or INT8 W not a multiple of 16 */
+  SWA_ENULL = -2,        /* a required pointer is NULL */
+  SWA_EALIGN = -3,       /* a K/V/q/out/staging/workspace pointer is not 16-byte aligned */
+  SWA_EUNSUPPORTED = -4, /* head_dim or kind not supported by this entry point */
+  SWA_EWORKSPACE = -5,   /* ws_bytes < swa_workspace_bytes(cache) */
+  SWA_EHIP = -6          /* a kernel launch failed */
+};
+
+enum {
+  SWA_KV_BF16 = 0, /* K/V rows bf16; q and new rows bf16 */
+  SWA_KV_FP32 = 1, /* K/V rows fp32; q and new rows fp32 */
+  SWA_KV_INT8 = 2  /* K/V INT8 codes per 16-token block + fp16 band witness; q, new rows bf16 */
+};
+
+/* Cache descriptor.  Supported head_dim D: BF16 {64, 128, 256}; FP32
+ * {16, 32, 64, 128}; INT8 {128} (16 bands of 8 dims).
+ *
+ *  k, v           [B][H][W][D]   bf16 | fp32 | int8 codes
+ *  pos            [B][W]  int32  absolute position held by each slot, -1 if
+ *                                none (INT8: position of the committed code row)
+ *  next_position  [B]     int32  position the next appended token receives
+ *  INT8 only:
+ *  k_scale,v_scale [B][H][W/16] fp32  absmax/127 of the block in those slots
+ *  witness        [B][H][W][D/8] fp16 bits: band norms of the key residual,
+ *                                rounded toward +infinity
+ *  k_stage,v_stage [B][H][16][D] bf16 rows of the incomplete newest block,
+ *                                row index = position mod 16
+ */
+typedef struct swa_cache {
+  int32_t kind, B, H, D, W;
+  int32_t reserved; /* must be 0 */
+  void *k, *v;
+  int32_t *pos;
+  int32_t *next_position;
+  float *k_scale, *v_scale;
+  uint16_t *witness;
+  void *k_stage, *v_stage;
+} swa_cache;
+
+/* Empty the cache: next_position[b] = 0 and pos[b][*] = -1 for every b (INT8
+ * also clears the block scales).  Row contents are left as they are; no
+ * slot is visible until written.  Errors: SWA_EINVAL, SWA_ENULL, SWA_EHIP. */
+int swa_cache_reset(const swa_cache *c, void *stream);
+
+/* Append T tokens per sequence (prefill chunk or one decode token).
+ * framerc.cn §2.2 and §3.3-§3.4: write, evict the oldest when over W;
+ * airsota.com §三 step 1 (write at the current position); huhohoo.com
+ * (next_position advances with the rows).
+ *  k_new, v_new  [B][H][T][D] in the cache's input dtype (INT8 kind: bf16).
+ * Token j of sequence b gets position p = next_position[b] + j and slot
+ * p mod W; pos[b][slot] = p; afterwards next_position[b] += T.  Only the last
+ * min(T, W) tokens are stored (the others would be overwritten).
+ * INT8 kind (agifrontier.github.io WitCert, section 频带酉性与双层证书: the
+ * write path quantizes and records band norms of the residual): a token first
+ * goes to the staging rows; when the block of positions [16m, 16m+16) is
+ * complete it is quantized into slots (16m mod W).. with one fp32 absmax/127
+ * scale per block and tensor, codes rint(x/s) clamped to +-127, and the key
+ * residual's 16 band norms written rounded up to fp16.  T = 0 is a no-op. */
+int kv_append(const swa_cache *c, const void *k_new, const void *v_new, int32_t T, void *stream);
+
+/* Decode attention for one query per sequence over the last min(W, n) tokens,
+ * n = next_position[b] (append first, then attend: airsota.com §三 steps 2-4;
+ * scores q.k/sqrt(D), max-subtracted softmax, weighted V).  BF16 and FP32
+ * kinds.  Split over the context with an online softmax; the last work-group
+ * of each (b, h) merges the splits.
+ *  q    [B][H][D]  cache input dtype
+ *  out  [B][H][D]  fp32; a sequence with n = 0 gets zeros
+ *  ws   device workspace of ws_bytes >= swa_workspace_bytes(c), zero-filled
+ *       once by swa_workspace_init before its first use; each call leaves it
+ *       ready for the next.  Calls sharing one workspace must be ordered on
+ *       one stream. */
+int decode_attn(const swa_cache *c, const void *q, float *out, void *ws, size_t ws_bytes,
+                void *stream);
+
+/* INT8 decode attention with the fused witness bound (WitCert, section
+ * 频带酉性与双层证书: |q.r_t|/sqrt(d) <= c_t = (1/sqrt(d)) sum_b ||q_b|| w_{t,b};
+ * section SGLang 生产级落地: per-block scales fold into per-token scalars).
+ * Visible tokens in committed blocks are read as scale*code, the newest
+ * n mod 16 tokens exactly from the staging rows (their c_t is 0).
+ *  q      [B][H][D] bf16
+ *  out    [B][H][D] fp32
+ *  cmax   [B][H]    fp32: max of c_t over the visible tokens (0 if none are
+ *                   quantized), times (1 + 2^-12) to cover float32 rounding
+ *  c_all  NULL, or [B][H][W] fp32: c_t of the visible token in each slot,
+ *         0 for slots with no visible quantized token (verification only)
+ *  ws, ws_bytes: as for decode_attn. */
+int decode_attn_int8_witness(const swa_cache *c, const void *q, float *out, float *cmax,
+                             float *c_all, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes the decode entry points need for this cache shape (split
+ * partials and per-(b,h) arrival counters).  0 for an invalid descriptor. */
+size_t swa_workspace_bytes(const swa_cache *c);
+
+/* Zero-fill a workspace before its first use.  Errors: SWA_ENULL, SWA_EALIGN,
+ * SWA_EHIP. */
+int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Debug check of the position invariant (framerc.cn §3.2 PositionInvariant,
+ * §6.3 the invariant as a runtime assertion): adds to *violations (device
+ * int32, caller zeroes it) the number of slots whose pos differs from the
+ * newest position p < n (INT8: p < 16*(n/16)) with p mod W == slot, or -1. */
+int swa_validate(const swa_cache *c, int32_t *violations, void *stream);
+
+/* Static text for a status code. */
+const char *swa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

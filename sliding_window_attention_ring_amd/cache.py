@@ -1,0 +1,184 @@
+"""Python binding of the C ABI: torch tensors in, device pointers out.
+
+torch provides device memory and the current HIP stream; every step of the
+decode path runs in the HIP kernels of libswa.so.  The functions keep the C
+names (``kv_append``, ``decode_attn``, ``decode_attn_int8_witness``, ...) and
+only check and marshal their arguments.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _capi
+from ._capi import KIND, SwaCacheDesc, check, lib
+
+_INPUT_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.bfloat16}
+_STORE_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.int8}
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, shape, dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class KVCache:
+    """Device tensors of one sliding-window ring cache and its descriptor.
+
+    kind: "bf16" | "fp32" | "int8"; B sequences, H heads, head_dim D, window W.
+    Tensors (see include/swa.h for the layouts): ``k``, ``v``, ``pos``,
+    ``next_position`` and, for INT8, ``k_scale``, ``v_scale``, ``witness``
+    (fp16), ``k_stage``, ``v_stage``.
+    """
+
+    def __init__(self, kind: str, B: int, H: int, D: int, W: int, device="cuda"):
+        if kind not in KIND:
+            raise ValueError(f"kind must be one of {sorted(KIND)}")
+        self.kind, self.B, self.H, self.D, self.W = kind, B, H, D, W
+        dev = torch.device(device)
+        self.k = torch.empty((B, H, W, D), dtype=_STORE_DTYPE[kind], device=dev)
+        self.v = torch.empty_like(self.k)
+        self.pos = torch.empty((B, W), dtype=torch.int32, device=dev)
+        self.next_position = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.k_scale = self.v_scale = self.witness = self.k_stage = self.v_stage = None
+        if kind == "int8":
+            self.k_scale = torch.empty((B, H, W // 16), dtype=torch.float32, device=dev)
+            self.v_scale = torch.empty_like(self.k_scale)
+            self.witness = torch.empty((B, H, W, D // 8), dtype=torch.float16, device=dev)
+            self.k_stage = torch.empty((B, H, 16, D), dtype=torch.bfloat16, device=dev)
+            self.v_stage = torch.empty_like(self.k_stage)
+        self.desc = self._make_desc()
+        self._ws = None
+        cache_reset(self)
+
+    def _make_desc(self, b: Optional[int] = None) -> SwaCacheDesc:
+        def sel(t):
+            if t is None:
+                return None
+            return t.data_ptr() if b is None else t[b].data_ptr()
+        return SwaCacheDesc(KIND[self.kind], self.B if b is None else 1, self.H, self.D, self.W, 0,
+                            sel(self.k), sel(self.v), sel(self.pos), sel(self.next_position),
+                            sel(self.k_scale), sel(self.v_scale), sel(self.witness),
+                            sel(self.k_stage), sel(self.v_stage))
+
+    def seq_view(self, b: int) -> "SeqView":
+        """Descriptor of sequence ``b`` alone (B = 1), for ragged appends."""
+        return SeqView(self, b)
+
+    @property
+    def input_dtype(self) -> torch.dtype:
+        return _INPUT_DTYPE[self.kind]
+
+    def workspace(self) -> torch.Tensor:
+        """The decode workspace of this cache, allocated and zero-filled once."""
+        if self._ws is None:
+            nbytes = workspace_bytes(self)
+            self._ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.k.device)
+            workspace_init(self._ws)
+        return self._ws
+
+
+class SeqView:
+    """One sequence of a KVCache as a B = 1 cache (shares the storage)."""
+
+    def __init__(self, cache: KVCache, b: int):
+        if not 0 <= b < cache.B:
+            raise IndexError(b)
+        self.parent, self.b = cache, b
+        self.kind, self.B, self.H, self.D, self.W = cache.kind, 1, cache.H, cache.D, cache.W
+        self.k = cache.k
+        self.desc = cache._make_desc(b)
+
+    @property
+    def input_dtype(self) -> torch.dtype:
+        return self.parent.input_dtype
+
+
+def cache_reset(cache, stream=None) -> None:
+    """``swa_cache_reset``: next_position = 0, every slot empty."""
+    check(lib().swa_cache_reset(ctypes.byref(cache.desc), _stream(stream)), "swa_cache_reset")
+
+
+def kv_append(cache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    """``kv_append``: append ``k_new``, ``v_new`` of shape [B, H, T, D]."""
+    T = k_new.shape[2] if k_new.dim() == 4 else -1
+    shape = (cache.B, cache.H, T, cache.D)
+    _need(k_new, shape, cache.input_dtype, "k_new")
+    _need(v_new, shape, cache.input_dtype, "v_new")
+    check(lib().kv_append(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), T, _stream(stream)),
+          "kv_append")
+
+
+def workspace_bytes(cache) -> int:
+    return int(lib().swa_workspace_bytes(ctypes.byref(cache.desc)))
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    check(lib().swa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+          "swa_workspace_init")
+
+
+def decode_attn(cache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``decode_attn``: fp32 output [B, H, D] for one query per sequence."""
+    _need(q, (cache.B, cache.H, cache.D), cache.input_dtype, "q")
+    if out is None:
+        out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=q.device)
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    ws = cache.workspace() if ws is None else ws
+    check(lib().decode_attn(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)), "decode_attn")
+    return out
+
+
+def decode_attn_int8_witness(cache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+                             cmax: Optional[torch.Tensor] = None, c_all: Optional[torch.Tensor] = None,
+                             want_c_all: bool = False, ws: Optional[torch.Tensor] = None,
+                             stream=None):
+    """``decode_attn_int8_witness``: returns (out [B,H,D], cmax [B,H], c_all [B,H,W] or None)."""
+    _need(q, (cache.B, cache.H, cache.D), torch.bfloat16, "q")
+    dev = q.device
+    if out is None:
+        out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=dev)
+    if cmax is None:
+        cmax = torch.empty((cache.B, cache.H), dtype=torch.float32, device=dev)
+    if c_all is None and want_c_all:
+        c_all = torch.empty((cache.B, cache.H, cache.W), dtype=torch.float32, device=dev)
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    _need(cmax, (cache.B, cache.H), torch.float32, "cmax")
+    if c_all is not None:
+        _need(c_all, (cache.B, cache.H, cache.W), torch.float32, "c_all")
+    ws = cache.workspace() if ws is None else ws
+    check(lib().decode_attn_int8_witness(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(cmax),
+                                         _ptr(c_all), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "decode_attn_int8_witness")
+    return out, cmax, c_all
+
+
+def validate(cache, stream=None) -> int:
+    """``swa_validate``: number of slots violating the position invariant (syncs)."""
+    viol = torch.zeros((1,), dtype=torch.int32, device=cache.k.device)
+    check(lib().swa_validate(ctypes.byref(cache.desc), _ptr(viol), _stream(stream)), "swa_validate")
+    return int(viol.item())
+
+
+def status_string(status: int) -> str:
+    return _capi.status_string(status)

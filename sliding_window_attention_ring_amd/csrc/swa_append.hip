@@ -1,0 +1,228 @@
+// Append kernels: write new K/V rows into the ring of W slots.
+//
+// Ring rule (page "用Lean4形式化验证滑动窗口KV Cache的正确性", §3.4): the token
+// with absolute position p is stored in slot p mod W and overwrites the
+// oldest; each slot also records p (§3.2, cells carry their position).
+// next_position advances with the rows (page "LLM 機制實驗（五）", section
+// 哪些東西必須一起裁剪).  The position is read from next_position on the
+// device, so a decode loop needs no host round trip.  The advance is a
+// separate launch ordered after the writes, so no work-group can read an
+// already-advanced value.
+#include "swa_device.h"
+#include "swa_launch.h"
+
+namespace swa {
+namespace {
+
+// One thread per 16-byte vector of the last Tw = min(T, W) new tokens.
+// A chunk longer than W writes only its last W tokens: the earlier ones
+// would be overwritten inside the same chunk, so skipping them keeps every
+// slot written by exactly one thread.
+__global__ void append_rows_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                                   uint4* __restrict__ K, uint4* __restrict__ V,
+                                   int32_t* __restrict__ pos, const int32_t* __restrict__ np,
+                                   int B, int H, int W, int T, int Tw, int vpr) {
+  const int64_t total = (int64_t)B * H * Tw * vpr;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int vec = (int)(i % vpr);
+    int64_t r = i / vpr;
+    const int jj = (int)(r % Tw);
+    r /= Tw;
+    const int h = (int)(r % H);
+    const int b = (int)(r / H);
+    const int j = T - Tw + jj;
+    const int64_t n0 = np[b];
+    if (n0 < 0) continue;  // precondition violated: write nothing (swa_validate reports it)
+    const int64_t p = n0 + j;
+    const int64_t slot = p % W;
+    const int64_t bh = (int64_t)b * H + h;
+    const int64_t src = (bh * T + j) * vpr + vec;
+    const int64_t dst = (bh * W + slot) * vpr + vec;
+    K[dst] = k_new[src];
+    V[dst] = v_new[src];
+    if (h == 0 && vec == 0) pos[(int64_t)b * W + slot] = (int32_t)p;
+  }
+}
+
+__global__ void advance_kernel(int32_t* __restrict__ np, int B, int T) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) np[b] += T;
+}
+
+// INT8 commit of complete 16-token blocks.  Grid (blocks, H, B), 128 threads:
+// wave 0 quantizes the key block and writes its witness, wave 1 the value
+// block.  Lane l handles token l/4 of the block and dims [32*(l%4), +32).
+// Rows come from the staging area for positions below the old
+// next_position and from the new chunk otherwise.
+//
+// Quantization (page "WitCert：运行时误差仪表盘", section SGLang 生产级落地:
+// one scale per block): s = f32(absmax / 127) with IEEE division, code =
+// rint(x / s) (IEEE division, ties to even) clamped to +-127; s = 0 gives zero
+// codes.  Witness (section 频带酉性与双层证书): the Euclidean norm of each
+// 8-dim band of the key residual k - s*code, stored as fp16 rounded toward
+// +infinity after a 2^-18 relative pad that covers the float32 rounding of
+// the residual and the norm, so the stored value is never below the exact
+// norm.
+constexpr int kD8 = 128;
+
+__global__ __launch_bounds__(128) void append_int8_blocks_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint16_t* __restrict__ k_stage, const uint16_t* __restrict__ v_stage,
+    int8_t* __restrict__ Kc, int8_t* __restrict__ Vc, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, uint16_t* __restrict__ witness, int32_t* __restrict__ pos,
+    const int32_t* __restrict__ np, int H, int W, int T) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int64_t n0 = np[b];
+  if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
+  const int64_t n1 = n0 + T;
+  const int64_t kb_hi = n1 / 16;
+  int64_t kb_lo = n0 / 16;
+  if (kb_hi - W / 16 > kb_lo) kb_lo = kb_hi - W / 16;
+  const int64_t kb = kb_lo + blockIdx.x;
+  if (kb >= kb_hi) return;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 2;        // token within the block
+  const int part = lane & 3;      // 32-dim quarter of the row
+  const int64_t p = kb * 16 + r;
+  const int64_t bh = (int64_t)b * H + h;
+
+  const uint16_t* src_new = wave == 0 ? k_new : v_new;
+  const uint16_t* src_stage = wave == 0 ? k_stage : v_stage;
+  const uint16_t* row = (p < n0) ? src_stage + (bh * 16 + (p & 15)) * kD8
+                                 : src_new + (bh * T + (p - n0)) * kD8;
+  const uint4* rv = reinterpret_cast<const uint4*>(row + part * 32);
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float f[8];
+    unpack8(rv[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[i * 8 + e] = f[e];
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = group_max<64>(amax);
+  const float s = __fdiv_rn(amax, 127.0f);
+
+  int8_t codes[32];
+  float cf[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    float c = 0.f;
+    if (s > 0.f) c = fminf(fmaxf(rintf(__fdiv_rn(x[e], s)), -127.f), 127.f);
+    cf[e] = c;
+    codes[e] = (int8_t)(int)c;
+  }
+  const int64_t slot = (kb * 16) % W + r;
+  int8_t* dst = (wave == 0 ? Kc : Vc) + (bh * W + slot) * kD8 + part * 32;
+  uint4 packed[2];
+  uint32_t* pw = reinterpret_cast<uint32_t*>(packed);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pw[i] = (uint32_t)(uint8_t)codes[4 * i] | ((uint32_t)(uint8_t)codes[4 * i + 1] << 8) |
+            ((uint32_t)(uint8_t)codes[4 * i + 2] << 16) | ((uint32_t)(uint8_t)codes[4 * i + 3] << 24);
+  }
+  reinterpret_cast<uint4*>(dst)[0] = packed[0];
+  reinterpret_cast<uint4*>(dst)[1] = packed[1];
+  if (lane == 0) {
+    float* sc = wave == 0 ? k_scale : v_scale;
+    sc[bh * (W / 16) + (kb * 16) % W / 16] = s;
+  }
+  if (wave == 0) {
+    uint16_t wb[4];
+#pragma unroll
+    for (int band = 0; band < 4; ++band) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float res = fmaf(-s, cf[band * 8 + e], x[band * 8 + e]);
+        ss = fmaf(res, res, ss);
+      }
+      const float nrm = sqrtf(ss) * (1.0f + 0x1p-18f);
+      wb[band] = f32_to_f16_up(nrm);
+    }
+    uint2 o;
+    o.x = (uint32_t)wb[0] | ((uint32_t)wb[1] << 16);
+    o.y = (uint32_t)wb[2] | ((uint32_t)wb[3] << 16);
+    reinterpret_cast<uint2*>(witness + (bh * W + slot) * (kD8 / 8))[part] = o;
+    if (h == 0 && part == 0) pos[(int64_t)b * W + slot] = (int32_t)p;
+  }
+}
+
+// Tokens of the new, still incomplete block go to the staging rows (row
+// index = position mod 16).  Runs after the commit kernel, which may read
+// staging rows of the block it completes.
+__global__ void append_int8_stage_kernel(const uint4* __restrict__ k_new,
+                                         const uint4* __restrict__ v_new,
+                                         uint4* __restrict__ k_stage, uint4* __restrict__ v_stage,
+                                         const int32_t* __restrict__ np, int H, int T, int vpr) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int64_t n0 = np[b];
+  if (n0 < 0) return;
+  const int64_t n1 = n0 + T;
+  int64_t lo = (n1 / 16) * 16;
+  if (lo < n0) lo = n0;
+  const int64_t cnt = n1 - lo;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int j = idx / vpr, vec = idx % vpr;
+  if (j >= cnt) return;
+  const int64_t p = lo + j;
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t src = (bh * T + (p - n0)) * vpr + vec;
+  const int64_t dst = (bh * 16 + (p & 15)) * vpr + vec;
+  k_stage[dst] = k_new[src];
+  v_stage[dst] = v_new[src];
+}
+
+}  // namespace
+
+hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void* v_new, int T,
+                              hipStream_t s) {
+  const int esz = c.kind == SWA_KV_FP32 ? 4 : 2;
+  const int vpr = c.D * esz / 16;
+  const int Tw = T < c.W ? T : c.W;
+  const int64_t total = (int64_t)c.B * c.H * Tw * vpr;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 1 << 20) blocks = 1 << 20;
+  hipLaunchKernelGGL(append_rows_kernel, dim3((unsigned)blocks), dim3(threads), 0, s,
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                     reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.pos,
+                     c.next_position, c.B, c.H, c.W, T, Tw, vpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void* v_new, int T,
+                              hipStream_t s) {
+  // At most ceil(T/16) blocks complete, and only the newest W/16 are kept.
+  int nblk = (T + 15) / 16;
+  if (nblk > c.W / 16) nblk = c.W / 16;
+  hipLaunchKernelGGL(append_int8_blocks_kernel, dim3(nblk, c.H, c.B), dim3(128), 0, s,
+                     reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new),
+                     reinterpret_cast<const uint16_t*>(c.k_stage),
+                     reinterpret_cast<const uint16_t*>(c.v_stage), reinterpret_cast<int8_t*>(c.k),
+                     reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale, c.witness, c.pos,
+                     c.next_position, c.H, c.W, T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int vpr = c.D * 2 / 16;
+  const int tok = T < 16 ? T : 16;
+  const int threads = 256;
+  const int blocks = (tok * vpr + threads - 1) / threads;
+  hipLaunchKernelGGL(append_int8_stage_kernel, dim3(blocks, c.H, c.B), dim3(threads), 0, s,
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                     reinterpret_cast<uint4*>(c.k_stage), reinterpret_cast<uint4*>(c.v_stage),
+                     c.next_position, c.H, T, vpr);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance(const swa_cache& c, int T, hipStream_t s) {
+  hipLaunchKernelGGL(advance_kernel, dim3((c.B + 255) / 256), dim3(256), 0, s, c.next_position, c.B, T);
+  return hipGetLastError();
+}
+
+}  // namespace swa

@@ -1,0 +1,236 @@
+// C ABI entry points (declared in include/swa.h): host-side argument
+// checks, the split policy of the decode kernels, and the small
+// maintenance kernels (reset, workspace fill, position-invariant check).
+#include <stdlib.h>
+
+#include "swa_device.h"
+#include "swa_launch.h"
+
+namespace swa {
+
+int decode_round_rows(const swa_cache& c);
+int decode_int8_round_blocks();
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool head_dim_supported(int kind, int D) {
+  switch (kind) {
+    case SWA_KV_BF16: return D == 64 || D == 128 || D == 256;
+    case SWA_KV_FP32: return D == 16 || D == 32 || D == 64 || D == 128;
+    case SWA_KV_INT8: return D == 128;
+  }
+  return false;
+}
+
+// Descriptor checks common to every entry point.
+int check_cache(const swa_cache* c) {
+  if (c == nullptr) return SWA_ENULL;
+  if (c->kind != SWA_KV_BF16 && c->kind != SWA_KV_FP32 && c->kind != SWA_KV_INT8) return SWA_EUNSUPPORTED;
+  if (c->B < 1 || c->H < 1 || c->W < 1 || c->reserved != 0) return SWA_EINVAL;
+  if (c->B > 65535 || c->H > 65535) return SWA_EINVAL;  // grid y/z limits
+  if (!head_dim_supported(c->kind, c->D)) return SWA_EUNSUPPORTED;
+  if (c->kind == SWA_KV_INT8 && c->W % 16 != 0) return SWA_EINVAL;
+  // The decode kernels address one (b, h) region with 32-bit byte offsets.
+  const int64_t esz = c->kind == SWA_KV_FP32 ? 4 : c->kind == SWA_KV_BF16 ? 2 : 1;
+  if ((int64_t)c->W * c->D * esz >= ((int64_t)1 << 32)) return SWA_EINVAL;
+  if (c->k == nullptr || c->v == nullptr || c->pos == nullptr || c->next_position == nullptr)
+    return SWA_ENULL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return SWA_EALIGN;
+  if (((uintptr_t)c->pos & 3u) || ((uintptr_t)c->next_position & 3u)) return SWA_EALIGN;
+  if (c->kind == SWA_KV_INT8) {
+    if (!c->k_scale || !c->v_scale || !c->witness || !c->k_stage || !c->v_stage) return SWA_ENULL;
+    if (!aligned16(c->k_stage) || !aligned16(c->v_stage) || !aligned16(c->witness)) return SWA_EALIGN;
+    if (((uintptr_t)c->k_scale & 3u) || ((uintptr_t)c->v_scale & 3u)) return SWA_EALIGN;
+  }
+  return SWA_OK;
+}
+
+// Target number of work-groups per decode launch: enough to fill 256 CUs
+// several times over.  SWA_TARGET_WGS overrides it (read once per process,
+// so workspace sizes stay consistent).
+int target_wgs() {
+  static int v = [] {
+    const char* s = getenv("SWA_TARGET_WGS");
+    int x = s ? atoi(s) : 0;
+    return x > 0 ? x : 4096;
+  }();
+  return v;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+__global__ void reset_kernel(int32_t* __restrict__ pos, int32_t* __restrict__ np, float* __restrict__ ks,
+                             float* __restrict__ vs, int B, int H, int W, int int8) {
+  const int64_t npos = (int64_t)B * W;
+  const int64_t nsc = int8 ? (int64_t)B * H * (W / 16) : 0;
+  const int64_t total = npos > nsc ? npos : nsc;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < npos) pos[i] = -1;
+    if (i < B) np[i] = 0;
+    if (i < nsc) { ks[i] = 0.f; vs[i] = 0.f; }
+  }
+}
+
+__global__ void fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// Slot s must hold the newest position p < lim with p mod W == s, or -1.
+// lim = n for row caches, 16*(n/16) for INT8 (only committed blocks).
+__global__ void validate_kernel(const int32_t* __restrict__ pos, const int32_t* __restrict__ np,
+                                int32_t* __restrict__ violations, int B, int W, int int8) {
+  const int64_t total = (int64_t)B * W;
+  int bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(i / W), s = (int)(i % W);
+    const int64_t n = np[b];
+    if (n < 0) { bad += 1; continue; }
+    const int64_t lim = int8 ? (n / 16) * 16 : n;
+    const int64_t expect = (lim <= s) ? -1 : s + (int64_t)W * ((lim - 1 - s) / W);
+    bad += (pos[i] != expect);
+  }
+  if (bad) atomicAdd(violations, bad);
+}
+
+unsigned grid_for(int64_t n, int threads, int64_t cap) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b < 1) b = 1;
+  return (unsigned)(b > cap ? cap : b);
+}
+
+}  // namespace
+
+SplitPlan plan_decode(const swa_cache& c) {
+  SplitPlan p;
+  const int64_t tgt = target_wgs();
+  if (c.kind == SWA_KV_INT8) {
+    const int64_t rb = decode_int8_round_blocks();
+    const int64_t wb = c.W / 16;
+    int64_t cb = round_up(((int64_t)c.B * c.H * wb + tgt - 1) / tgt, rb);
+    if (cb > round_up(wb, rb)) cb = round_up(wb, rb);
+    p.unit_per_split = (int)cb;
+    p.nsplit_max = (int)((wb + cb - 1) / cb);
+  } else {
+    const int64_t rr = decode_round_rows(c);
+    int64_t ch = round_up(((int64_t)c.B * c.H * c.W + tgt - 1) / tgt, rr);
+    if (ch > round_up(c.W, rr)) ch = round_up(c.W, rr);
+    p.unit_per_split = (int)ch;
+    p.nsplit_max = (int)((c.W + ch - 1) / ch);
+  }
+  if (p.nsplit_max < 1) p.nsplit_max = 1;
+  return p;
+}
+
+hipError_t launch_reset(const swa_cache& c, hipStream_t s) {
+  const int64_t n = (int64_t)c.B * c.W > (int64_t)c.B * c.H * (c.W / 16) ? (int64_t)c.B * c.W
+                                                                          : (int64_t)c.B * c.H * (c.W / 16);
+  hipLaunchKernelGGL(reset_kernel, dim3(grid_for(n > c.B ? n : c.B, 256, 1 << 16)), dim3(256), 0, s, c.pos,
+                     c.next_position, c.k_scale, c.v_scale, c.B, c.H, c.W, c.kind == SWA_KV_INT8 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 4);
+  hipLaunchKernelGGL(fill_zero_u32, dim3(grid_for(n, 256, 1 << 16)), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(const swa_cache& c, int32_t* violations, hipStream_t s) {
+  hipLaunchKernelGGL(validate_kernel, dim3(grid_for((int64_t)c.B * c.W, 256, 1 << 16)), dim3(256), 0, s,
+                     c.pos, c.next_position, violations, c.B, c.W, c.kind == SWA_KV_INT8 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace swa
+
+using namespace swa;
+
+extern "C" {
+
+const char* swa_status_string(int status) {
+  switch (status) {
+    case SWA_OK: return "ok";
+    case SWA_EINVAL: return "invalid size or descriptor field";
+    case SWA_ENULL: return "required pointer is NULL";
+    case SWA_EALIGN: return "pointer not aligned (16 bytes for K/V/q/out/staging/workspace)";
+    case SWA_EUNSUPPORTED: return "kind or head_dim not supported by this entry point";
+    case SWA_EWORKSPACE: return "workspace smaller than swa_workspace_bytes()";
+    case SWA_EHIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t swa_workspace_bytes(const swa_cache* c) {
+  if (check_cache(c) != SWA_OK) return 0;
+  const SplitPlan p = plan_decode(*c);
+  return counters_bytes(*c) +
+         (size_t)c->B * c->H * (size_t)p.nsplit_max * partial_floats(c->D) * sizeof(float);
+}
+
+int swa_cache_reset(const swa_cache* c, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  return launch_reset(*c, (hipStream_t)stream) == hipSuccess ? SWA_OK : SWA_EHIP;
+}
+
+int swa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws == nullptr) return SWA_ENULL;
+  if (!aligned16(ws)) return SWA_EALIGN;
+  if (ws_bytes == 0) return SWA_OK;
+  return launch_fill_zero(ws, ws_bytes, (hipStream_t)stream) == hipSuccess ? SWA_OK : SWA_EHIP;
+}
+
+int kv_append(const swa_cache* c, const void* k_new, const void* v_new, int32_t T, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (T < 0) return SWA_EINVAL;
+  if (T == 0) return SWA_OK;
+  if (k_new == nullptr || v_new == nullptr) return SWA_ENULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SWA_EALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = c->kind == SWA_KV_INT8 ? launch_append_int8(*c, k_new, v_new, T, s)
+                                        : launch_append_rows(*c, k_new, v_new, T, s);
+  if (e == hipSuccess) e = launch_advance(*c, T, s);
+  return e == hipSuccess ? SWA_OK : SWA_EHIP;
+}
+
+int decode_attn(const swa_cache* c, const void* q, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (c->kind == SWA_KV_INT8) return SWA_EUNSUPPORTED;
+  if (q == nullptr || out == nullptr || ws == nullptr) return SWA_ENULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return SWA_EALIGN;
+  if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
+  const SplitPlan p = plan_decode(*c);
+  return launch_decode(*c, q, out, ws, p, (hipStream_t)stream) == hipSuccess ? SWA_OK : SWA_EHIP;
+}
+
+int decode_attn_int8_witness(const swa_cache* c, const void* q, float* out, float* cmax, float* c_all,
+                             void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (c->kind != SWA_KV_INT8) return SWA_EUNSUPPORTED;
+  if (q == nullptr || out == nullptr || cmax == nullptr || ws == nullptr) return SWA_ENULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return SWA_EALIGN;
+  if (((uintptr_t)cmax & 3u) || ((uintptr_t)c_all & 3u)) return SWA_EALIGN;
+  if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
+  const SplitPlan p = plan_decode(*c);
+  return launch_decode_int8(*c, q, out, cmax, c_all, ws, p, (hipStream_t)stream) == hipSuccess ? SWA_OK
+                                                                                                 : SWA_EHIP;
+}
+
+int swa_validate(const swa_cache* c, int32_t* violations, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (violations == nullptr) return SWA_ENULL;
+  if ((uintptr_t)violations & 3u) return SWA_EALIGN;
+  return launch_validate(*c, violations, (hipStream_t)stream) == hipSuccess ? SWA_OK : SWA_EHIP;
+}
+
+}  // extern "C"

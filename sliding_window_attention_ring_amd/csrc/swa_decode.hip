@@ -1,0 +1,299 @@
+// Single-query decode attention over the ring (bf16 or fp32 rows).
+//
+// What is computed (page "【AI 工业核题 D4】KV Cache 自回归生成推理", §三 decode
+// step; page "用Lean4形式化验证滑动窗口KV Cache的正确性", §2.1): for the query of
+// step t = n-1 (n = next_position), scores q.k_j / sqrt(D) over the visible
+// tokens, a max-subtracted softmax and the weighted sum of V.  After n
+// appends the visible tokens are exactly the rows in slots [0, min(W, n)):
+// while unfilled, slots 0..n-1; once full, every slot holds one of the last W
+// positions.  Softmax-weighted V is a function of the set of (k, v) pairs, so
+// slot order never matters (§3.3 keeps attention separate from the cache
+// order).
+//
+// Layout of the work (gfx950, wave64):
+// * grid (split, h, b); a work-group of NW waves owns `chunk` consecutive
+//   slots of one (b, h); splits beyond the live length exit at once;
+// * a row of D elements is read by LPR lanes, 16 bytes each, so one wave
+//   load instruction covers 64/LPR consecutive rows (1 KiB, coalesced);
+// * each lane keeps U loads of K and U of V in flight for the next
+//   iteration while it computes on the current one (register double
+//   buffering);
+// * dot products are reduced inside each LPR-lane group with DPP row ops;
+//   the online softmax keeps a running (max, sum, acc) per lane group in
+//   base 2;
+// * lane groups, then waves (through LDS), then splits are merged with the
+//   log-sum-exp rule; the last work-group of each (b, h) to finish (an
+//   arrival counter in the workspace) merges the splits and normalizes.
+#include "swa_device.h"
+#include "swa_launch.h"
+
+namespace swa {
+namespace {
+
+// Row formats.  bf16 keys use the packed bf16 dot product (exact products,
+// fp32 accumulate) with the raw query, scaled once per row afterwards; fp32
+// rows use plain fused multiply-adds with a pre-scaled query.
+template <typename T>
+struct RowFmt;
+template <>
+struct RowFmt<uint16_t> {  // bf16
+  static constexpr int kEpv = 8;
+  struct Q { uint32_t w[4]; };
+  static __device__ __forceinline__ Q load_q(const uint4 v, float) { return Q{{v.x, v.y, v.z, v.w}}; }
+  static __device__ __forceinline__ float dot(const Q& q, const uint4 k) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    float d = 0.f;
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.w[0]), __builtin_bit_cast(bf2, k.x), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.w[1]), __builtin_bit_cast(bf2, k.y), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.w[2]), __builtin_bit_cast(bf2, k.z), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.w[3]), __builtin_bit_cast(bf2, k.w), d, false);
+    return d;
+  }
+  static constexpr bool kPostScale = true;
+  static __device__ __forceinline__ void unpack(const uint4 v, float (&f)[8]) { unpack8(v, f); }
+};
+template <>
+struct RowFmt<float> {
+  static constexpr int kEpv = 4;
+  struct Q { float f[4]; };
+  static __device__ __forceinline__ Q load_q(const uint4 v, float scale) {
+    Q q;
+    unpack4(v, q.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q.f[e] *= scale;
+    return q;
+  }
+  static __device__ __forceinline__ float dot(const Q& q, const uint4 k) {
+    float f[4];
+    unpack4(k, f);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d = fmaf(q.f[e], f[e], d);
+    return d;
+  }
+  static constexpr bool kPostScale = false;
+  static __device__ __forceinline__ void unpack(const uint4 v, float (&f)[4]) { unpack4(v, f); }
+};
+
+constexpr float kNegBig = -1e30f;  // finite start value of the running max
+
+template <typename T, int D, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(
+    const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
+    const uint4* __restrict__ q, float* __restrict__ out, float* __restrict__ part,
+    uint32_t* __restrict__ counters, int H, int W, int chunk, int nsplit_max) {
+  using F = RowFmt<T>;
+  constexpr int EPV = F::kEpv;
+  constexpr int VPR = D / EPV;          // 16-byte vectors per row
+  constexpr int LPR = VPR;              // lanes per row
+  constexpr int RPL = 64 / LPR;         // rows per wave load
+  constexpr int RPI = RPL * U;          // rows per wave iteration
+  constexpr int PF = D + 4;             // floats per split partial
+  static_assert(LPR >= 2 && LPR <= 32, "row must span 2..32 lanes");
+
+  __shared__ float sm_m[NW], sm_l[NW];
+  __shared__ float sm_acc[NW][D];
+  __shared__ int sm_last;
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)b * H + h;
+  const int n = np[b];
+  const int len = n < W ? n : W;
+  if (len <= 0) {  // empty cache: defined as a zero output
+    if (split == 0)
+      for (int t = threadIdx.x; t < D; t += NW * 64) out[bh * D + t] = 0.f;
+    return;
+  }
+  const int nsplit = (len + chunk - 1) / chunk;
+  if (split >= nsplit) return;
+  const int r0 = split * chunk;
+  const int r1 = (r0 + chunk < len) ? r0 + chunk : len;
+
+  const int g = lane / LPR;      // row within a wave load
+  const int vec = lane % LPR;    // 16-byte vector within the row
+  // Per-(b,h) regions are below 4 GiB, so rows are addressed by 32-bit byte
+  // offsets from a wave-uniform base.
+  const char* Kbh = reinterpret_cast<const char*>(K + bh * (int64_t)W * VPR);
+  const char* Vbh = reinterpret_cast<const char*>(V + bh * (int64_t)W * VPR);
+
+  const float qscale = kLog2e / sqrtf((float)D);  // base-2 softmax of q.k/sqrt(D)
+  const typename F::Q qv = F::load_q(q[bh * VPR + vec], qscale);
+
+  float m = kNegBig, l = 0.f, acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+
+  auto load = [&](uint4 (&kb)[U], uint4 (&vb)[U], int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int row = base + u * RPL + g;
+      row = row < r1 ? row : r1 - 1;  // past the end: re-read a live row, masked below
+      const uint32_t off = (uint32_t)(row * VPR + vec) * 16u;
+      kb[u] = load_stream(reinterpret_cast<const uint4*>(Kbh + off));
+      vb[u] = load_stream(reinterpret_cast<const uint4*>(Vbh + off));
+    }
+  };
+  auto step = [&](const uint4 (&kb)[U], const uint4 (&vb)[U], int base) {
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float d = group_sum<LPR>(F::dot(qv, kb[u]));
+      if constexpr (F::kPostScale) d *= qscale;
+      const int row = base + u * RPL + g;
+      s[u] = row < r1 ? d : -INFINITY;
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
+    const float alpha = exp2_fast(m - mx);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = exp2_fast(s[u] - mx);
+      l += p;
+      float f[EPV];
+      F::unpack(vb[u], f);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] = fmaf(p, f[e], acc[e]);
+    }
+    m = mx;
+  };
+
+  // Two register buffers in turn: while one is consumed the other's loads
+  // are in flight.  Inside the loop the prefetch is unconditional, so the
+  // wait before each use only covers the older buffer.
+  const int stride = NW * RPI;
+  int base = r0 + wave * RPI;
+  if (base < r1) {
+    uint4 ka[U], va[U], kb[U], vb[U];
+    load(ka, va, base);
+    while (true) {
+      if (base + stride >= r1) { step(ka, va, base); break; }
+      load(kb, vb, base + stride);
+      step(ka, va, base);
+      base += stride;
+      if (base + stride >= r1) { step(kb, vb, base); break; }
+      load(ka, va, base + stride);
+      step(kb, vb, base);
+      base += stride;
+    }
+  }
+
+  // Merge the lane groups of this wave (lanes with equal `vec` hold the same dims).
+  float mw = m;
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+  {
+    const float sc = exp2_fast(m - mw);
+    l *= sc;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] *= sc;
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], o);
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) sm_acc[wave][lane * EPV + e] = acc[e];
+    if (lane == 0) { sm_m[wave] = mw; sm_l[wave] = l; }
+  }
+  __syncthreads();
+
+  // Merge the waves: thread t owns output dim t.
+  const int t = threadIdx.x;
+  float M = kNegBig, L = 0.f, A = 0.f;
+  if (t < D) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = exp2_fast(sm_m[w] - M);
+      L = fmaf(sm_l[w], sc, L);
+      A = fmaf(sm_acc[w][t], sc, A);
+    }
+  }
+  if (nsplit == 1) {
+    if (t < D) out[bh * D + t] = A / L;
+    return;
+  }
+
+  // Publish this split's partial, then count arrivals for (b, h).
+  float* my = part + (bh * nsplit_max + split) * PF;
+  if (t < D) my[4 + t] = A;
+  if (t == 0) { my[0] = M; my[1] = L; }
+  __threadfence();
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t prev = atomicAdd(&counters[bh], 1u);
+    sm_last = (prev == (uint32_t)(nsplit - 1));
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+
+  // Last arrival: log-sum-exp merge of all splits, normalize, reset the counter.
+  if (t < D) {
+    const float* pp = part + bh * nsplit_max * PF;
+    float Mg = kNegBig;
+    for (int sp = 0; sp < nsplit; ++sp) Mg = fmaxf(Mg, pp[sp * PF]);
+    float Lg = 0.f, Ag = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float sc = exp2_fast(pp[sp * PF] - Mg);
+      Lg = fmaf(pp[sp * PF + 1], sc, Lg);
+      Ag = fmaf(pp[sp * PF + 4 + t], sc, Ag);
+    }
+    out[bh * D + t] = Ag / Lg;
+  }
+  if (t == 0) counters[bh] = 0u;
+}
+
+template <typename T, int D>
+hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, const SplitPlan& plan,
+                      hipStream_t s) {
+  constexpr int NW = 4, U = 4;
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + counters_bytes(c));
+  hipLaunchKernelGGL((decode_kernel<T, D, NW, U>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
+                     reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v),
+                     c.next_position, reinterpret_cast<const uint4*>(q), out, part, counters, c.H, c.W,
+                     plan.unit_per_split, plan.nsplit_max);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Rows of one work-group iteration round (all NW waves): the split size is a
+// multiple of it so that every wave does the same number of iterations.
+int decode_round_rows(const swa_cache& c) {
+  const int esz = c.kind == SWA_KV_FP32 ? 4 : 2;
+  const int lpr = c.D * esz / 16;
+  return 4 /*NW*/ * (64 / lpr) * 4 /*U*/;
+}
+
+hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws, const SplitPlan& plan,
+                         hipStream_t s) {
+  if (c.kind == SWA_KV_BF16) {
+    switch (c.D) {
+      case 64: return launch_one<uint16_t, 64>(c, q, out, ws, plan, s);
+      case 128: return launch_one<uint16_t, 128>(c, q, out, ws, plan, s);
+      case 256: return launch_one<uint16_t, 256>(c, q, out, ws, plan, s);
+    }
+  } else if (c.kind == SWA_KV_FP32) {
+    switch (c.D) {
+      case 16: return launch_one<float, 16>(c, q, out, ws, plan, s);
+      case 32: return launch_one<float, 32>(c, q, out, ws, plan, s);
+      case 64: return launch_one<float, 64>(c, q, out, ws, plan, s);
+      case 128: return launch_one<float, 128>(c, q, out, ws, plan, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace swa

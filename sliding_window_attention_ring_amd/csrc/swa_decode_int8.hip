@@ -1,0 +1,341 @@
+// INT8 decode attention with the fused witness bound (head_dim 128).
+//
+// Page "WitCert：运行时误差仪表盘，把崩溃的KV量化从22.8拉回79.7":
+// * section 频带酉性与双层证书: the logit error of a token with key residual
+//   r_t is |q.r_t|/sqrt(d) <= c_t = (1/sqrt(d)) sum_b ||q_b|| w_{t,b}, with
+//   w_{t,b} the stored band norms (16 bands of 8 dims, fp16);
+// * section SGLang 生产级落地: with one scale per block the scale is a scalar
+//   for every token of the block, so the key scale multiplies the finished
+//   dot product and the value scale multiplies the softmax weight -- no
+//   per-element dequantization multiply.
+//
+// Visible tokens for the query of step t = n-1 (n = next_position, len =
+// min(W, n)) are the positions [n-len, n-1].  Those below 16*(n/16) sit in
+// committed blocks of the ring: blocks k0..nb-1 with k0 = (n-len)/16, block k
+// in slots [16k mod W, +16); in block k0 the positions below n-len are masked.
+// The newest n mod 16 tokens are exact bf16 rows in the staging area and
+// carry c_t = 0; the merging work-group folds them in.
+//
+// Layout of the work: grid (split, h, b), NW waves; a split owns `cb`
+// consecutive blocks; a wave takes UB blocks per iteration.  Per block a
+// lane loads 2x16 B of key codes and 2x16 B of value codes (8 lanes per
+// 128-byte row, rows g and g+8) and 8 B of witness (4 lanes per token).
+#include "swa_device.h"
+#include "swa_launch.h"
+
+namespace swa {
+namespace {
+
+constexpr int D = 128;
+constexpr int PF = D + 4;          // m, l, cmax, pad, acc[D]
+constexpr float kNegBig = -1e30f;
+// Relative pad on the reported bound: covers the float32 rounding of the
+// band norms of q, the 16-term sum and 1/sqrt(D) (each well below 2^-20).
+constexpr float kBoundPad = 1.0f + 0x1p-12f;
+
+struct Blk {
+  uint4 k0, k1, v0, v1;
+  uint2 w;
+};
+
+template <int NW, int UB>
+__global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
+    const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
+    const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const uint16_t* __restrict__ kst,
+    const uint16_t* __restrict__ vst, const int32_t* __restrict__ np, const uint16_t* __restrict__ q,
+    float* __restrict__ out, float* __restrict__ cmax_out, float* __restrict__ c_all,
+    float* __restrict__ part, uint32_t* __restrict__ counters, int H, int W, int cb, int nsplit_max) {
+  __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
+  __shared__ float sm_acc[NW][D];
+  __shared__ float sm_s[16];
+  __shared__ int sm_last;
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
+  const int n = np[b];
+  const int len = n < W ? n : W;
+  const int nb = n / 16;                 // committed blocks
+  const int p0 = n - len;                // oldest visible position
+  const int k0 = p0 / 16;
+  const int nbr = nb > k0 ? nb - k0 : 0; // ring blocks holding visible tokens
+  int nsplit = (nbr + cb - 1) / cb;
+  if (nsplit < 1) nsplit = 1;
+  if (split >= nsplit) return;
+  const int blo = k0 + split * cb;
+  const int bhi = (blo + cb < nb) ? blo + cb : nb;
+  const int wblocks = W / 16;
+
+  const float qscale = kLog2e / sqrtf((float)D);
+  const float rsd = 1.0f / sqrtf((float)D);
+
+  // Key-dot mapping: lane covers dims [16*(lane%8), +16) of row lane/8 (+8).
+  const int g = lane >> 3, vq = lane & 7;
+  float qf[16];
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(q + bh * D) + 2 * vq;
+    float f[8];
+    unpack8(qv[0], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] = f[e] * qscale;
+    unpack8(qv[1], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[8 + e] = f[e] * qscale;
+  }
+  // Witness mapping: lane covers bands [4*(lane%4), +4) of token lane/4.
+  // nq[i] = ||q_band|| / sqrt(D) for those bands.
+  const int wt = lane >> 2, wq = lane & 3;
+  float nq[4];
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(q + bh * D) + 4 * wq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float f[8];
+      unpack8(qv[i], f);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+      nq[i] = sqrtf(ss) * rsd;
+    }
+  }
+
+  float m = kNegBig, l = 0.f, cm = 0.f, acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+  // Per-(b,h) regions are below 4 GiB: 32-bit byte offsets from wave-uniform bases.
+  const char* Kbh = reinterpret_cast<const char*>(Kc + bh * (int64_t)W * D);
+  const char* Vbh = reinterpret_cast<const char*>(Vc + bh * (int64_t)W * D);
+  const char* Wbh = reinterpret_cast<const char*>(wit + bh * (int64_t)W * 16);
+  const float* ksbh = ksc + bh * wblocks;
+  const float* vsbh = vsc + bh * wblocks;
+
+  auto load = [&](Blk (&bk)[UB], int kb0) {
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) {
+      int kb = kb0 + ub;
+      kb = kb < bhi ? kb : bhi - 1;  // past the end: re-read a live block, masked below
+      const uint32_t sb = (uint32_t)(kb % wblocks) * 16u;  // first slot of the block
+      const uint32_t ok = sb * D + (uint32_t)lane * 16u;
+      bk[ub].k0 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok));
+      bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok + 1024u));
+      bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok));
+      bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok + 1024u));
+      bk[ub].w = load_stream(reinterpret_cast<const uint2*>(Wbh + sb * 32u + (uint32_t)lane * 8u));
+    }
+  };
+
+  auto step = [&](const Blk (&cur)[UB], int kb0) {
+    float s[2 * UB], sv[UB];
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) {
+      const int kb = kb0 + ub;
+      const bool live = kb < bhi;
+      const int kbc = live ? kb : bhi - 1;
+      const int sbk = kbc % wblocks;
+      const float sk = ksbh[sbk];
+      sv[ub] = vsbh[sbk];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint4 c = half ? cur[ub].k1 : cur[ub].k0;
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d = fmaf(qf[4 * i + j], s8(cw[i], j), d);
+        d = group_sum<8>(d) * sk;  // key scale folded into the finished dot
+        const int pos = kb * 16 + g + 8 * half;
+        s[2 * ub + half] = (live && pos >= p0) ? d : -INFINITY;
+      }
+      // Witness bound of token wt of this block.
+      {
+        const uint2 w = cur[ub].w;
+        float cp = nq[0] * f16_to_f32((uint16_t)(w.x & 0xffff));
+        cp = fmaf(nq[1], f16_to_f32((uint16_t)(w.x >> 16)), cp);
+        cp = fmaf(nq[2], f16_to_f32((uint16_t)(w.y & 0xffff)), cp);
+        cp = fmaf(nq[3], f16_to_f32((uint16_t)(w.y >> 16)), cp);
+        cp = group_sum<4>(cp);
+        const int pos = kb * 16 + wt;
+        if (live && pos >= p0) {
+          cm = fmaxf(cm, cp);
+          if (c_all != nullptr && wq == 0) c_all[bh * W + (int64_t)sbk * 16 + wt] = cp * kBoundPad;
+        }
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < 2 * UB; ++i) mx = fmaxf(mx, s[i]);
+    const float alpha = exp2_fast(m - mx);
+    l *= alpha;
+#pragma unroll
+    for (int e2 = 0; e2 < 16; ++e2) acc[e2] *= alpha;
+#pragma unroll
+    for (int ub = 0; ub < UB; ++ub) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float p = exp2_fast(s[2 * ub + half] - mx);
+        l += p;
+        const float pv = p * sv[ub];  // value scale folded into the weight
+        const uint4 c = half ? cur[ub].v1 : cur[ub].v0;
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pv, s8(cw[i], j), acc[4 * i + j]);
+      }
+    }
+    m = mx;
+  };
+
+  // Two register buffers in turn; the prefetch inside the loop is
+  // unconditional so each wait only covers the older buffer.
+  const int stride = NW * UB;
+  int kb0 = blo + wave * UB;
+  if (kb0 < bhi) {
+    Blk ba[UB], bb[UB];
+    load(ba, kb0);
+    while (true) {
+      if (kb0 + stride >= bhi) { step(ba, kb0); break; }
+      load(bb, kb0 + stride);
+      step(ba, kb0);
+      kb0 += stride;
+      if (kb0 + stride >= bhi) { step(bb, kb0); break; }
+      load(ba, kb0 + stride);
+      step(bb, kb0);
+      kb0 += stride;
+    }
+  }
+
+  // Merge the 8 lane groups of the wave (lanes with equal lane%8 share dims).
+  float mw = m;
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+  {
+    const float sc = exp2_fast(m - mw);
+    l *= sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] *= sc;
+  }
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += __shfl_xor(acc[e], o);
+  }
+  cm = group_max<64>(cm);
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sm_acc[wave][lane * 16 + e] = acc[e];
+    if (lane == 0) { sm_m[wave] = mw; sm_l[wave] = l; sm_c[wave] = cm; }
+  }
+  __syncthreads();
+
+  float M = kNegBig, L = 0.f, A = 0.f, CM = 0.f;
+  if (t < D) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { M = fmaxf(M, sm_m[w]); CM = fmaxf(CM, sm_c[w]); }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = exp2_fast(sm_m[w] - M);
+      L = fmaf(sm_l[w], sc, L);
+      A = fmaf(sm_acc[w][t], sc, A);
+    }
+  }
+
+  if (nsplit > 1) {
+    float* my = part + (bh * nsplit_max + split) * PF;
+    if (t < D) my[4 + t] = A;
+    if (t == 0) { my[0] = M; my[1] = L; my[2] = CM; }
+    __threadfence();
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev = atomicAdd(&counters[bh], 1u);
+      sm_last = (prev == (uint32_t)(nsplit - 1));
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    __threadfence();
+    if (t < D) {
+      const float* pp = part + bh * nsplit_max * PF;
+      float Mg = kNegBig, CMg = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) { Mg = fmaxf(Mg, pp[sp * PF]); CMg = fmaxf(CMg, pp[sp * PF + 2]); }
+      float Lg = 0.f, Ag = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float sc = exp2_fast(pp[sp * PF] - Mg);
+        Lg = fmaf(pp[sp * PF + 1], sc, Lg);
+        Ag = fmaf(pp[sp * PF + 4 + t], sc, Ag);
+      }
+      M = Mg; L = Lg; A = Ag; CM = CMg;
+    }
+    if (t == 0) counters[bh] = 0u;
+  }
+
+  // Fold in the exact staging tokens (positions 16*nb .. n-1, row = pos mod 16).
+  const int ns = n - nb * 16;
+  if (ns > 0) {
+    // Scores: 16 lanes per token, 8 bf16 each (256 threads = 16 tokens).
+    const int tok = t >> 4, v16 = t & 15;
+    float d = 0.f;
+    if (tok < ns) {
+      float f[8], qv[8];
+      unpack8(reinterpret_cast<const uint4*>(kst + (bh * 16 + tok) * D)[v16], f);
+      unpack8(reinterpret_cast<const uint4*>(q + bh * D)[v16], qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qv[e] * qscale, f[e], d);
+    }
+    d = group_sum<16>(d);
+    if (v16 == 0 && tok < 16) sm_s[tok] = tok < ns ? d : -INFINITY;
+    __syncthreads();
+    if (t < D) {
+      float ms = -INFINITY;
+      for (int i = 0; i < ns; ++i) ms = fmaxf(ms, sm_s[i]);
+      const float Mn = fmaxf(M, ms);
+      const float sc = exp2_fast(M - Mn);
+      L *= sc;
+      A *= sc;
+      for (int i = 0; i < ns; ++i) {
+        const float p = exp2_fast(sm_s[i] - Mn);
+        L += p;
+        A = fmaf(p, bf16_to_f32(vst[(bh * 16 + i) * D + t]), A);
+      }
+    }
+  }
+  if (t < D) out[bh * D + t] = L > 0.f ? A / L : 0.f;
+  if (t == 0) cmax_out[bh] = CM * kBoundPad;
+}
+
+__global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+}  // namespace
+
+int decode_int8_round_blocks() { return 4 /*NW*/ * 2 /*UB*/; }
+
+hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax, float* c_all,
+                              void* ws, const SplitPlan& plan, hipStream_t s) {
+  constexpr int NW = 4, UB = 2;
+  if (c_all != nullptr) {
+    const int64_t n = (int64_t)c.B * c.H * c.W;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1 << 16) blocks = 1 << 16;
+    hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)blocks), dim3(256), 0, s, c_all, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + counters_bytes(c));
+  hipLaunchKernelGGL((decode_int8_kernel<NW, UB>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
+                     reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
+                     c.v_scale, c.witness, reinterpret_cast<const uint16_t*>(c.k_stage),
+                     reinterpret_cast<const uint16_t*>(c.v_stage), c.next_position,
+                     reinterpret_cast<const uint16_t*>(q), out, cmax, c_all, part, counters, c.H, c.W,
+                     plan.unit_per_split, plan.nsplit_max);
+  return hipGetLastError();
+}
+
+}  // namespace swa

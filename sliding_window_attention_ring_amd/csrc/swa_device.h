@@ -1,0 +1,98 @@
+// Device helpers shared by the gfx950 kernels: wave64 lane-group reductions
+// on DPP row operations, bf16/fp16 unpacking and directed rounding to fp16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+constexpr int kWave = 64;
+// log2(e): scores are kept in base 2 so the softmax uses the native exp2.
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
+// every lane of a group ends with the group total.  Steps: swap neighbours,
+// swap pairs (quad permutes), mirror within half-rows of 8, mirror within
+// rows of 16, then cross-row exchanges.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
+  if constexpr (G >= 16) x += dpp_f32<0x140>(x); // row_mirror
+  if constexpr (G >= 32) x += __shfl_xor(x, 16);
+  if constexpr (G >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int G>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (G >= 2) x = fmaxf(x, dpp_f32<0xB1>(x));
+  if constexpr (G >= 4) x = fmaxf(x, dpp_f32<0x4E>(x));
+  if constexpr (G >= 8) x = fmaxf(x, dpp_f32<0x141>(x));
+  if constexpr (G >= 16) x = fmaxf(x, dpp_f32<0x140>(x));
+  if constexpr (G >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (G >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 is the high half of an fp32: unpacking is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Eight fp32 from a 16-byte vector of eight bf16 (element order kept).
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// Four fp32 from a 16-byte vector of four fp32.
+__device__ __forceinline__ void unpack4(const uint4 v, float (&f)[4]) {
+  f[0] = __builtin_bit_cast(float, v.x); f[1] = __builtin_bit_cast(float, v.y);
+  f[2] = __builtin_bit_cast(float, v.z); f[3] = __builtin_bit_cast(float, v.w);
+}
+
+// Signed byte j of a 32-bit word as fp32 (one sign-extending convert).
+__device__ __forceinline__ float s8(uint32_t w, int j) {
+  return (float)(int32_t)(int8_t)(w >> (8 * j));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Nonnegative fp32 -> fp16 bits, rounded toward +infinity (never below x).
+__device__ __forceinline__ uint16_t f32_to_f16_up(float x) {
+  _Float16 h = (_Float16)x;  // round to nearest even
+  uint16_t bits = __builtin_bit_cast(uint16_t, h);
+  if ((float)h < x) bits = (uint16_t)(bits + 1);  // next fp16 toward +inf (x >= 0)
+  return bits;
+}
+
+// Streaming 16-byte load that does not keep the line in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+}  // namespace swa

@@ -1,0 +1,46 @@
+// Host-side launch interface between the C-ABI layer and the kernel files.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/swa.h"
+
+namespace swa {
+
+// Decode split policy: tokens (bf16/fp32) or 16-token blocks (INT8) per
+// work-group, and the largest split count any (b, h) can need.
+struct SplitPlan {
+  int unit_per_split;  // rows (bf16/fp32) or blocks (INT8) per work-group
+  int nsplit_max;
+};
+
+SplitPlan plan_decode(const swa_cache& c);
+
+// Floats per split partial: m, l, cmax, pad, acc[D].
+inline int partial_floats(int D) { return D + 4; }
+
+// Byte offset of the partials inside the workspace (after the counters).
+inline size_t counters_bytes(const swa_cache& c) {
+  size_t n = (size_t)c.B * c.H * sizeof(uint32_t);
+  return (n + 255) & ~(size_t)255;
+}
+
+hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void* v_new, int T,
+                              hipStream_t s);
+hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void* v_new, int T,
+                              hipStream_t s);
+hipError_t launch_advance(const swa_cache& c, int T, hipStream_t s);
+
+hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws,
+                         const SplitPlan& plan, hipStream_t s);
+hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax,
+                              float* c_all, void* ws, const SplitPlan& plan, hipStream_t s);
+
+hipError_t launch_reset(const swa_cache& c, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_validate(const swa_cache& c, int32_t* violations, hipStream_t s);
+
+}  // namespace swa

@@ -1,0 +1,116 @@
+"""Helpers for the GPU parity tests: device checks, host copies of device
+tensors, and comparisons of the HIP results with the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bits, decoder, int8 as oint8
+
+TOL = 2e-3  # max abs error of outputs vs the float64 oracle on the same inputs
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sliding_window_attention_ring_amd as swa
+    swa.lib()  # fails loudly if the HIP library is missing
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """Host copy with the storage bits: bf16/fp16 -> uint16, others as is."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 values of a bf16/fp32 tensor (host)."""
+    return bits.to_f64(host_bits(t))
+
+
+def check_ring_rows(cache, k_in: np.ndarray, v_in: np.ndarray, n: np.ndarray):
+    """bf16/fp32 cache: pos, next_position and every live slot's K/V bits equal
+    what the ring must hold after n[b] appends of rows k_in[b][h][p] (bits)."""
+    pos = host_bits(cache.pos)
+    npos = host_bits(cache.next_position)
+    kk, vv = host_bits(cache.k), host_bits(cache.v)
+    for b in range(cache.B):
+        assert npos[b] == n[b], (b, npos[b], n[b])
+        exp = decoder.expected_ring(np.arange(n[b]), cache.W)
+        np.testing.assert_array_equal(pos[b], exp)
+        live = np.nonzero(exp >= 0)[0]
+        np.testing.assert_array_equal(kk[b][:, live], k_in[b][:, exp[live]])
+        np.testing.assert_array_equal(vv[b][:, live], v_in[b][:, exp[live]])
+
+
+def oracle_out(k64: np.ndarray, v64: np.ndarray, q64: np.ndarray, n: int, W: int) -> np.ndarray:
+    """Masked full-history attention of the query at step n-1 for every head:
+    k64, v64 [H, >=n, D]; q64 [H, D]."""
+    hist = decoder.SequenceHistory(k64.shape[0], k64.shape[2])
+    hist.append(k64[:, :n], v64[:, :n])
+    return hist.attend(q64, W)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, what: str, tol: float = TOL):
+    err = float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref))) if ref.size else 0.0
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol}"
+    return err
+
+
+def check_int8_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, n: int):
+    """INT8 cache of (b, h): codes, scales, slot positions bit-exact vs the
+    oracle; stored witness never below the exact band norm and within one
+    fp16 step above it; staging rows equal the input bits."""
+    st = decoder.expected_int8_store(k64, v64, n, cache.W)
+    kc = host_bits(cache.k[b, h]); vc = host_bits(cache.v[b, h])
+    ks = host_bits(cache.k_scale[b, h]); vs = host_bits(cache.v_scale[b, h])
+    wit = host_bits(cache.witness[b, h]).view(np.float16).astype(np.float64)
+    pos = host_bits(cache.pos[b])
+    np.testing.assert_array_equal(pos, st["slot_pos"])
+    live = np.nonzero(st["slot_pos"] >= 0)[0]
+    np.testing.assert_array_equal(kc[live], st["k_codes"][live])
+    np.testing.assert_array_equal(vc[live], st["v_codes"][live])
+    lb = np.unique(live // 16)
+    np.testing.assert_array_equal(ks[lb], st["k_scale"][lb])
+    np.testing.assert_array_equal(vs[lb], st["v_scale"][lb])
+    we, wg = st["witness"][live], wit[live]
+    assert np.all(wg >= we), "stored witness below the exact band norm"
+    assert np.all(wg <= we * (1 + 2.0 ** -9) + 2.0 ** -24), "stored witness not tight"
+    ksg = host_bits(cache.k_stage[b, h]); vsg = host_bits(cache.v_stage[b, h])
+    for p in st["staged_positions"]:
+        np.testing.assert_array_equal(bits.to_f64(ksg[p % 16]), k64[p])
+        np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])
+
+
+def check_int8_decode(out, cmax, c_all, b, h, q64, k64, v64, n, W, what=""):
+    """INT8 decode of (b, h) vs the oracle: output within TOL; cmax and every
+    per-slot c_t sound (>= the true logit error of that token) and tight."""
+    res = oint8.int8_decode(q64, k64, v64, n, W)
+    err = assert_close(out, res["out"], f"int8 out {what} b={b} h={h}")
+    e, c = res["e"], res["c"]
+    emax = float(np.max(e)) if e.size else 0.0
+    assert cmax >= emax, f"cmax {cmax} below the true max logit error {emax}"
+    assert cmax <= res["cmax"] * (1 + 2.0 ** -9) + 1e-30, (cmax, res["cmax"])
+    if c_all is not None:
+        slots = res["positions"] % W
+        cg = np.asarray(c_all, dtype=np.float64)[slots]
+        assert np.all(cg >= e), "per-token bound below the true logit error"
+        assert np.all(cg <= c * (1 + 2.0 ** -9) + 1e-30), "per-token bound not tight"
+        quant = res["positions"] < 16 * (n // 16)
+        assert not np.any(cg[~quant]), "exact (staged) tokens must have c = 0"
+        vis = np.zeros(W, dtype=bool)
+        vis[slots[quant]] = True
+        assert not np.any(np.asarray(c_all)[~vis]), "slots without a visible quantized token must be 0"
+    return err

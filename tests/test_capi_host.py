@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/swa.h declares, and rejects bad arguments before launching anything
+(none of these calls reaches the GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+LIB = os.path.join(ROOT, "sliding_window_attention_ring_amd", "libswa.so")
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libswa.so not built")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "swa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_and_exports_agree():
+    from sliding_window_attention_ring_amd import _capi
+    decl = declared_functions()
+    assert decl == set(_capi.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert decl <= exported
+    L = _capi.lib()
+    for name in decl:
+        assert hasattr(L, name)
+
+
+def desc(**kw):
+    from sliding_window_attention_ring_amd._capi import SwaCacheDesc
+    base = dict(kind=0, B=2, H=4, D=128, W=64, reserved=0, k=0x10000, v=0x20000, pos=0x30000,
+                next_position=0x40000, k_scale=0x50000, v_scale=0x60000, witness=0x70000,
+                k_stage=0x80000, v_stage=0x90000)
+    base.update(kw)
+    return SwaCacheDesc(**base)
+
+
+def test_status_strings():
+    from sliding_window_attention_ring_amd import _capi
+    for code in range(-6, 1):
+        assert _capi.status_string(code) and _capi.status_string(code) != "unknown status"
+    assert _capi.status_string(-99) == "unknown status"
+
+
+def test_argument_checks_return_codes():
+    from sliding_window_attention_ring_amd._capi import lib
+    L = lib()
+    p = ctypes.byref
+    d = desc()
+    A16, ODD = ctypes.c_void_p(0xA0000), ctypes.c_void_p(0xA0004)
+    ws = ctypes.c_void_p(0xB0000)
+    assert L.kv_append(None, A16, A16, 1, None) == -2                       # NULL cache
+    assert L.kv_append(p(desc(B=0)), A16, A16, 1, None) == -1               # B < 1
+    assert L.kv_append(p(desc(reserved=1)), A16, A16, 1, None) == -1
+    assert L.kv_append(p(desc(D=100)), A16, A16, 1, None) == -4             # head_dim
+    assert L.kv_append(p(desc(kind=7)), A16, A16, 1, None) == -4
+    assert L.kv_append(p(desc(kind=2, W=20)), A16, A16, 1, None) == -1      # INT8 W % 16
+    assert L.kv_append(p(desc(kind=2, D=64)), A16, A16, 1, None) == -4
+    assert L.kv_append(p(desc(kind=2, witness=None)), A16, A16, 1, None) == -2
+    assert L.kv_append(p(desc(k=0x10004)), A16, A16, 1, None) == -3         # alignment
+    assert L.kv_append(p(d), ODD, A16, 1, None) == -3
+    assert L.kv_append(p(d), None, A16, 1, None) == -2
+    assert L.kv_append(p(d), A16, A16, -1, None) == -1
+    assert L.kv_append(p(d), A16, A16, 0, None) == 0                        # T = 0: no-op
+    need = L.swa_workspace_bytes(p(d))
+    assert need > 0 and L.swa_workspace_bytes(p(desc(D=100))) == 0
+    assert L.decode_attn(p(d), A16, A16, ws, need - 1, None) == -5           # small workspace
+    assert L.decode_attn(p(d), ODD, A16, ws, need, None) == -3
+    assert L.decode_attn(p(desc(kind=2)), A16, A16, ws, need, None) == -4    # INT8 needs the witness entry
+    assert L.decode_attn_int8_witness(p(d), A16, A16, A16, None, ws, need, None) == -4
+    assert L.decode_attn_int8_witness(p(desc(kind=2)), A16, A16, None, None, ws, 1 << 30, None) == -2
+    assert L.swa_validate(p(d), None, None) == -2
+    assert L.swa_workspace_init(None, 64, None) == -2
+    assert L.swa_workspace_init(ODD, 64, None) == -3
+    assert L.swa_workspace_init(A16, 0, None) == 0
+
+
+def test_workspace_size_follows_split_plan():
+    """Workspace = 256-byte-aligned counters + B*H*nsplit*(D+4) floats."""
+    from sliding_window_attention_ring_amd._capi import lib
+    L = lib()
+    for kw in [dict(kind=0, B=16, H=32, D=128, W=32768), dict(kind=2, B=16, H=32, D=128, W=32768),
+               dict(kind=1, B=1, H=2, D=16, W=4), dict(kind=0, B=4, H=8, D=128, W=131072)]:
+        d = desc(**kw)
+        nb = L.swa_workspace_bytes(ctypes.byref(d))
+        counters = (kw["B"] * kw["H"] * 4 + 255) // 256 * 256
+        per = kw["B"] * kw["H"] * (kw["D"] + 4) * 4
+        assert (nb - counters) % per == 0 and (nb - counters) // per >= 1

@@ -196,3 +196,34 @@ def test_storage_format(golden):
     assert nb * 2 == g["witness_bytes_per_token_head"]  # fp16 per band
     per_token_head = 2 * d * 1 + nb * 2 + 2 * 4 / int8.BLOCK  # codes K+V, witness, scales
     assert per_token_head == 288.5
+
+
+def test_codes_use_correctly_rounded_division_near_ties():
+    """Near rounding ties the float32 quotient x/s (correctly rounded, computed
+    here from exact rationals) decides the code; a reciprocal multiply would
+    differ on some of these inputs."""
+    rng = np.random.default_rng(77)
+    checked = 0
+    for _ in range(400):
+        s = np.float32(rng.uniform(0.01, 0.05))
+        k = int(rng.integers(-126, 126))
+        x0 = np.float32((k + 0.5) * float(s))
+        for x in (np.nextafter(x0, np.float32(-1e9)), x0, np.nextafter(x0, np.float32(1e9))):
+            quot = nearest_f32(Fraction(float(x)) / Fraction(float(s)))
+            expect = min(range(-127, 128), key=lambda c: (abs(Fraction(float(quot)) - c), c & 1))
+            assert int(int8.block_codes(np.array([x], dtype=np.float32), s)[0]) == expect
+            checked += 1
+    assert checked == 1200
+
+
+def test_rope_angle_from_definition():
+    """theta_i = base^(-2i/D): with D = 128 and base 10000, pair i = 32 turns by
+    exactly 10000^(-1/2) = 0.01 rad per position; pair 0 by 1 rad."""
+    e = np.zeros(128)
+    e[64] = 1.0
+    y = rope.rope_interleaved(e, 1)
+    assert y[64] == pytest.approx(np.cos(0.01), abs=1e-15) and y[65] == pytest.approx(np.sin(0.01), abs=1e-15)
+    e0 = np.zeros(128)
+    e0[0] = 1.0
+    y0 = rope.rope_interleaved(e0, 3)
+    assert y0[0] == pytest.approx(np.cos(3.0), abs=1e-15) and y0[1] == pytest.approx(np.sin(3.0), abs=1e-15)
