@@ -1,0 +1,265 @@
+"""Decode-step benchmark on one MI355X.
+
+A step is one pass of the decode hot path over the whole batch: append one
+token per sequence (``kv_append``), then one query per sequence attends to
+the cache (``decode_attn_int8_witness`` for INT8 workloads, ``decode_attn``
+otherwise).  The default workload is the INT8 cache with the witness bound at
+32768 context (B=16, H=32, D=128), prefilled with 32768 rotary keys.
+
+Prints ONE JSON line on stdout.  ``value`` is the whole step's algorithmic
+HBM bytes per second (GB/s); ``roofline`` reports the decode kernel alone,
+timed with HIP events on its launch stream; ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+       [--workload NAME] [--no-cpu-baseline] [--calibrate-copy]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn achieved HBM GB/s (% of peak) + tokens·heads/s at 32k ctx"
+PEAK_GBS = 8000.0  # MI355X HBM3E peak
+CSRC = os.path.join(ROOT, "sliding_window_attention_ring_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kind: str) -> str:
+    files = ["swa_device.h", "swa_decode_int8.hip" if kind == "int8" else "swa_decode.hip"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kind: str):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{workload}_decode_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith("#"):
+            a, b = ln.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash(kind):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def step_bytes(wl, n_after: int):
+    """Algorithmic HBM bytes of one step whose append brings next_position to
+    n_after: (decode bytes, append bytes, visible tokens per (b, h))."""
+    BH, D = wl.B * wl.H, wl.D
+    vis = min(wl.W, n_after)
+    q_out = BH * D * 2 + BH * D * 4
+    if wl.kind == "int8":
+        staged = n_after % 16
+        quant = vis - staged
+        dec = BH * (quant * (2 * D + 2 * D // 8 + 2 * 4 / 16) + staged * 2 * D * 2) + q_out + BH * 4
+        app = BH * 2 * D * 2 * 2  # read the new rows, write them to staging
+        if n_after % 16 == 0:     # a block completes: read 16 staged rows, write codes/witness/scales
+            app += BH * 16 * (2 * D * 2 + 2 * D + 2 * D // 8) + BH * 2 * 4
+    else:
+        esz = 4 if wl.kind == "fp32" else 2
+        dec = BH * vis * 2 * D * esz + (BH * D * esz + BH * D * 4)
+        app = BH * 2 * D * esz * 2 + wl.B * 4
+    return dec, app, vis
+
+
+def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0):
+    """Time the oracle (as it stands) on a sample of (b, h) pairs of the same
+    workload at next_position n, one thread; GB/s of algorithmic bytes."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, bits, int8 as oint8
+    from workloads import gen
+
+    rng = np.random.default_rng(2026)
+    pairs = [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(256)]
+    q = gen.to_bits(q_of(n - 1))
+    vis = min(wl.W, n)
+    done, t_used, nbytes = 0, 0.0, 0.0
+    per_pair, _, _ = step_bytes(wl, n)
+    per_pair /= wl.B * wl.H
+    with threadpool_limits(limits=1):
+        for b, h in pairs:
+            kk = bits.to_f64(gen.to_bits(k_all[b, h, :n]))
+            vv = bits.to_f64(gen.to_bits(v_all[b, h, :n]))
+            qq = bits.to_f64(q[b, h])
+            t0 = time.perf_counter()
+            if wl.kind == "int8":
+                oint8.int8_decode(qq, kk, vv, n, wl.W)
+            else:
+                attention.masked_attention(qq, np.arange(n), kk, vv, n - 1, wl.W)
+            t_used += time.perf_counter() - t0
+            done += 1
+            nbytes += per_pair
+            if t_used >= budget_s:
+                break
+    return {
+        "value": nbytes / t_used / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} (b,h) pairs of {wl.name} at context {vis}, float64 NumPy, 1 thread, "
+                  f"{t_used:.1f} s ({done * vis / t_used:.3g} KV-token-heads/s)",
+    }
+
+
+def main():
+    from workloads import ALL, INT8_32K
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=INT8_32K.name, choices=sorted(ALL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode step needs no exchange, see the design notes for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_attention_ring_amd as swa
+    from workloads import gen
+
+    wl = ALL[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_steps = args.warmup + args.steps
+    prefill = wl.prefill or wl.W
+    total = prefill + n_steps
+    log(f"[bench] workload {wl.name}: B={wl.B} H={wl.H} D={wl.D} W={wl.W} prefill={prefill} "
+        f"steps={args.steps} warmup={args.warmup}")
+
+    t0 = time.time()
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache(wl.kind, wl.B, wl.H, wl.D, wl.W, device=dev)
+    chunk = wl.prefill_chunk or prefill
+    for c0 in range(0, prefill, chunk):
+        c1 = min(prefill, c0 + chunk)
+        swa.kv_append(cache, k_all[:, :, c0:c1].contiguous(), v_all[:, :, c0:c1].contiguous())
+    ks = [k_all[:, :, p:p + 1].contiguous() for p in range(prefill, total)]
+    vs = [v_all[:, :, p:p + 1].contiguous() for p in range(prefill, total)]
+    qs = [gen.query(wl, p, device=dev) for p in range(prefill, total)]
+    ws = cache.workspace()
+    out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.float32, device=dev)
+    cmax = torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.1f} s")
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(i):
+        swa.kv_append(cache, ks[i], vs[i])
+        if wl.kind == "int8":
+            swa.decode_attn_int8_witness(cache, qs[i], out=out, cmax=cmax, ws=ws)
+        else:
+            swa.decode_attn(cache, qs[i], out=out, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    dec_bytes = app_bytes = vis_tokens = 0.0
+    for i in range(args.steps):
+        d, a, vis = step_bytes(wl, prefill + args.warmup + i + 1)
+        dec_bytes, app_bytes, vis_tokens = dec_bytes + d, app_bytes + a, vis_tokens + vis
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        j = args.warmup + i
+        swa.kv_append(cache, ks[j], vs[j])
+        evs[i][0].record(stream)
+        if wl.kind == "int8":
+            swa.decode_attn_int8_witness(cache, qs[j], out=out, cmax=cmax, ws=ws)
+        else:
+            swa.decode_attn(cache, qs[j], out=out, ws=ws)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = (dec_bytes + app_bytes) / elapsed / 1e9
+    achieved = (dec_bytes / args.steps) / (kern_ms * 1e-3) / 1e9
+    BH = wl.B * wl.H
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "head_dim": wl.D, "window": wl.W,
+                   "context": min(wl.W, prefill), "kv_dtype": wl.kind,
+                   "positions": [prefill + args.warmup, prefill + n_steps - 1],
+                   "step": "kv_append(T=1) + " + ("decode_attn_int8_witness" if wl.kind == "int8"
+                                                  else "decode_attn")},
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "kv_token_heads_per_s": vis_tokens * BH / elapsed,
+        "query_token_heads_per_s": BH * args.steps / elapsed,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": read_traffic(wl.name, wl.kind),
+            "kernel": "decode_int8_kernel" if wl.kind == "int8" else "decode_kernel",
+            "kernel_ms": round(kern_ms, 4),
+            "algorithmic_bytes_per_launch": dec_bytes / args.steps,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl, k_all, v_all, lambda p: gen.query(wl, p), prefill)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -100,14 +100,13 @@ int kv_append(const swa_cache *c, const void *k_new, const void *v_new, int32_t 
 /* Decode attention for one query per sequence over the last min(W, n) tokens,
  * n = next_position[b] (append first, then attend: airsota.com §三 steps 2-4;
  * scores q.k/sqrt(D), max-subtracted softmax, weighted V).  BF16 and FP32
- * kinds.  Split over the context with an online softmax; the last work-group
- * of each (b, h) merges the splits.
+ * kinds.  Split over the context with an online softmax; a second kernel
+ * merges the splits of each (b, h).
  *  q    [B][H][D]  cache input dtype
  *  out  [B][H][D]  fp32; a sequence with n = 0 gets zeros
- *  ws   device workspace of ws_bytes >= swa_workspace_bytes(c), zero-filled
- *       once by swa_workspace_init before its first use; each call leaves it
- *       ready for the next.  Calls sharing one workspace must be ordered on
- *       one stream. */
+ *  ws   device workspace of ws_bytes >= swa_workspace_bytes(c) holding the
+ *       split partials; its contents need no initialization.  Calls sharing
+ *       one workspace must be ordered on one stream. */
 int decode_attn(const swa_cache *c, const void *q, float *out, void *ws, size_t ws_bytes,
                 void *stream);
 
@@ -126,12 +125,12 @@ int decode_attn(const swa_cache *c, const void *q, float *out, void *ws, size_t 
 int decode_attn_int8_witness(const swa_cache *c, const void *q, float *out, float *cmax,
                              float *c_all, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes the decode entry points need for this cache shape (split
- * partials and per-(b,h) arrival counters).  0 for an invalid descriptor. */
+/* Workspace bytes the decode entry points need for this cache shape (the
+ * split partials: B*H*nsplit*(D+4) floats).  0 for an invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);
 
-/* Zero-fill a workspace before its first use.  Errors: SWA_ENULL, SWA_EALIGN,
- * SWA_EHIP. */
+/* Zero-fill a workspace (optional: the decode entry points overwrite what
+ * they read).  Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
 int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Debug check of the position invariant (framerc.cn §3.2 PositionInvariant,

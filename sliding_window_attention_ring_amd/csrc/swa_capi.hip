@@ -47,14 +47,22 @@ int check_cache(const swa_cache* c) {
   return SWA_OK;
 }
 
-// Target number of work-groups per decode launch: enough to fill 256 CUs
-// several times over.  SWA_TARGET_WGS overrides it (read once per process,
-// so workspace sizes stay consistent).
+// Target number of decode work-groups per launch: two per compute unit of
+// the device (512 on MI355X).  Measured on MI355X, fewer and longer splits
+// stream HBM better than many short ones (each split pays a query load and
+// a partial write, and the merge reads every partial), and two 4-wave
+// work-groups per CU already keep enough loads in flight.  SWA_TARGET_WGS
+// overrides it; read once per process so workspace sizes stay consistent.
 int target_wgs() {
   static int v = [] {
     const char* s = getenv("SWA_TARGET_WGS");
     int x = s ? atoi(s) : 0;
-    return x > 0 ? x : 4096;
+    if (x > 0) return x;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    return 2 * cus;
   }();
   return v;
 }
@@ -169,8 +177,7 @@ const char* swa_status_string(int status) {
 size_t swa_workspace_bytes(const swa_cache* c) {
   if (check_cache(c) != SWA_OK) return 0;
   const SplitPlan p = plan_decode(*c);
-  return counters_bytes(*c) +
-         (size_t)c->B * c->H * (size_t)p.nsplit_max * partial_floats(c->D) * sizeof(float);
+  return (size_t)c->B * c->H * (size_t)p.nsplit_max * partial_floats(c->D) * sizeof(float);
 }
 
 int swa_cache_reset(const swa_cache* c, void* stream) {

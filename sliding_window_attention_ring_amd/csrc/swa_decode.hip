@@ -21,9 +21,12 @@
 // * dot products are reduced inside each LPR-lane group with DPP row ops;
 //   the online softmax keeps a running (max, sum, acc) per lane group in
 //   base 2;
-// * lane groups, then waves (through LDS), then splits are merged with the
-//   log-sum-exp rule; the last work-group of each (b, h) to finish (an
-//   arrival counter in the workspace) merges the splits and normalizes.
+// * lane groups, then waves (through LDS) are merged with the log-sum-exp
+//   rule; a (b, h) served by one split writes its output directly, otherwise
+//   each split writes a partial (m, l, acc[D]) and a small second kernel
+//   merges the splits and normalizes.  The kernel boundary makes the
+//   partials visible across the XCDs' separate L2 caches, so no work-group
+//   needs a device-wide fence (each would write back and invalidate its L2).
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -81,7 +84,7 @@ template <typename T, int D, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
     const uint4* __restrict__ q, float* __restrict__ out, float* __restrict__ part,
-    uint32_t* __restrict__ counters, int H, int W, int chunk, int nsplit_max) {
+    int H, int W, int chunk, int nsplit_max) {
   using F = RowFmt<T>;
   constexpr int EPV = F::kEpv;
   constexpr int VPR = D / EPV;          // 16-byte vectors per row
@@ -93,7 +96,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
-  __shared__ int sm_last;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -101,11 +103,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   const int64_t bh = (int64_t)b * H + h;
   const int n = np[b];
   const int len = n < W ? n : W;
-  if (len <= 0) {  // empty cache: defined as a zero output
-    if (split == 0)
-      for (int t = threadIdx.x; t < D; t += NW * 64) out[bh * D + t] = 0.f;
-    return;
-  }
+  if (len <= 0) return;  // empty cache: the merge kernel writes zeros
   const int nsplit = (len + chunk - 1) / chunk;
   if (split >= nsplit) return;
   const int r0 = split * chunk;
@@ -224,45 +222,44 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     return;
   }
 
-  // Publish this split's partial, then count arrivals for (b, h).
+  // Publish this split's partial for the merge kernel.
   float* my = part + (bh * nsplit_max + split) * PF;
   if (t < D) my[4 + t] = A;
   if (t == 0) { my[0] = M; my[1] = L; }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const uint32_t prev = atomicAdd(&counters[bh], 1u);
-    sm_last = (prev == (uint32_t)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
+}
 
-  // Last arrival: log-sum-exp merge of all splits, normalize, reset the counter.
-  if (t < D) {
-    const float* pp = part + bh * nsplit_max * PF;
-    float Mg = kNegBig;
-    for (int sp = 0; sp < nsplit; ++sp) Mg = fmaxf(Mg, pp[sp * PF]);
-    float Lg = 0.f, Ag = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float sc = exp2_fast(pp[sp * PF] - Mg);
-      Lg = fmaf(pp[sp * PF + 1], sc, Lg);
-      Ag = fmaf(pp[sp * PF + 4 + t], sc, Ag);
-    }
-    out[bh * D + t] = Ag / Lg;
-  }
-  if (t == 0) counters[bh] = 0u;
+// Log-sum-exp merge of the split partials of one (b, h); thread t owns dim t.
+// A (b, h) served by a single split already has its output; an empty cache
+// gets zeros.
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(const int32_t* __restrict__ np,
+                                                  const float* __restrict__ part, float* __restrict__ out,
+                                                  int H, int W, int chunk, int nsplit_max) {
+  constexpr int PF = D + 4;
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
+  const int n = np[b];
+  const int len = n < W ? n : W;
+  if (len <= 0) { out[bh * D + t] = 0.f; return; }
+  const int nsplit = (len + chunk - 1) / chunk;
+  if (nsplit == 1) return;
+  float M, L, A;
+  merge_partials<PF>(part + bh * nsplit_max * PF, nsplit, t, M, L, A);
+  out[bh * D + t] = A / L;
 }
 
 template <typename T, int D>
 hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, const SplitPlan& plan,
                       hipStream_t s) {
   constexpr int NW = 4, U = 4;
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + counters_bytes(c));
+  float* part = reinterpret_cast<float*>(ws);
   hipLaunchKernelGGL((decode_kernel<T, D, NW, U>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
                      reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v),
-                     c.next_position, reinterpret_cast<const uint4*>(q), out, part, counters, c.H, c.W,
+                     c.next_position, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,
+                     plan.unit_per_split, plan.nsplit_max);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(c.H, c.B), dim3(D), 0, s, c.next_position, part, out, c.H, c.W,
                      plan.unit_per_split, plan.nsplit_max);
   return hipGetLastError();
 }

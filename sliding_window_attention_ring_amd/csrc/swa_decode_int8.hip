@@ -14,10 +14,13 @@
 // committed blocks of the ring: blocks k0..nb-1 with k0 = (n-len)/16, block k
 // in slots [16k mod W, +16); in block k0 the positions below n-len are masked.
 // The newest n mod 16 tokens are exact bf16 rows in the staging area and
-// carry c_t = 0; the merging work-group folds them in.
+// carry c_t = 0; the merge kernel folds them in.
 //
 // Layout of the work: grid (split, h, b), NW waves; a split owns `cb`
-// consecutive blocks; a wave takes UB blocks per iteration.  Per block a
+// consecutive blocks; a wave takes UB blocks per iteration.  Every split
+// writes a partial (m, l, cmax, acc[D]); a second kernel merges the splits
+// of each (b, h) -- the kernel boundary makes the partials visible across
+// the XCDs' L2 caches without any device-wide fence.  Per block a
 // lane loads 2x16 B of key codes and 2x16 B of value codes (8 lanes per
 // 128-byte row, rows g and g+8) and 8 B of witness (4 lanes per token).
 #include "swa_device.h"
@@ -41,14 +44,11 @@ struct Blk {
 template <int NW, int UB>
 __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
-    const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const uint16_t* __restrict__ kst,
-    const uint16_t* __restrict__ vst, const int32_t* __restrict__ np, const uint16_t* __restrict__ q,
-    float* __restrict__ out, float* __restrict__ cmax_out, float* __restrict__ c_all,
-    float* __restrict__ part, uint32_t* __restrict__ counters, int H, int W, int cb, int nsplit_max) {
+    const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const int32_t* __restrict__ np,
+    const uint16_t* __restrict__ q, float* __restrict__ c_all, float* __restrict__ part, int H, int W, int cb,
+    int nsplit_max) {
   __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
   __shared__ float sm_acc[NW][D];
-  __shared__ float sm_s[16];
-  __shared__ int sm_last;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -245,38 +245,39 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     }
   }
 
-  if (nsplit > 1) {
-    float* my = part + (bh * nsplit_max + split) * PF;
-    if (t < D) my[4 + t] = A;
-    if (t == 0) { my[0] = M; my[1] = L; my[2] = CM; }
-    __threadfence();
-    __syncthreads();
-    if (t == 0) {
-      const uint32_t prev = atomicAdd(&counters[bh], 1u);
-      sm_last = (prev == (uint32_t)(nsplit - 1));
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    __threadfence();
-    if (t < D) {
-      const float* pp = part + bh * nsplit_max * PF;
-      float Mg = kNegBig, CMg = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) { Mg = fmaxf(Mg, pp[sp * PF]); CMg = fmaxf(CMg, pp[sp * PF + 2]); }
-      float Lg = 0.f, Ag = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float sc = exp2_fast(pp[sp * PF] - Mg);
-        Lg = fmaf(pp[sp * PF + 1], sc, Lg);
-        Ag = fmaf(pp[sp * PF + 4 + t], sc, Ag);
-      }
-      M = Mg; L = Lg; A = Ag; CM = CMg;
-    }
-    if (t == 0) counters[bh] = 0u;
-  }
+  float* my = part + (bh * nsplit_max + split) * PF;
+  if (t < D) my[4 + t] = A;
+  if (t == 0) { my[0] = M; my[1] = L; my[2] = CM; }
+}
 
-  // Fold in the exact staging tokens (positions 16*nb .. n-1, row = pos mod 16).
+// Merge of one (b, h): log-sum-exp over the split partials, then the exact
+// staging tokens (positions 16*nb .. n-1, row = position mod 16, c_t = 0),
+// then normalization.  256 threads; thread t < D owns output dim t.
+__global__ __launch_bounds__(256) void merge_int8_kernel(
+    const int32_t* __restrict__ np, const float* __restrict__ part, const uint16_t* __restrict__ kst,
+    const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q, float* __restrict__ out,
+    float* __restrict__ cmax_out, int H, int W, int cb, int nsplit_max) {
+  __shared__ float sm_s[16];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
+  const int n = np[b];
+  const int len = n < W ? n : W;
+  const int nb = n / 16;
+  const int k0 = (n - len) / 16;
+  const int nbr = nb > k0 ? nb - k0 : 0;
+  int nsplit = (nbr + cb - 1) / cb;
+  if (nsplit < 1) nsplit = 1;
+  const float qscale = kLog2e / sqrtf((float)D);
+
+  float M = kNegBig, L = 0.f, A = 0.f, CM = 0.f;
+  if (t < D) {
+    const float* pp = part + bh * nsplit_max * PF;
+    merge_partials<PF>(pp, nsplit, t, M, L, A);
+    for (int sp = 0; sp < nsplit; ++sp) CM = fmaxf(CM, pp[sp * PF + 2]);
+  }
   const int ns = n - nb * 16;
   if (ns > 0) {
-    // Scores: 16 lanes per token, 8 bf16 each (256 threads = 16 tokens).
+    // Scores: 16 lanes per staged token, 8 bf16 each (256 threads = 16 tokens).
     const int tok = t >> 4, v16 = t & 15;
     float d = 0.f;
     if (tok < ns) {
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
       for (int e = 0; e < 8; ++e) d = fmaf(qv[e] * qscale, f[e], d);
     }
     d = group_sum<16>(d);
-    if (v16 == 0 && tok < 16) sm_s[tok] = tok < ns ? d : -INFINITY;
+    if (v16 == 0) sm_s[tok] = tok < ns ? d : -INFINITY;
     __syncthreads();
     if (t < D) {
       float ms = -INFINITY;
@@ -327,14 +328,17 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + counters_bytes(c));
+  float* part = reinterpret_cast<float*>(ws);
   hipLaunchKernelGGL((decode_int8_kernel<NW, UB>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
                      reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
-                     c.v_scale, c.witness, reinterpret_cast<const uint16_t*>(c.k_stage),
-                     reinterpret_cast<const uint16_t*>(c.v_stage), c.next_position,
-                     reinterpret_cast<const uint16_t*>(q), out, cmax, c_all, part, counters, c.H, c.W,
-                     plan.unit_per_split, plan.nsplit_max);
+                     c.v_scale, c.witness, c.next_position, reinterpret_cast<const uint16_t*>(q), c_all, part,
+                     c.H, c.W, plan.unit_per_split, plan.nsplit_max);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_int8_kernel, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part,
+                     reinterpret_cast<const uint16_t*>(c.k_stage), reinterpret_cast<const uint16_t*>(c.v_stage),
+                     reinterpret_cast<const uint16_t*>(q), out, cmax, c.H, c.W, plan.unit_per_split,
+                     plan.nsplit_max);
   return hipGetLastError();
 }
 

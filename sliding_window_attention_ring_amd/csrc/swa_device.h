@@ -95,4 +95,46 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Log-sum-exp merge of split partials laid out as [nsplit][PF] floats with
+// m at 0, l at 1 and acc at 4.. (base-2 scores): M = max m_s, L = sum
+// 2^(m_s-M) l_s, A = sum 2^(m_s-M) acc_s[t].  Loads are issued eight splits
+// at a time so their latencies overlap.
+template <int PF>
+__device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int nsplit, int t, float& M,
+                                               float& L, float& A) {
+  M = -1e30f;
+  int sp = 0;
+  for (; sp + 8 <= nsplit; sp += 8) {
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m8[i] = pp[(sp + i) * PF];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, m8[i]);
+  }
+  for (; sp < nsplit; ++sp) M = fmaxf(M, pp[sp * PF]);
+  L = 0.f;
+  A = 0.f;
+  sp = 0;
+  for (; sp + 8 <= nsplit; sp += 8) {
+    float m8[8], l8[8], a8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m8[i] = pp[(sp + i) * PF];
+      l8[i] = pp[(sp + i) * PF + 1];
+      a8[i] = pp[(sp + i) * PF + 4 + t];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sc = exp2_fast(m8[i] - M);
+      L = fmaf(l8[i], sc, L);
+      A = fmaf(a8[i], sc, A);
+    }
+  }
+  for (; sp < nsplit; ++sp) {
+    const float sc = exp2_fast(pp[sp * PF] - M);
+    L = fmaf(pp[sp * PF + 1], sc, L);
+    A = fmaf(pp[sp * PF + 4 + t], sc, A);
+  }
+}
+
 }  // namespace swa

@@ -22,11 +22,6 @@ SplitPlan plan_decode(const swa_cache& c);
 // Floats per split partial: m, l, cmax, pad, acc[D].
 inline int partial_floats(int D) { return D + 4; }
 
-// Byte offset of the partials inside the workspace (after the counters).
-inline size_t counters_bytes(const swa_cache& c) {
-  size_t n = (size_t)c.B * c.H * sizeof(uint32_t);
-  return (n + 255) & ~(size_t)255;
-}
 
 hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void* v_new, int T,
                               hipStream_t s);

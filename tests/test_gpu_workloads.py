@@ -1,0 +1,185 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same split policy, same entry points).  Outputs are compared
+with the float64 oracle on every (b, h) pair where the oracle is fast enough,
+otherwise on seeded samples of pairs; ring state is compared bit-exactly on
+sampled sequences and checked everywhere with swa_validate.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import gen
+from oracle import attention, decoder
+from tests.gpu_util import (assert_close, check_int8_decode, check_int8_store, f64, host_bits,
+                            require_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+def prefill(swa, cache, k_all, v_all, n, chunk):
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        swa.kv_append(cache, k_all[:, :, c0:c1].contiguous(), v_all[:, :, c0:c1].contiguous())
+
+
+def test_full_cache_ragged_4096():
+    """B=8, H=32, D=128, capacity 4096, lengths U{1024..4096}: all 256 pairs."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.FULL_RAGGED
+    lens = gen.ragged_lengths(wl)
+    say("ragged lengths", lens.tolist())
+    dev = torch.device("cuda")
+    k_all = gen.tokens(wl, "k", wl.W, device=dev)
+    v_all = gen.tokens(wl, "v", wl.W, device=dev)
+    cache = swa.KVCache("bf16", wl.B, wl.H, wl.D, wl.W)
+    for b, n in enumerate(lens):
+        swa.kv_append(cache.seq_view(b), k_all[b:b + 1, :, :n].contiguous(), v_all[b:b + 1, :, :n].contiguous())
+    q = gen.query(wl, 0, device=dev)
+    out = swa.decode_attn(cache, q).cpu().numpy()
+    assert swa.validate(cache) == 0
+    assert host_bits(cache.next_position).tolist() == lens.tolist()
+    q64 = f64(q)
+    worst = 0.0
+    for b, n in enumerate(lens):
+        k64, v64 = f64(k_all[b, :, :n]), f64(v_all[b, :, :n])
+        for h in range(wl.H):
+            ref = attention.masked_attention(q64[b, h], np.arange(n), k64[h], v64[h], n - 1, wl.W)
+            worst = max(worst, assert_close(out[b, h], ref, f"ragged b={b} h={h}"))
+    say(f"ragged max abs err {worst:.2e}")
+
+
+def test_ring_w4096_positions_8192_to_8447():
+    """B=16, H=32, W=4096: prefill 0..8191 in two chunks, then 256 append+attend
+    steps; every step checks 4 sampled pairs and the position invariant; ring
+    bits of sampled sequences are compared at the first, a middle and the
+    last step.  The sampled pairs rotate over a fixed seeded set of 8."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.RING
+    dev = torch.device("cuda")
+    total = wl.prefill + wl.steps
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("bf16", wl.B, wl.H, wl.D, wl.W)
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(3)
+    pairs = [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(8)]
+    hist64 = {bh: (f64(k_all[bh[0], bh[1]]), f64(v_all[bh[0], bh[1]])) for bh in pairs}
+    worst = 0.0
+    for i in range(wl.steps):
+        p = wl.prefill + i
+        swa.kv_append(cache, k_all[:, :, p:p + 1].contiguous(), v_all[:, :, p:p + 1].contiguous())
+        q = gen.query(wl, p, device=dev)
+        out = swa.decode_attn(cache, q)
+        assert swa.validate(cache) == 0, f"step {p}"
+        outh = out.cpu().numpy()
+        qh = f64(q)
+        for j in range(4):
+            b, h = pairs[(4 * i + j) % len(pairs)]
+            k64, v64 = hist64[(b, h)]
+            ref = attention.masked_attention(qh[b, h], np.arange(p + 1), k64[:p + 1], v64[:p + 1], p, wl.W)
+            worst = max(worst, assert_close(outh[b, h], ref, f"ring step {p} b={b} h={h}"))
+        if i in (0, wl.steps // 2, wl.steps - 1):
+            b = int(rng.integers(wl.B))
+            exp = decoder.expected_ring(np.arange(p + 1), wl.W)
+            np.testing.assert_array_equal(host_bits(cache.pos[b]), exp)
+            kb = host_bits(cache.k[b])
+            np.testing.assert_array_equal(kb, host_bits(k_all[b][:, torch.as_tensor(exp, device=dev)]))
+    say(f"ring max abs err {worst:.2e}")
+
+
+def test_long_context_131072_spiked():
+    """B=4, H=8, W=131072 with 1% of keys x8: all 32 pairs."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.LONG
+    dev = torch.device("cuda")
+    k_all = gen.tokens(wl, "k", wl.W, device=dev)
+    v_all = gen.tokens(wl, "v", wl.W, device=dev)
+    cache = swa.KVCache("bf16", wl.B, wl.H, wl.D, wl.W)
+    prefill(swa, cache, k_all, v_all, wl.W, 32768)
+    q = gen.query(wl, wl.W - 1, device=dev)
+    out = swa.decode_attn(cache, q).cpu().numpy()
+    assert swa.validate(cache) == 0
+    q64 = f64(q)
+    worst = 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            k64, v64 = f64(k_all[b, h]), f64(v_all[b, h])
+            ref = attention.masked_attention(q64[b, h], np.arange(wl.W), k64, v64, wl.W - 1, wl.W)
+            worst = max(worst, assert_close(out[b, h], ref, f"long b={b} h={h}"))
+    say(f"long-context max abs err {worst:.2e}")
+
+
+def test_bf16_ctx32768_sampled():
+    """B=16, H=32, W=32768 bf16 (rotary keys): 8 sampled pairs after prefill
+    and after 3 more steps."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.BF16_32K
+    dev = torch.device("cuda")
+    total = wl.prefill + 3
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("bf16", wl.B, wl.H, wl.D, wl.W)
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(5)
+    n = wl.prefill
+    for extra in range(4):
+        if extra:
+            swa.kv_append(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous())
+            n += 1
+        q = gen.query(wl, n - 1, device=dev)
+        out = swa.decode_attn(cache, q).cpu().numpy()
+        qh = f64(q)
+        for _ in range(2 if extra else 8):
+            b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+            k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+            ref = attention.masked_attention(qh[b, h], np.arange(n), k64, v64, n - 1, wl.W)
+            assert_close(out[b, h], ref, f"bf16-32k n={n} b={b} h={h}")
+    assert swa.validate(cache) == 0
+
+
+def test_int8_witness_ctx32768():
+    """B=16, H=32, W=32768 INT8 with rotary keys: after the 32768-token
+    prefill, 3 sampled pairs get the full store check (codes, scales bits,
+    witness >= exact norms) and the per-token bound check; then 20 steps at
+    positions 32768..32787 (crossing the block boundary at 32784) check one
+    pair each."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.INT8_32K
+    dev = torch.device("cuda")
+    total = wl.prefill + wl.steps
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("int8", wl.B, wl.H, wl.D, wl.W)
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(8)
+    n = wl.prefill
+    q = gen.query(wl, n - 1, device=dev)
+    out, cmax, c_all = swa.decode_attn_int8_witness(cache, q, want_c_all=True)
+    assert swa.validate(cache) == 0
+    out, cmax, c_all, qh = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy(), f64(q)
+    for _ in range(3):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        say("int8 32k store check", b, h)
+        check_int8_store(cache, b, h, k64, v64, n)
+        check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, qh[b, h], k64, v64, n, wl.W, "32k")
+    for i in range(wl.steps):
+        swa.kv_append(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous())
+        n += 1
+        q = gen.query(wl, n - 1, device=dev)
+        out, cmax, c_all = swa.decode_attn_int8_witness(cache, q, want_c_all=True)
+        assert swa.validate(cache) == 0
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]), c_all[b, h].cpu().numpy(), b, h,
+                          f64(q[b, h]), k64, v64, n, wl.W, f"32k step n={n}")
+    say("int8 32k steps ok, last n", n)
