@@ -5,7 +5,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+# SWA_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("SWA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 
 SWA_OK = 0
 STATUS = {0: "SWA_OK", -1: "SWA_EINVAL", -2: "SWA_ENULL", -3: "SWA_EALIGN", -4: "SWA_EUNSUPPORTED",

@@ -26,9 +26,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def command(out: str = LIB) -> list:
+def command(out: str = LIB, defines=()) -> list:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        *[f"-D{d}" for d in defines],
         # packed fp32 instructions stay off: plain v_fma/v_add only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-result",
@@ -38,10 +39,14 @@ def command(out: str = LIB) -> list:
     ]
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source into ``libswa.so`` next to this file (always rebuilds)."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
+    """Compile every source into ``libswa.so`` next to this file (always rebuilds).
+
+    ``defines`` (e.g. ``["SWA_INT8_UB=4"]``) override the kernels' tuning
+    constants; ``out`` writes the library elsewhere (load it with SWA_LIB).
+    """
+    tmp = out + ".tmp"
+    cmd = command(tmp, defines)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,9 +57,14 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    build(out=a.out, defines=a.defines)

@@ -65,32 +65,22 @@ __global__ void advance_kernel(int32_t* __restrict__ np, int B, int T) {
 // the residual and the norm, so the stored value is never below the exact
 // norm.
 constexpr int kD8 = 128;
+// Chunks up to this many tokens take the single-launch path.
+constexpr int kSmallT = 16;
 
-__global__ __launch_bounds__(128) void append_int8_blocks_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const uint16_t* __restrict__ k_stage, const uint16_t* __restrict__ v_stage,
-    int8_t* __restrict__ Kc, int8_t* __restrict__ Vc, float* __restrict__ k_scale,
-    float* __restrict__ v_scale, uint16_t* __restrict__ witness, int32_t* __restrict__ pos,
-    const int32_t* __restrict__ np, int H, int W, int T) {
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int64_t n0 = np[b];
-  if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
-  const int64_t n1 = n0 + T;
-  const int64_t kb_hi = n1 / 16;
-  int64_t kb_lo = n0 / 16;
-  if (kb_hi - W / 16 > kb_lo) kb_lo = kb_hi - W / 16;
-  const int64_t kb = kb_lo + blockIdx.x;
-  if (kb >= kb_hi) return;
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+// One wave quantizes one 16-token block (index kb) of one tensor of one
+// (b, h).  Lane l handles token l/4 of the block and dims [32*(l%4), +32).
+// Rows come from the staging area for positions below n0 (the old
+// next_position) and from the new chunk otherwise.  For keys it also writes
+// the witness and, if pos_b is not null, the slot positions.
+__device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint16_t* __restrict__ src_new,
+                                                  const uint16_t* __restrict__ src_stage, int64_t n0, int T,
+                                                  int64_t kb, int64_t bh, int W, int8_t* __restrict__ codes,
+                                                  float* __restrict__ scale, uint16_t* __restrict__ witness,
+                                                  int32_t* __restrict__ pos_b) {
   const int r = lane >> 2;        // token within the block
   const int part = lane & 3;      // 32-dim quarter of the row
   const int64_t p = kb * 16 + r;
-  const int64_t bh = (int64_t)b * H + h;
-
-  const uint16_t* src_new = wave == 0 ? k_new : v_new;
-  const uint16_t* src_stage = wave == 0 ? k_stage : v_stage;
   const uint16_t* row = (p < n0) ? src_stage + (bh * 16 + (p & 15)) * kD8
                                  : src_new + (bh * T + (p - n0)) * kD8;
   const uint4* rv = reinterpret_cast<const uint4*>(row + part * 32);
@@ -108,31 +98,28 @@ __global__ __launch_bounds__(128) void append_int8_blocks_kernel(
   amax = group_max<64>(amax);
   const float s = __fdiv_rn(amax, 127.0f);
 
-  int8_t codes[32];
+  int8_t cq[32];
   float cf[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
     float c = 0.f;
     if (s > 0.f) c = fminf(fmaxf(rintf(__fdiv_rn(x[e], s)), -127.f), 127.f);
     cf[e] = c;
-    codes[e] = (int8_t)(int)c;
+    cq[e] = (int8_t)(int)c;
   }
   const int64_t slot = (kb * 16) % W + r;
-  int8_t* dst = (wave == 0 ? Kc : Vc) + (bh * W + slot) * kD8 + part * 32;
+  int8_t* dst = codes + (bh * W + slot) * kD8 + part * 32;
   uint4 packed[2];
   uint32_t* pw = reinterpret_cast<uint32_t*>(packed);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    pw[i] = (uint32_t)(uint8_t)codes[4 * i] | ((uint32_t)(uint8_t)codes[4 * i + 1] << 8) |
-            ((uint32_t)(uint8_t)codes[4 * i + 2] << 16) | ((uint32_t)(uint8_t)codes[4 * i + 3] << 24);
+    pw[i] = (uint32_t)(uint8_t)cq[4 * i] | ((uint32_t)(uint8_t)cq[4 * i + 1] << 8) |
+            ((uint32_t)(uint8_t)cq[4 * i + 2] << 16) | ((uint32_t)(uint8_t)cq[4 * i + 3] << 24);
   }
   reinterpret_cast<uint4*>(dst)[0] = packed[0];
   reinterpret_cast<uint4*>(dst)[1] = packed[1];
-  if (lane == 0) {
-    float* sc = wave == 0 ? k_scale : v_scale;
-    sc[bh * (W / 16) + (kb * 16) % W / 16] = s;
-  }
-  if (wave == 0) {
+  if (lane == 0) scale[bh * (W / 16) + (kb * 16) % W / 16] = s;
+  if (key) {
     uint16_t wb[4];
 #pragma unroll
     for (int band = 0; band < 4; ++band) {
@@ -149,8 +136,110 @@ __global__ __launch_bounds__(128) void append_int8_blocks_kernel(
     o.x = (uint32_t)wb[0] | ((uint32_t)wb[1] << 16);
     o.y = (uint32_t)wb[2] | ((uint32_t)wb[3] << 16);
     reinterpret_cast<uint2*>(witness + (bh * W + slot) * (kD8 / 8))[part] = o;
-    if (h == 0 && part == 0) pos[(int64_t)b * W + slot] = (int32_t)p;
+    if (pos_b != nullptr && part == 0) pos_b[slot] = (int32_t)p;
   }
+}
+
+// Grid (blocks, H, B), 128 threads: wave 0 commits the key block (with
+// witness), wave 1 the value block.
+__global__ __launch_bounds__(128) void append_int8_blocks_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint16_t* __restrict__ k_stage, const uint16_t* __restrict__ v_stage,
+    int8_t* __restrict__ Kc, int8_t* __restrict__ Vc, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, uint16_t* __restrict__ witness, int32_t* __restrict__ pos,
+    const int32_t* __restrict__ np, int H, int W, int T) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int64_t n0 = np[b];
+  if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
+  const int64_t n1 = n0 + T;
+  const int64_t kb_hi = n1 / 16;
+  int64_t kb_lo = n0 / 16;
+  if (kb_hi - W / 16 > kb_lo) kb_lo = kb_hi - W / 16;
+  const int64_t kb = kb_lo + blockIdx.x;
+  if (kb >= kb_hi) return;
+  const bool key = (threadIdx.x >> 6) == 0;
+  const int64_t bh = (int64_t)b * H + h;
+  commit_block_wave(threadIdx.x & 63, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, bh, W,
+                    key ? Kc : Vc, key ? k_scale : v_scale, witness,
+                    h == 0 ? pos + (int64_t)b * W : nullptr);
+}
+
+// Decode-sized INT8 append (T <= 16) in one launch: one work-group of 16
+// waves per sequence commits the (at most one) block the chunk completes
+// -- 2H wave tasks, keys and values of every head -- then stages the tokens
+// of the new incomplete block, then advances next_position.  Only this
+// work-group reads or writes next_position[b], and the barriers order the
+// staging reads of the commit before the staging writes.
+__global__ __launch_bounds__(1024) void append_int8_small_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_stage,
+    uint16_t* __restrict__ v_stage, int8_t* __restrict__ Kc, int8_t* __restrict__ Vc,
+    float* __restrict__ k_scale, float* __restrict__ v_scale, uint16_t* __restrict__ witness,
+    int32_t* __restrict__ pos, int32_t* __restrict__ np, int H, int W, int T) {
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n0 = np[b];
+  if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
+  const int64_t n1 = n0 + T;
+  const int64_t kb_hi = n1 / 16;
+  int64_t kb_lo = n0 / 16;
+  if (kb_hi - W / 16 > kb_lo) kb_lo = kb_hi - W / 16;
+  for (int64_t kb = kb_lo; kb < kb_hi; ++kb) {
+    for (int task = wave; task < 2 * H; task += 16) {
+      const int h = task >> 1;
+      const bool key = (task & 1) == 0;
+      const int64_t bh = (int64_t)b * H + h;
+      commit_block_wave(lane, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, bh, W,
+                        key ? Kc : Vc, key ? k_scale : v_scale, witness,
+                        h == 0 ? pos + (int64_t)b * W : nullptr);
+    }
+  }
+  __syncthreads();
+  int64_t lo = kb_hi * 16;
+  if (lo < n0) lo = n0;
+  const int cnt = (int)(n1 - lo);
+  constexpr int vpr = kD8 * 2 / 16;
+  const int total = H * cnt * vpr;
+  const uint4* kn = reinterpret_cast<const uint4*>(k_new);
+  const uint4* vn = reinterpret_cast<const uint4*>(v_new);
+  uint4* ks = reinterpret_cast<uint4*>(k_stage);
+  uint4* vs = reinterpret_cast<uint4*>(v_stage);
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int vec = i % vpr;
+    const int j = (i / vpr) % cnt;
+    const int h = i / (vpr * cnt);
+    const int64_t p = lo + j;
+    const int64_t bh = (int64_t)b * H + h;
+    ks[(bh * 16 + (p & 15)) * vpr + vec] = kn[(bh * T + (p - n0)) * vpr + vec];
+    vs[(bh * 16 + (p & 15)) * vpr + vec] = vn[(bh * T + (p - n0)) * vpr + vec];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) np[b] = (int32_t)n1;
+}
+
+// Decode-sized row append (T <= 16) in one launch: one work-group per
+// sequence writes the rows and positions, then advances next_position.
+__global__ __launch_bounds__(256) void append_rows_small_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint4* __restrict__ K,
+    uint4* __restrict__ V, int32_t* __restrict__ pos, int32_t* __restrict__ np, int H, int W, int T, int Tw,
+    int vpr) {
+  const int b = blockIdx.x;
+  const int64_t n0 = np[b];
+  if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
+  const int total = H * Tw * vpr;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int vec = i % vpr;
+    const int jj = (i / vpr) % Tw;
+    const int h = i / (vpr * Tw);
+    const int j = T - Tw + jj;
+    const int64_t p = n0 + j;
+    const int64_t slot = p % W;
+    const int64_t bh = (int64_t)b * H + h;
+    K[(bh * W + slot) * vpr + vec] = k_new[(bh * T + j) * vpr + vec];
+    V[(bh * W + slot) * vpr + vec] = v_new[(bh * T + j) * vpr + vec];
+    if (h == 0 && vec == 0) pos[(int64_t)b * W + slot] = (int32_t)p;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) np[b] = (int32_t)(n0 + T);
 }
 
 // Tokens of the new, still incomplete block go to the staging rows (row
@@ -181,10 +270,19 @@ __global__ void append_int8_stage_kernel(const uint4* __restrict__ k_new,
 }  // namespace
 
 hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void* v_new, int T,
-                              hipStream_t s) {
+                              hipStream_t s, bool* advanced) {
   const int esz = c.kind == SWA_KV_FP32 ? 4 : 2;
   const int vpr = c.D * esz / 16;
   const int Tw = T < c.W ? T : c.W;
+  if (T <= kSmallT) {
+    hipLaunchKernelGGL(append_rows_small_kernel, dim3(c.B), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                       reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.pos, c.next_position, c.H,
+                       c.W, T, Tw, vpr);
+    *advanced = true;
+    return hipGetLastError();
+  }
+  *advanced = false;
   const int64_t total = (int64_t)c.B * c.H * Tw * vpr;
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
@@ -197,7 +295,17 @@ hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void*
 }
 
 hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void* v_new, int T,
-                              hipStream_t s) {
+                              hipStream_t s, bool* advanced) {
+  if (T <= kSmallT) {
+    hipLaunchKernelGGL(append_int8_small_kernel, dim3(c.B), dim3(1024), 0, s,
+                       reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new),
+                       reinterpret_cast<uint16_t*>(c.k_stage), reinterpret_cast<uint16_t*>(c.v_stage),
+                       reinterpret_cast<int8_t*>(c.k), reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale,
+                       c.witness, c.pos, c.next_position, c.H, c.W, T);
+    *advanced = true;
+    return hipGetLastError();
+  }
+  *advanced = false;
   // At most ceil(T/16) blocks complete, and only the newest W/16 are kept.
   int nblk = (T + 15) / 16;
   if (nblk > c.W / 16) nblk = c.W / 16;

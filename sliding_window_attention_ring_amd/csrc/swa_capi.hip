@@ -201,9 +201,10 @@ int kv_append(const swa_cache* c, const void* k_new, const void* v_new, int32_t 
   if (k_new == nullptr || v_new == nullptr) return SWA_ENULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return SWA_EALIGN;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = c->kind == SWA_KV_INT8 ? launch_append_int8(*c, k_new, v_new, T, s)
-                                        : launch_append_rows(*c, k_new, v_new, T, s);
-  if (e == hipSuccess) e = launch_advance(*c, T, s);
+  bool advanced = false;
+  hipError_t e = c->kind == SWA_KV_INT8 ? launch_append_int8(*c, k_new, v_new, T, s, &advanced)
+                                        : launch_append_rows(*c, k_new, v_new, T, s, &advanced);
+  if (e == hipSuccess && !advanced) e = launch_advance(*c, T, s);
   return e == hipSuccess ? SWA_OK : SWA_EHIP;
 }
 

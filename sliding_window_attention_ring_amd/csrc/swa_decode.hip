@@ -80,6 +80,14 @@ struct RowFmt<float> {
 
 constexpr float kNegBig = -1e30f;  // finite start value of the running max
 
+// Waves per work-group and row loads per lane per iteration.
+#ifndef SWA_ROW_NW
+#define SWA_ROW_NW 4
+#endif
+#ifndef SWA_ROW_U
+#define SWA_ROW_U 4
+#endif
+
 template <typename T, int D, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const int32_t* __restrict__ np
 template <typename T, int D>
 hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, const SplitPlan& plan,
                       hipStream_t s) {
-  constexpr int NW = 4, U = 4;
+  constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
   float* part = reinterpret_cast<float*>(ws);
   hipLaunchKernelGGL((decode_kernel<T, D, NW, U>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
                      reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v),
@@ -271,7 +279,7 @@ hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, c
 int decode_round_rows(const swa_cache& c) {
   const int esz = c.kind == SWA_KV_FP32 ? 4 : 2;
   const int lpr = c.D * esz / 16;
-  return 4 /*NW*/ * (64 / lpr) * 4 /*U*/;
+  return SWA_ROW_NW * (64 / lpr) * SWA_ROW_U;
 }
 
 hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws, const SplitPlan& plan,

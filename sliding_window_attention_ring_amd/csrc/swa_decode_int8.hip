@@ -29,6 +29,18 @@
 namespace swa {
 namespace {
 
+// Waves per work-group and 16-token blocks per wave iteration.
+#ifndef SWA_INT8_NW
+#define SWA_INT8_NW 4
+#endif
+#ifndef SWA_INT8_UB
+#define SWA_INT8_UB 2
+#endif
+// 1: key dots on packed fp16 (codes as 1024+u, query in fp16) with v_dot2_f32_f16.
+#ifndef SWA_INT8_KDOT_F16
+#define SWA_INT8_KDOT_F16 0
+#endif
+
 constexpr int D = 128;
 constexpr int PF = D + 4;          // m, l, cmax, pad, acc[D]
 constexpr float kNegBig = -1e30f;
@@ -40,6 +52,77 @@ struct Blk {
   uint4 k0, k1, v0, v1;
   uint2 w;
 };
+
+// Dot product of this lane's 16 query dims with 16 int8 key codes, in
+// base-2 logit units before the block scale.
+#if SWA_INT8_KDOT_F16
+// Codes c are shifted to u = c + 128 (xor 0x80) and packed two per register
+// as the fp16 values 1024 + u (bits 0x64uu, built with one byte permute);
+// the query is held in fp16 (exact for bf16 values of magnitude 2^-14..65504).
+// sum q(1024 + u) = sum q c + 1152 sum q, so the per-lane constant
+// 1152*sum(q) is removed before the cross-lane sum.
+struct KeyDot {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 q2[8];
+  float corr, scale;
+  __device__ __forceinline__ void init(const uint4* qv, float qscale) {
+    float f[16];
+    float t8[8];
+    unpack8(qv[0], t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = t8[e];
+    unpack8(qv[1], t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[8 + e] = t8[e];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      q2[i] = h2{(_Float16)f[2 * i], (_Float16)f[2 * i + 1]};
+      sum += (float)q2[i].x + (float)q2[i].y;
+    }
+    corr = 1152.0f * sum;
+    scale = qscale;
+  }
+  __device__ __forceinline__ float dot(const uint4 c) const {
+    const uint32_t w[4] = {c.x ^ 0x80808080u, c.y ^ 0x80808080u, c.z ^ 0x80808080u, c.w ^ 0x80808080u};
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, w[i], 0x04010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, w[i], 0x04030402u);
+      d = __builtin_amdgcn_fdot2(q2[2 * i], __builtin_bit_cast(h2, lo), d, false);
+      d = __builtin_amdgcn_fdot2(q2[2 * i + 1], __builtin_bit_cast(h2, hi), d, false);
+    }
+    return d - corr;
+  }
+  __device__ __forceinline__ float finish(float d) const { return d * scale; }
+};
+#else
+// Each code converts with one sign-extending byte convert; the query is
+// pre-scaled by log2(e)/sqrt(D).
+struct KeyDot {
+  float qf[16];
+  __device__ __forceinline__ void init(const uint4* qv, float qscale) {
+    float t8[8];
+    unpack8(qv[0], t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] = t8[e] * qscale;
+    unpack8(qv[1], t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[8 + e] = t8[e] * qscale;
+  }
+  __device__ __forceinline__ float dot(const uint4 c) const {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d = fmaf(qf[4 * i + j], s8(cw[i], j), d);
+    return d;
+  }
+  __device__ __forceinline__ float finish(float d) const { return d; }
+};
+#endif
 
 template <int NW, int UB>
 __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
@@ -73,17 +156,8 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 
   // Key-dot mapping: lane covers dims [16*(lane%8), +16) of row lane/8 (+8).
   const int g = lane >> 3, vq = lane & 7;
-  float qf[16];
-  {
-    const uint4* qv = reinterpret_cast<const uint4*>(q + bh * D) + 2 * vq;
-    float f[8];
-    unpack8(qv[0], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[e] = f[e] * qscale;
-    unpack8(qv[1], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[8 + e] = f[e] * qscale;
-  }
+  KeyDot kd;
+  kd.init(reinterpret_cast<const uint4*>(q + bh * D) + 2 * vq, qscale);
   // Witness mapping: lane covers bands [4*(lane%4), +4) of token lane/4.
   // nq[i] = ||q_band|| / sqrt(D) for those bands.
   const int wt = lane >> 2, wq = lane & 3;
@@ -139,14 +213,8 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
       sv[ub] = vsbh[sbk];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const uint4 c = half ? cur[ub].k1 : cur[ub].k0;
-        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) d = fmaf(qf[4 * i + j], s8(cw[i], j), d);
-        d = group_sum<8>(d) * sk;  // key scale folded into the finished dot
+        float d = kd.dot(half ? cur[ub].k1 : cur[ub].k0);
+        d = kd.finish(group_sum<8>(d)) * sk;  // key scale folded into the finished dot
         const int pos = kb * 16 + g + 8 * half;
         s[2 * ub + half] = (live && pos >= p0) ? d : -INFINITY;
       }
@@ -315,11 +383,11 @@ __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
 
 }  // namespace
 
-int decode_int8_round_blocks() { return 4 /*NW*/ * 2 /*UB*/; }
+int decode_int8_round_blocks() { return SWA_INT8_NW * SWA_INT8_UB; }
 
 hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax, float* c_all,
                               void* ws, const SplitPlan& plan, hipStream_t s) {
-  constexpr int NW = 4, UB = 2;
+  constexpr int NW = SWA_INT8_NW, UB = SWA_INT8_UB;
   if (c_all != nullptr) {
     const int64_t n = (int64_t)c.B * c.H * c.W;
     int64_t blocks = (n + 255) / 256;

@@ -23,10 +23,12 @@ SplitPlan plan_decode(const swa_cache& c);
 inline int partial_floats(int D) { return D + 4; }
 
 
+// *advanced is set when the launch also advanced next_position (the
+// single-launch path for short chunks); otherwise launch_advance must follow.
 hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void* v_new, int T,
-                              hipStream_t s);
+                              hipStream_t s, bool* advanced);
 hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void* v_new, int T,
-                              hipStream_t s);
+                              hipStream_t s, bool* advanced);
 hipError_t launch_advance(const swa_cache& c, int T, hipStream_t s);
 
 hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws,
