@@ -125,6 +125,23 @@ int decode_attn(const swa_cache *c, const void *q, float *out, void *ws, size_t 
 int decode_attn_int8_witness(const swa_cache *c, const void *q, float *out, float *cmax,
                              float *c_all, void *ws, size_t ws_bytes, void *stream);
 
+/* decode_attn_int8_witness plus a total-variation bound and a gate flag
+ * (WitCert, section 为什么在线监控 KV 误差如此困难: prior work bounds the TV of
+ * the attention weights by tanh of the largest logit error; section SGLang
+ * 生产级落地: the decode pass emits a per-step TV bound for the gate).
+ * Every visible logit moved by at most cmax, so
+ *  tv    [B][H] fp32: tanh(cmax/2), an upper bound on the total variation
+ *        between the attention weights over the exact keys and over the
+ *        quantized keys (tight in the worst case over logit perturbations
+ *        of that size; tanh(cmax) would also be sound, and looser)
+ *  gate  NULL, or [B][H] int32: 1 where tv > tau, else 0 (tau = 0.2 marks the
+ *        pages' danger threshold); gate needs tv.
+ * tv = NULL makes this identical to decode_attn_int8_witness.  Errors as
+ * there, plus SWA_ENULL for gate without tv and SWA_EINVAL for a NaN tau. */
+int decode_attn_int8_witness_tv(const swa_cache *c, const void *q, float *out, float *cmax, float *tv,
+                                int32_t *gate, float tau, float *c_all, void *ws, size_t ws_bytes,
+                                void *stream);
+
 /* Workspace bytes the decode entry points need for this cache shape (the
  * split partials: B*H*nsplit*(D+4) floats).  0 for an invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);

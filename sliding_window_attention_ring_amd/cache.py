@@ -173,6 +173,30 @@ def decode_attn_int8_witness(cache, q: torch.Tensor, out: Optional[torch.Tensor]
     return out, cmax, c_all
 
 
+def decode_attn_int8_witness_tv(cache, q: torch.Tensor, tau: float = 0.2, out: Optional[torch.Tensor] = None,
+                                cmax: Optional[torch.Tensor] = None, tv: Optional[torch.Tensor] = None,
+                                gate: Optional[torch.Tensor] = None, want_c_all: bool = False,
+                                ws: Optional[torch.Tensor] = None, stream=None):
+    """``decode_attn_int8_witness_tv``: returns (out, cmax, tv [B,H], gate [B,H] int32, c_all or None)."""
+    _need(q, (cache.B, cache.H, cache.D), torch.bfloat16, "q")
+    dev = q.device
+    BH = (cache.B, cache.H)
+    out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=dev) if out is None else out
+    cmax = torch.empty(BH, dtype=torch.float32, device=dev) if cmax is None else cmax
+    tv = torch.empty(BH, dtype=torch.float32, device=dev) if tv is None else tv
+    gate = torch.empty(BH, dtype=torch.int32, device=dev) if gate is None else gate
+    c_all = torch.empty((cache.B, cache.H, cache.W), dtype=torch.float32, device=dev) if want_c_all else None
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    for t, name, dt in ((cmax, "cmax", torch.float32), (tv, "tv", torch.float32), (gate, "gate", torch.int32)):
+        _need(t, BH, dt, name)
+    ws = cache.workspace() if ws is None else ws
+    check(lib().decode_attn_int8_witness_tv(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(cmax), _ptr(tv),
+                                            _ptr(gate), float(tau), _ptr(c_all), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream)),
+          "decode_attn_int8_witness_tv")
+    return out, cmax, tv, gate, c_all
+
+
 def validate(cache, stream=None) -> int:
     """``swa_validate``: number of slots violating the position invariant (syncs)."""
     viol = torch.zeros((1,), dtype=torch.int32, device=cache.k.device)

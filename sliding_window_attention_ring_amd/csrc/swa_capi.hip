@@ -219,18 +219,27 @@ int decode_attn(const swa_cache* c, const void* q, float* out, void* ws, size_t 
   return launch_decode(*c, q, out, ws, p, (hipStream_t)stream) == hipSuccess ? SWA_OK : SWA_EHIP;
 }
 
-int decode_attn_int8_witness(const swa_cache* c, const void* q, float* out, float* cmax, float* c_all,
-                             void* ws, size_t ws_bytes, void* stream) {
+int decode_attn_int8_witness_tv(const swa_cache* c, const void* q, float* out, float* cmax, float* tv,
+                                int32_t* gate, float tau, float* c_all, void* ws, size_t ws_bytes, void* stream) {
   int st = check_cache(c);
   if (st != SWA_OK) return st;
   if (c->kind != SWA_KV_INT8) return SWA_EUNSUPPORTED;
   if (q == nullptr || out == nullptr || cmax == nullptr || ws == nullptr) return SWA_ENULL;
+  if (gate != nullptr && tv == nullptr) return SWA_ENULL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return SWA_EALIGN;
-  if (((uintptr_t)cmax & 3u) || ((uintptr_t)c_all & 3u)) return SWA_EALIGN;
+  if (((uintptr_t)cmax & 3u) || ((uintptr_t)c_all & 3u) || ((uintptr_t)tv & 3u) || ((uintptr_t)gate & 3u))
+    return SWA_EALIGN;
+  if (!(tau == tau)) return SWA_EINVAL;  // NaN threshold
   if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
   const SplitPlan p = plan_decode(*c);
-  return launch_decode_int8(*c, q, out, cmax, c_all, ws, p, (hipStream_t)stream) == hipSuccess ? SWA_OK
-                                                                                                 : SWA_EHIP;
+  return launch_decode_int8(*c, q, out, cmax, c_all, tv, gate, tau, ws, p, (hipStream_t)stream) == hipSuccess
+             ? SWA_OK
+             : SWA_EHIP;
+}
+
+int decode_attn_int8_witness(const swa_cache* c, const void* q, float* out, float* cmax, float* c_all,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return decode_attn_int8_witness_tv(c, q, out, cmax, nullptr, nullptr, 0.f, c_all, ws, ws_bytes, stream);
 }
 
 int swa_validate(const swa_cache* c, int32_t* violations, void* stream) {

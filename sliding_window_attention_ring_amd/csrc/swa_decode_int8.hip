@@ -321,10 +321,15 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 // Merge of one (b, h): log-sum-exp over the split partials, then the exact
 // staging tokens (positions 16*nb .. n-1, row = position mod 16, c_t = 0),
 // then normalization.  256 threads; thread t < D owns output dim t.
+// Optional epilogue (tv != null): every visible logit moved by at most
+// E = cmax, so the attention weights moved by at most tanh(E/2) in total
+// variation (page "WitCert", section 为什么在线监控 KV 误差如此困难 gives the
+// looser tanh(E) form); gate = tv > tau.
 __global__ __launch_bounds__(256) void merge_int8_kernel(
     const int32_t* __restrict__ np, const float* __restrict__ part, const uint16_t* __restrict__ kst,
     const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q, float* __restrict__ out,
-    float* __restrict__ cmax_out, int H, int W, int cb, int nsplit_max) {
+    float* __restrict__ cmax_out, float* __restrict__ tv, int32_t* __restrict__ gate, float tau, int H, int W,
+    int cb, int nsplit_max) {
   __shared__ float sm_s[16];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int64_t bh = (int64_t)b * H + h;
@@ -373,7 +378,16 @@ __global__ __launch_bounds__(256) void merge_int8_kernel(
     }
   }
   if (t < D) out[bh * D + t] = L > 0.f ? A / L : 0.f;
-  if (t == 0) cmax_out[bh] = CM * kBoundPad;
+  if (t == 0) {
+    const float cm = CM * kBoundPad;
+    cmax_out[bh] = cm;
+    if (tv != nullptr) {
+      // tanhf is within a few ulp; the 2^-20 pad keeps the value an upper bound.
+      const float b = fminf(tanhf(0.5f * cm) * (1.0f + 0x1p-20f), 1.0f);
+      tv[bh] = b;
+      if (gate != nullptr) gate[bh] = b > tau ? 1 : 0;
+    }
+  }
 }
 
 __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
@@ -386,7 +400,8 @@ __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
 int decode_int8_round_blocks() { return SWA_INT8_NW * SWA_INT8_UB; }
 
 hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax, float* c_all,
-                              void* ws, const SplitPlan& plan, hipStream_t s) {
+                              float* tv, int32_t* gate, float tau, void* ws, const SplitPlan& plan,
+                              hipStream_t s) {
   constexpr int NW = SWA_INT8_NW, UB = SWA_INT8_UB;
   if (c_all != nullptr) {
     const int64_t n = (int64_t)c.B * c.H * c.W;
@@ -405,8 +420,8 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_int8_kernel, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part,
                      reinterpret_cast<const uint16_t*>(c.k_stage), reinterpret_cast<const uint16_t*>(c.v_stage),
-                     reinterpret_cast<const uint16_t*>(q), out, cmax, c.H, c.W, plan.unit_per_split,
-                     plan.nsplit_max);
+                     reinterpret_cast<const uint16_t*>(q), out, cmax, tv, gate, tau, c.H, c.W,
+                     plan.unit_per_split, plan.nsplit_max);
   return hipGetLastError();
 }
 

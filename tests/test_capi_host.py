@@ -76,6 +76,11 @@ def test_argument_checks_return_codes():
     assert L.decode_attn(p(desc(kind=2)), A16, A16, ws, need, None) == -4    # INT8 needs the witness entry
     assert L.decode_attn_int8_witness(p(d), A16, A16, A16, None, ws, need, None) == -4
     assert L.decode_attn_int8_witness(p(desc(kind=2)), A16, A16, None, None, ws, 1 << 30, None) == -2
+    i8 = desc(kind=2)
+    assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, None, A16, 0.2, None, ws, 1 << 30, None) == -2
+    assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, A16, A16, float("nan"), None, ws, 1 << 30,
+                                         None) == -1
+    assert L.decode_attn_int8_witness_tv(p(d), A16, A16, A16, A16, A16, 0.2, None, ws, 1 << 30, None) == -4
     assert L.swa_validate(p(d), None, None) == -2
     assert L.swa_workspace_init(None, 64, None) == -2
     assert L.swa_workspace_init(ODD, 64, None) == -3

@@ -116,3 +116,36 @@ def test_int8_zero_blocks_and_exact_multiples():
         check_int8_store(cache, 0, h, k64[0, h], v64[0, h], n)
         check_int8_decode(out[0, h].cpu().numpy(), float(cmax[0, h]), c_all[0, h].cpu().numpy(), 0, h,
                           q64[0, h], k64[0, h], v64[0, h], n, W, what="exact")
+
+
+def test_int8_tv_bound_and_gate():
+    """TV epilogue: tv >= the true total variation between exact-key and
+    quantized-key attention weights, tv = tanh(cmax/2) (padded), gate = tv >
+    tau; a head whose block holds one huge key (coarse scale, forced from the
+    host) must raise the gate while ordinary heads stay below tau.  Outputs
+    and cmax equal those of decode_attn_int8_witness bit for bit."""
+    import sliding_window_attention_ring_amd as swa
+    from oracle import tv as otv
+    B, H, D, W, n = 2, 3, 128, 64, 100
+    g = torch.Generator().manual_seed(11)
+    k = torch.randn((B, H, n, D), generator=g)
+    k[1, 2, 70, 5] = 400.0  # outlier: block 4 of (b=1, h=2) gets a coarse scale
+    k = k.to(torch.bfloat16)
+    v = torch.randn((B, H, n, D), generator=g).to(torch.bfloat16)
+    q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+    cache = swa.KVCache("int8", B, H, D, W)
+    swa.kv_append(cache, k.cuda(), v.cuda())
+    out, cmax, tvb, gate, _ = swa.decode_attn_int8_witness_tv(cache, q.cuda(), tau=0.2)
+    out2, cmax2, _ = swa.decode_attn_int8_witness(cache, q.cuda())
+    assert torch.equal(out, out2) and torch.equal(cmax, cmax2)
+    tvb, gate, cmax = tvb.cpu().numpy(), gate.cpu().numpy(), cmax.cpu().numpy()
+    k64, v64, q64 = f64(k), f64(v), f64(q)
+    for b in range(B):
+        for h in range(H):
+            r = otv.int8_attention_tv(q64[b, h], k64[b, h], v64[b, h], n, W)
+            t = float(tvb[b, h])
+            assert t >= r["tv"], (b, h, t, r["tv"])
+            assert t >= np.tanh(0.5 * float(cmax[b, h])) * (1 - 2.0 ** -22)
+            assert t <= r["bound"] * (1 + 2.0 ** -8) + 1e-7, (t, r["bound"])
+            assert gate[b, h] == (1 if t > 0.2 else 0)
+            assert gate[b, h] == (1 if (b, h) == (1, 2) else 0)

@@ -1,0 +1,75 @@
+"""Pins for the TV bound (oracle/tv.py).
+
+What pins it:
+* TV is a distance: 0 on equal inputs, symmetric, 1 on disjoint supports;
+* brute force over every +-E sign pattern on small softmaxes never exceeds
+  tanh(E/2), and the closed-form worst case (mass 1/(1+e^E) moved up, the
+  rest down) attains it; random perturbations inside the box stay below it;
+* tanh(E/2) <= tanh(E), the pages' prior form;
+* on INT8 caches, the true TV between exact-key and quantized-key weights is
+  below tanh(cmax/2), also for a block made coarse by an outlier key.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import tv
+from oracle.attention import softmax_weights
+
+
+def test_tv_distance_axioms():
+    p = np.array([0.2, 0.3, 0.5])
+    assert tv.tv_distance(p, p) == 0.0
+    q = np.array([0.5, 0.3, 0.2])
+    assert tv.tv_distance(p, q) == tv.tv_distance(q, p) == pytest.approx(0.3)
+    assert tv.tv_distance([1, 0], [0, 1]) == 1.0
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 6])
+def test_sign_patterns_never_exceed_tanh_half(n):
+    rng = np.random.default_rng(n)
+    for _ in range(40):
+        p = rng.dirichlet(np.ones(n) * rng.uniform(0.2, 3))
+        p = np.clip(p, 1e-12, None)
+        p /= p.sum()
+        e = rng.uniform(0.001, 3.0)
+        assert tv.max_tv_over_signs(p, e) <= tv.tv_bound(e) + 1e-12
+
+
+def test_worst_case_attains_the_bound():
+    for e in [0.01, 0.3, 1.0, 2.5]:
+        a = 1.0 / (1.0 + np.exp(e))
+        p = np.array([a, 1 - a])
+        pert = softmax_weights(np.log(p) + np.array([e, -e]))
+        assert tv.tv_distance(p, pert) == pytest.approx(np.tanh(e / 2), rel=1e-12)
+        assert tv.max_tv_over_signs(p, e) == pytest.approx(np.tanh(e / 2), rel=1e-12)
+
+
+def test_random_perturbations_inside_the_box():
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        n = int(rng.integers(2, 40))
+        s = rng.standard_normal(n) * rng.uniform(0.1, 5)
+        e = rng.uniform(0.0, 2.0)
+        eps = rng.uniform(-e, e, n)
+        t = tv.tv_distance(softmax_weights(s), softmax_weights(s + eps))
+        assert t <= tv.tv_bound(e) + 1e-12
+        assert tv.tv_bound(e) <= tv.prior_tv_bound(e)
+
+
+def test_int8_cache_tv_below_bound():
+    rng = np.random.default_rng(2)
+    d, w = 128, 64
+    for n in [5, 16, 40, 64, 100]:
+        k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+        k = k.astype(np.float32).astype(np.float64)
+        q = rng.standard_normal(d) * 3
+        r = tv.int8_attention_tv(q, k, v, n, w)
+        assert r["tv"] <= r["bound"]
+        assert r["cmax"] >= r["emax"]
+    # an outlier key makes its block's scale coarse: larger error, still bounded
+    k = rng.standard_normal((48, d))
+    k[20, 7] = 400.0
+    q = rng.standard_normal(d) * 3
+    r = tv.int8_attention_tv(q, k, rng.standard_normal((48, d)), 48, 64)
+    assert r["tv"] <= r["bound"] and r["bound"] > 0.2
