@@ -73,3 +73,31 @@ def test_int8_cache_tv_below_bound():
     q = rng.standard_normal(d) * 3
     r = tv.int8_attention_tv(q, k, rng.standard_normal((48, d)), 48, 64)
     assert r["tv"] <= r["bound"] and r["bound"] > 0.2
+
+
+def test_bound_is_attained_by_tv_bound():
+    for e in [0.05, 0.7, 2.0]:
+        a = 1.0 / (1.0 + np.exp(e))
+        assert tv.max_tv_over_signs(np.array([a, 1 - a]), e) == pytest.approx(tv.tv_bound(e), rel=1e-12)
+
+
+def test_int8_tv_via_one_hot_values():
+    """With value rows a*e_j (one-hot, a = 127/128 so the block scale 2^-7 and
+    the codes are exact), attention returns a times its weight vector, so the
+    INT8 decode output and the masked float64 attention give the
+    quantized-key and exact-key weights by another route."""
+    from oracle import attention, int8 as oint8
+    rng = np.random.default_rng(4)
+    d, w = 128, 64
+    for n in [40, 64, 100]:
+        k = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+        q = rng.standard_normal(d) * 2
+        v = np.zeros((n, d))
+        ln = min(w, n)
+        for i, p in enumerate(range(n - ln, n)):
+            v[p, i] = 127.0 / 128.0
+        pq = oint8.int8_decode(q, k, v, n, w)["out"][:ln] / (127.0 / 128.0)
+        pe = attention.masked_attention(q, np.arange(n), k, v, n - 1, w)[:ln] / (127.0 / 128.0)
+        r = tv.int8_attention_tv(q, k, v, n, w)
+        assert r["tv"] == pytest.approx(tv.tv_distance(pe, pq), abs=1e-12)
+        assert r["tv"] > 0
