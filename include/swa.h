@@ -150,6 +150,20 @@ size_t swa_workspace_bytes(const swa_cache *c);
  * they read).  Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
 int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
+/* Prefix reuse (huhohoo.com, sections 哪些東西必須一起裁剪 and
+ * 為什麼滑窗部分命中必須回退): truncate sequence b to its first cut[b] tokens,
+ * so the next appended token gets position cut[b] -- when that is exact.
+ * It is exact iff every row of the shorter history's window is still
+ * stored: 0 <= cut <= n and (n <= W, or cut == n, or cut == 0); an INT8 cache
+ * also needs cut % 16 == 0 or cut >= 16*(n/16) (committed blocks keep only
+ * codes).  Exact: slots holding positions >= cut become empty (pos = -1)
+ * and next_position[b] = cut.  Otherwise sequence b is left unchanged and the
+ * caller must recompute it.
+ *  cut  [B] device int32
+ *  ok   NULL, or [B] device int32: 1 truncated (or nothing to do), 0 fall back
+ * Errors: SWA_ENULL, SWA_EALIGN, descriptor errors, SWA_EHIP. */
+int kv_truncate(const swa_cache *c, const int32_t *cut, int32_t *ok, void *stream);
+
 /* Debug check of the position invariant (framerc.cn §3.2 PositionInvariant,
  * §6.3 the invariant as a runtime assertion): adds to *violations (device
  * int32, caller zeroes it) the number of slots whose pos differs from the

@@ -38,4 +38,4 @@ against facts the pages and mathematics fix (worked examples, closed forms,
 brute force, an independent library routine).  None is "parity unpinned".
 """
 
-from . import bits, listmodel, attention, int8, rope, decoder, tv  # noqa: F401
+from . import bits, listmodel, attention, int8, rope, decoder, tv, reuse  # noqa: F401

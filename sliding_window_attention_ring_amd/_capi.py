@@ -15,7 +15,7 @@ KIND = {"bf16": 0, "fp32": 1, "int8": 2}
 
 # Every symbol include/swa.h declares.
 EXPORTS = ("swa_cache_reset", "kv_append", "decode_attn", "decode_attn_int8_witness",
-           "decode_attn_int8_witness_tv",
+           "decode_attn_int8_witness_tv", "kv_truncate",
            "swa_workspace_bytes", "swa_workspace_init", "swa_validate", "swa_status_string")
 
 
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
             "decode_attn_int8_witness": (ctypes.c_int, [P, VP, VP, VP, VP, VP, SZ, VP]),
             "decode_attn_int8_witness_tv": (ctypes.c_int, [P, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP, SZ,
                                                            VP]),
+            "kv_truncate": (ctypes.c_int, [P, VP, VP, VP]),
             "swa_workspace_bytes": (SZ, [P]),
             "swa_workspace_init": (ctypes.c_int, [VP, SZ, VP]),
             "swa_validate": (ctypes.c_int, [P, VP, VP]),

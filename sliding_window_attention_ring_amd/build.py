@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libswa.so")
-SOURCES = ["swa_capi.hip", "swa_append.hip", "swa_decode.hip", "swa_decode_int8.hip"]
+SOURCES = ["swa_capi.hip", "swa_append.hip", "swa_decode.hip", "swa_decode_int8.hip", "swa_reuse.hip"]
 ARCH = "gfx950"
 
 

@@ -197,6 +197,14 @@ def decode_attn_int8_witness_tv(cache, q: torch.Tensor, tau: float = 0.2, out: O
     return out, cmax, tv, gate, c_all
 
 
+def kv_truncate(cache, cut: torch.Tensor, stream=None) -> torch.Tensor:
+    """``kv_truncate``: returns ok [B] int32 (1 truncated, 0 must recompute)."""
+    _need(cut, (cache.B,), torch.int32, "cut")
+    ok = torch.empty((cache.B,), dtype=torch.int32, device=cut.device)
+    check(lib().kv_truncate(ctypes.byref(cache.desc), _ptr(cut), _ptr(ok), _stream(stream)), "kv_truncate")
+    return ok
+
+
 def validate(cache, stream=None) -> int:
     """``swa_validate``: number of slots violating the position invariant (syncs)."""
     viol = torch.zeros((1,), dtype=torch.int32, device=cache.k.device)

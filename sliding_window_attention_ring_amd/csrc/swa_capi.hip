@@ -242,6 +242,14 @@ int decode_attn_int8_witness(const swa_cache* c, const void* q, float* out, floa
   return decode_attn_int8_witness_tv(c, q, out, cmax, nullptr, nullptr, 0.f, c_all, ws, ws_bytes, stream);
 }
 
+int kv_truncate(const swa_cache* c, const int32_t* cut, int32_t* ok, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (cut == nullptr) return SWA_ENULL;
+  if (((uintptr_t)cut & 3u) || ((uintptr_t)ok & 3u)) return SWA_EALIGN;
+  return launch_truncate(*c, cut, ok, (hipStream_t)stream) == hipSuccess ? SWA_OK : SWA_EHIP;
+}
+
 int swa_validate(const swa_cache* c, int32_t* violations, void* stream) {
   int st = check_cache(c);
   if (st != SWA_OK) return st;

@@ -38,6 +38,7 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
                               const SplitPlan& plan, hipStream_t s);
 
 hipError_t launch_reset(const swa_cache& c, hipStream_t s);
+hipError_t launch_truncate(const swa_cache& c, const int32_t* cut, int32_t* ok, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_validate(const swa_cache& c, int32_t* violations, hipStream_t s);
 
