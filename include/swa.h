@@ -37,7 +37,8 @@ extern "C" {
 
 enum {
   SWA_OK = 0,
-  SWA_EINVAL = -1,       /* B, H, W < 1, T < 0, W*D*elem >= 2^32, or INT8 W not a multiple of 16 */
+  SWA_EINVAL = -1,       /* B, H, W < 1, T < 0, W*D*elem >= 2^32, unknown layout, or W not a
+                            multiple of 16 for INT8 or PAGED */
   SWA_ENULL = -2,        /* a required pointer is NULL */
   SWA_EALIGN = -3,       /* a K/V/q/out/staging/workspace pointer is not 16-byte aligned */
   SWA_EUNSUPPORTED = -4, /* head_dim or kind not supported by this entry point */
@@ -51,33 +52,51 @@ enum {
   SWA_KV_INT8 = 2  /* K/V INT8 codes per 16-token block + fp16 band witness; q, new rows bf16 */
 };
 
+/* Physical layout of the rows (the logical cache is the same either way:
+ * the window lastWindow(W, history), framerc.cn §3.4 and §6.1).
+ * RING:  one contiguous ring of W slots per (b, h).
+ * PAGED: pools of 16-token pages shared by all sequences (the paging of
+ *        airsota.com §八, pages of 16 tokens); block_table[b][j] names the
+ *        page holding ring slots 16j..16j+15 of sequence b.  Needs W % 16 == 0. */
+enum { SWA_LAYOUT_RING = 0, SWA_LAYOUT_PAGED = 1 };
+
 /* Cache descriptor.  Supported head_dim D: BF16 {64, 128, 256}; FP32
  * {16, 32, 64, 128}; INT8 {128} (16 bands of 8 dims).
  *
- *  k, v           [B][H][W][D]   bf16 | fp32 | int8 codes
+ *  RING layout                   PAGED layout (P = num_pages)
+ *  k, v       [B][H][W][D]       [P][H][16][D]    bf16 | fp32 | int8 codes
+ *  INT8 only:
+ *  k_scale,   [B][H][W/16] fp32  [P][H] fp32      absmax/127 of the block
+ *  v_scale
+ *  witness    [B][H][W][D/8]     [P][H][16][D/8]  fp16 bits: band norms of the
+ *                                                 key residual, rounded up
+ *  Both layouts:
  *  pos            [B][W]  int32  absolute position held by each slot, -1 if
  *                                none (INT8: position of the committed code row)
  *  next_position  [B]     int32  position the next appended token receives
- *  INT8 only:
- *  k_scale,v_scale [B][H][W/16] fp32  absmax/127 of the block in those slots
- *  witness        [B][H][W][D/8] fp16 bits: band norms of the key residual,
- *                                rounded toward +infinity
- *  k_stage,v_stage [B][H][16][D] bf16 rows of the incomplete newest block,
- *                                row index = position mod 16
+ *  k_stage,v_stage [B][H][16][D] bf16 (INT8) rows of the incomplete newest
+ *                                block, row index = position mod 16
+ *  block_table    [B][W/16] int32 (PAGED) page of each 16-slot ring block;
+ *                                entries for blocks the sequence uses must be
+ *                                in [0, P), and no two sequences may share a
+ *                                page; unused entries are ignored
  */
 typedef struct swa_cache {
   int32_t kind, B, H, D, W;
-  int32_t reserved; /* must be 0 */
+  int32_t layout; /* SWA_LAYOUT_RING or SWA_LAYOUT_PAGED */
   void *k, *v;
   int32_t *pos;
   int32_t *next_position;
   float *k_scale, *v_scale;
   uint16_t *witness;
   void *k_stage, *v_stage;
+  int32_t *block_table; /* PAGED only */
+  int64_t num_pages;    /* PAGED only */
 } swa_cache;
 
-/* Empty the cache: next_position[b] = 0 and pos[b][*] = -1 for every b (INT8
- * also clears the block scales).  Row contents are left as they are; no
+/* Empty the cache: next_position[b] = 0 and pos[b][*] = -1 for every b (a
+ * RING INT8 cache also clears its block scales; PAGED pools, which other
+ * caches may share, are not touched).  Row contents are left as they are; no
  * slot is visible until written.  Errors: SWA_EINVAL, SWA_ENULL, SWA_EHIP. */
 int swa_cache_reset(const swa_cache *c, void *stream);
 
@@ -167,7 +186,8 @@ int kv_truncate(const swa_cache *c, const int32_t *cut, int32_t *ok, void *strea
 /* Debug check of the position invariant (framerc.cn §3.2 PositionInvariant,
  * §6.3 the invariant as a runtime assertion): adds to *violations (device
  * int32, caller zeroes it) the number of slots whose pos differs from the
- * newest position p < n (INT8: p < 16*(n/16)) with p mod W == slot, or -1. */
+ * newest position p < n (INT8: p < 16*(n/16)) with p mod W == slot, or -1;
+ * PAGED: also each live slot whose block_table entry is outside [0, P). */
 int swa_validate(const swa_cache *c, int32_t *violations, void *stream);
 
 /* Static text for a status code. */

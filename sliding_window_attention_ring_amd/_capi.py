@@ -12,6 +12,7 @@ SWA_OK = 0
 STATUS = {0: "SWA_OK", -1: "SWA_EINVAL", -2: "SWA_ENULL", -3: "SWA_EALIGN", -4: "SWA_EUNSUPPORTED",
           -5: "SWA_EWORKSPACE", -6: "SWA_EHIP"}
 KIND = {"bf16": 0, "fp32": 1, "int8": 2}
+LAYOUT = {"ring": 0, "paged": 1}
 
 # Every symbol include/swa.h declares.
 EXPORTS = ("swa_cache_reset", "kv_append", "decode_attn", "decode_attn_int8_witness",
@@ -24,12 +25,13 @@ class SwaCacheDesc(ctypes.Structure):
 
     _fields_ = [
         ("kind", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
-        ("D", ctypes.c_int32), ("W", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("W", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("pos", ctypes.c_void_p), ("next_position", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("witness", ctypes.c_void_p),
         ("k_stage", ctypes.c_void_p), ("v_stage", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("num_pages", ctypes.c_int64),
     ]
 
 

@@ -14,7 +14,7 @@ from typing import Optional
 import torch
 
 from . import _capi
-from ._capi import KIND, SwaCacheDesc, check, lib
+from ._capi import KIND, LAYOUT, SwaCacheDesc, check, lib
 
 _INPUT_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.bfloat16}
 _STORE_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.int8}
@@ -41,43 +41,77 @@ def _need(t: torch.Tensor, shape, dtype, name: str) -> None:
 
 
 class KVCache:
-    """Device tensors of one sliding-window ring cache and its descriptor.
+    """Device tensors of one sliding-window cache and its descriptor.
 
     kind: "bf16" | "fp32" | "int8"; B sequences, H heads, head_dim D, window W.
-    Tensors (see include/swa.h for the layouts): ``k``, ``v``, ``pos``,
-    ``next_position`` and, for INT8, ``k_scale``, ``v_scale``, ``witness``
-    (fp16), ``k_stage``, ``v_stage``.
+    layout "ring": ``k``, ``v`` are [B, H, W, D] (INT8: ``k_scale``/``v_scale``
+    [B, H, W/16], ``witness`` [B, H, W, D/8] fp16).  layout "paged": they are
+    pools of ``num_pages`` 16-token pages ([P, H, 16, D], [P, H], [P, H, 16,
+    D/8]) and ``block_table`` [B, W/16] int32 names the page of each ring
+    block; by default every sequence gets W/16 distinct pages in a seeded
+    shuffled order.  Per-sequence tensors: ``pos`` [B, W], ``next_position``
+    [B] and, for INT8, ``k_stage``/``v_stage`` [B, H, 16, D].
     """
 
-    def __init__(self, kind: str, B: int, H: int, D: int, W: int, device="cuda"):
+    def __init__(self, kind: str, B: int, H: int, D: int, W: int, device="cuda", layout: str = "ring",
+                 num_pages: Optional[int] = None, block_table: Optional[torch.Tensor] = None):
         if kind not in KIND:
             raise ValueError(f"kind must be one of {sorted(KIND)}")
-        self.kind, self.B, self.H, self.D, self.W = kind, B, H, D, W
+        if layout not in LAYOUT:
+            raise ValueError(f"layout must be one of {sorted(LAYOUT)}")
+        self.kind, self.B, self.H, self.D, self.W, self.layout = kind, B, H, D, W, layout
         dev = torch.device(device)
-        self.k = torch.empty((B, H, W, D), dtype=_STORE_DTYPE[kind], device=dev)
+        paged = layout == "paged"
+        if paged:
+            if W % 16:
+                raise ValueError("a paged cache needs W % 16 == 0")
+            self.num_pages = B * (W // 16) if num_pages is None else int(num_pages)
+            rows = (self.num_pages, H, 16)
+        else:
+            self.num_pages = 0
+            rows = (B, H, W)
+        self.k = torch.empty(rows + (D,), dtype=_STORE_DTYPE[kind], device=dev)
         self.v = torch.empty_like(self.k)
         self.pos = torch.empty((B, W), dtype=torch.int32, device=dev)
         self.next_position = torch.empty((B,), dtype=torch.int32, device=dev)
         self.k_scale = self.v_scale = self.witness = self.k_stage = self.v_stage = None
         if kind == "int8":
-            self.k_scale = torch.empty((B, H, W // 16), dtype=torch.float32, device=dev)
+            scales = (self.num_pages, H) if paged else (B, H, W // 16)
+            self.k_scale = torch.empty(scales, dtype=torch.float32, device=dev)
             self.v_scale = torch.empty_like(self.k_scale)
-            self.witness = torch.empty((B, H, W, D // 8), dtype=torch.float16, device=dev)
+            self.witness = torch.empty(rows + (D // 8,), dtype=torch.float16, device=dev)
             self.k_stage = torch.empty((B, H, 16, D), dtype=torch.bfloat16, device=dev)
             self.v_stage = torch.empty_like(self.k_stage)
+        self.block_table = None
+        if paged:
+            if block_table is None:
+                if self.num_pages < B * (W // 16):
+                    raise ValueError("pass a block_table when the pool has fewer than B*W/16 pages")
+                g = torch.Generator().manual_seed(B * 1000003 + W)
+                block_table = torch.randperm(self.num_pages, generator=g)[: B * (W // 16)].reshape(B, W // 16)
+            self.block_table = block_table.to(device=dev, dtype=torch.int32).contiguous()
         self.desc = self._make_desc()
         self._ws = None
         cache_reset(self)
 
     def _make_desc(self, b: Optional[int] = None) -> SwaCacheDesc:
-        def sel(t):
+        paged = self.layout == "paged"
+
+        def per_seq(t):  # tensors indexed by sequence
             if t is None:
                 return None
             return t.data_ptr() if b is None else t[b].data_ptr()
-        return SwaCacheDesc(KIND[self.kind], self.B if b is None else 1, self.H, self.D, self.W, 0,
-                            sel(self.k), sel(self.v), sel(self.pos), sel(self.next_position),
-                            sel(self.k_scale), sel(self.v_scale), sel(self.witness),
-                            sel(self.k_stage), sel(self.v_stage))
+
+        def pool(t):  # row storage: per sequence in a ring, shared in a paged pool
+            if t is None:
+                return None
+            return t.data_ptr() if (paged or b is None) else t[b].data_ptr()
+
+        return SwaCacheDesc(KIND[self.kind], self.B if b is None else 1, self.H, self.D, self.W,
+                            LAYOUT[self.layout], pool(self.k), pool(self.v), per_seq(self.pos),
+                            per_seq(self.next_position), pool(self.k_scale), pool(self.v_scale),
+                            pool(self.witness), per_seq(self.k_stage), per_seq(self.v_stage),
+                            per_seq(self.block_table), self.num_pages)
 
     def seq_view(self, b: int) -> "SeqView":
         """Descriptor of sequence ``b`` alone (B = 1), for ragged appends."""

@@ -20,7 +20,7 @@ namespace {
 // slot written by exactly one thread.
 __global__ void append_rows_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
                                    uint4* __restrict__ K, uint4* __restrict__ V,
-                                   int32_t* __restrict__ pos, const int32_t* __restrict__ np,
+                                   int32_t* __restrict__ pos, const int32_t* __restrict__ np, RowMap map,
                                    int B, int H, int W, int T, int Tw, int vpr) {
   const int64_t total = (int64_t)B * H * Tw * vpr;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -38,7 +38,7 @@ __global__ void append_rows_kernel(const uint4* __restrict__ k_new, const uint4*
     const int64_t slot = p % W;
     const int64_t bh = (int64_t)b * H + h;
     const int64_t src = (bh * T + j) * vpr + vec;
-    const int64_t dst = (bh * W + slot) * vpr + vec;
+    const int64_t dst = map.row(b, h, slot) * vpr + vec;
     K[dst] = k_new[src];
     V[dst] = v_new[src];
     if (h == 0 && vec == 0) pos[(int64_t)b * W + slot] = (int32_t)p;
@@ -75,9 +75,11 @@ constexpr int kSmallT = 16;
 // the witness and, if pos_b is not null, the slot positions.
 __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint16_t* __restrict__ src_new,
                                                   const uint16_t* __restrict__ src_stage, int64_t n0, int T,
-                                                  int64_t kb, int64_t bh, int W, int8_t* __restrict__ codes,
-                                                  float* __restrict__ scale, uint16_t* __restrict__ witness,
-                                                  int32_t* __restrict__ pos_b) {
+                                                  int64_t kb, int b, int h, const RowMap& map,
+                                                  int8_t* __restrict__ codes, float* __restrict__ scale,
+                                                  uint16_t* __restrict__ witness, int32_t* __restrict__ pos_b) {
+  const int W = map.W;
+  const int64_t bh = (int64_t)b * map.H + h;
   const int r = lane >> 2;        // token within the block
   const int part = lane & 3;      // 32-dim quarter of the row
   const int64_t p = kb * 16 + r;
@@ -108,7 +110,8 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
     cq[e] = (int8_t)(int)c;
   }
   const int64_t slot = (kb * 16) % W + r;
-  int8_t* dst = codes + (bh * W + slot) * kD8 + part * 32;
+  const int64_t row_idx = map.row(b, h, slot);
+  int8_t* dst = codes + row_idx * kD8 + part * 32;
   uint4 packed[2];
   uint32_t* pw = reinterpret_cast<uint32_t*>(packed);
 #pragma unroll
@@ -118,7 +121,7 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
   }
   reinterpret_cast<uint4*>(dst)[0] = packed[0];
   reinterpret_cast<uint4*>(dst)[1] = packed[1];
-  if (lane == 0) scale[bh * (W / 16) + (kb * 16) % W / 16] = s;
+  if (lane == 0) scale[map.block(b, h, slot)] = s;
   if (key) {
     uint16_t wb[4];
 #pragma unroll
@@ -135,7 +138,7 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
     uint2 o;
     o.x = (uint32_t)wb[0] | ((uint32_t)wb[1] << 16);
     o.y = (uint32_t)wb[2] | ((uint32_t)wb[3] << 16);
-    reinterpret_cast<uint2*>(witness + (bh * W + slot) * (kD8 / 8))[part] = o;
+    reinterpret_cast<uint2*>(witness + row_idx * (kD8 / 8))[part] = o;
     if (pos_b != nullptr && part == 0) pos_b[slot] = (int32_t)p;
   }
 }
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(128) void append_int8_blocks_kernel(
     const uint16_t* __restrict__ k_stage, const uint16_t* __restrict__ v_stage,
     int8_t* __restrict__ Kc, int8_t* __restrict__ Vc, float* __restrict__ k_scale,
     float* __restrict__ v_scale, uint16_t* __restrict__ witness, int32_t* __restrict__ pos,
-    const int32_t* __restrict__ np, int H, int W, int T) {
+    const int32_t* __restrict__ np, RowMap map, int H, int W, int T) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int64_t n0 = np[b];
   if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
@@ -158,8 +161,7 @@ __global__ __launch_bounds__(128) void append_int8_blocks_kernel(
   const int64_t kb = kb_lo + blockIdx.x;
   if (kb >= kb_hi) return;
   const bool key = (threadIdx.x >> 6) == 0;
-  const int64_t bh = (int64_t)b * H + h;
-  commit_block_wave(threadIdx.x & 63, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, bh, W,
+  commit_block_wave(threadIdx.x & 63, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, b, h, map,
                     key ? Kc : Vc, key ? k_scale : v_scale, witness,
                     h == 0 ? pos + (int64_t)b * W : nullptr);
 }
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(1024) void append_int8_small_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_stage,
     uint16_t* __restrict__ v_stage, int8_t* __restrict__ Kc, int8_t* __restrict__ Vc,
     float* __restrict__ k_scale, float* __restrict__ v_scale, uint16_t* __restrict__ witness,
-    int32_t* __restrict__ pos, int32_t* __restrict__ np, int H, int W, int T) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ np, RowMap map, int H, int W, int T) {
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t n0 = np[b];
@@ -187,8 +189,7 @@ __global__ __launch_bounds__(1024) void append_int8_small_kernel(
     for (int task = wave; task < 2 * H; task += 16) {
       const int h = task >> 1;
       const bool key = (task & 1) == 0;
-      const int64_t bh = (int64_t)b * H + h;
-      commit_block_wave(lane, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, bh, W,
+      commit_block_wave(lane, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, b, h, map,
                         key ? Kc : Vc, key ? k_scale : v_scale, witness,
                         h == 0 ? pos + (int64_t)b * W : nullptr);
     }
@@ -220,8 +221,8 @@ __global__ __launch_bounds__(1024) void append_int8_small_kernel(
 // sequence writes the rows and positions, then advances next_position.
 __global__ __launch_bounds__(256) void append_rows_small_kernel(
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint4* __restrict__ K,
-    uint4* __restrict__ V, int32_t* __restrict__ pos, int32_t* __restrict__ np, int H, int W, int T, int Tw,
-    int vpr) {
+    uint4* __restrict__ V, int32_t* __restrict__ pos, int32_t* __restrict__ np, RowMap map, int H, int W, int T,
+    int Tw, int vpr) {
   const int b = blockIdx.x;
   const int64_t n0 = np[b];
   if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
@@ -234,8 +235,9 @@ __global__ __launch_bounds__(256) void append_rows_small_kernel(
     const int64_t p = n0 + j;
     const int64_t slot = p % W;
     const int64_t bh = (int64_t)b * H + h;
-    K[(bh * W + slot) * vpr + vec] = k_new[(bh * T + j) * vpr + vec];
-    V[(bh * W + slot) * vpr + vec] = v_new[(bh * T + j) * vpr + vec];
+    const int64_t dst = map.row(b, h, slot) * vpr + vec;
+    K[dst] = k_new[(bh * T + j) * vpr + vec];
+    V[dst] = v_new[(bh * T + j) * vpr + vec];
     if (h == 0 && vec == 0) pos[(int64_t)b * W + slot] = (int32_t)p;
   }
   __syncthreads();
@@ -277,8 +279,8 @@ hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void*
   if (T <= kSmallT) {
     hipLaunchKernelGGL(append_rows_small_kernel, dim3(c.B), dim3(256), 0, s,
                        reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
-                       reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.pos, c.next_position, c.H,
-                       c.W, T, Tw, vpr);
+                       reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.pos, c.next_position,
+                       row_map(c), c.H, c.W, T, Tw, vpr);
     *advanced = true;
     return hipGetLastError();
   }
@@ -290,7 +292,7 @@ hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void*
   hipLaunchKernelGGL(append_rows_kernel, dim3((unsigned)blocks), dim3(threads), 0, s,
                      reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
                      reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.pos,
-                     c.next_position, c.B, c.H, c.W, T, Tw, vpr);
+                     c.next_position, row_map(c), c.B, c.H, c.W, T, Tw, vpr);
   return hipGetLastError();
 }
 
@@ -301,7 +303,7 @@ hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void*
                        reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new),
                        reinterpret_cast<uint16_t*>(c.k_stage), reinterpret_cast<uint16_t*>(c.v_stage),
                        reinterpret_cast<int8_t*>(c.k), reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale,
-                       c.witness, c.pos, c.next_position, c.H, c.W, T);
+                       c.witness, c.pos, c.next_position, row_map(c), c.H, c.W, T);
     *advanced = true;
     return hipGetLastError();
   }
@@ -314,7 +316,7 @@ hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void*
                      reinterpret_cast<const uint16_t*>(c.k_stage),
                      reinterpret_cast<const uint16_t*>(c.v_stage), reinterpret_cast<int8_t*>(c.k),
                      reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale, c.witness, c.pos,
-                     c.next_position, c.H, c.W, T);
+                     c.next_position, row_map(c), c.H, c.W, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int vpr = c.D * 2 / 16;

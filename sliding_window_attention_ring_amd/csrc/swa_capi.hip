@@ -28,7 +28,8 @@ bool head_dim_supported(int kind, int D) {
 int check_cache(const swa_cache* c) {
   if (c == nullptr) return SWA_ENULL;
   if (c->kind != SWA_KV_BF16 && c->kind != SWA_KV_FP32 && c->kind != SWA_KV_INT8) return SWA_EUNSUPPORTED;
-  if (c->B < 1 || c->H < 1 || c->W < 1 || c->reserved != 0) return SWA_EINVAL;
+  if (c->B < 1 || c->H < 1 || c->W < 1) return SWA_EINVAL;
+  if (c->layout != SWA_LAYOUT_RING && c->layout != SWA_LAYOUT_PAGED) return SWA_EINVAL;
   if (c->B > 65535 || c->H > 65535) return SWA_EINVAL;  // grid y/z limits
   if (!head_dim_supported(c->kind, c->D)) return SWA_EUNSUPPORTED;
   if (c->kind == SWA_KV_INT8 && c->W % 16 != 0) return SWA_EINVAL;
@@ -39,6 +40,11 @@ int check_cache(const swa_cache* c) {
     return SWA_ENULL;
   if (!aligned16(c->k) || !aligned16(c->v)) return SWA_EALIGN;
   if (((uintptr_t)c->pos & 3u) || ((uintptr_t)c->next_position & 3u)) return SWA_EALIGN;
+  if (c->layout == SWA_LAYOUT_PAGED) {
+    if (c->W % 16 != 0 || c->num_pages < 1) return SWA_EINVAL;
+    if (c->block_table == nullptr) return SWA_ENULL;
+    if ((uintptr_t)c->block_table & 3u) return SWA_EALIGN;
+  }
   if (c->kind == SWA_KV_INT8) {
     if (!c->k_scale || !c->v_scale || !c->witness || !c->k_stage || !c->v_stage) return SWA_ENULL;
     if (!aligned16(c->k_stage) || !aligned16(c->v_stage) || !aligned16(c->witness)) return SWA_EALIGN;
@@ -88,8 +94,10 @@ __global__ void fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
 }
 
 // Slot s must hold the newest position p < lim with p mod W == s, or -1.
-// lim = n for row caches, 16*(n/16) for INT8 (only committed blocks).
+// lim = n for row caches, 16*(n/16) for INT8 (only committed blocks).  A
+// paged cache must also map every live slot to a page of the pool.
 __global__ void validate_kernel(const int32_t* __restrict__ pos, const int32_t* __restrict__ np,
+                                const int32_t* __restrict__ table, int64_t num_pages,
                                 int32_t* __restrict__ violations, int B, int W, int int8) {
   const int64_t total = (int64_t)B * W;
   int bad = 0;
@@ -101,6 +109,10 @@ __global__ void validate_kernel(const int32_t* __restrict__ pos, const int32_t* 
     const int64_t lim = int8 ? (n / 16) * 16 : n;
     const int64_t expect = (lim <= s) ? -1 : s + (int64_t)W * ((lim - 1 - s) / W);
     bad += (pos[i] != expect);
+    if (table != nullptr && expect >= 0) {
+      const int64_t page = table[(int64_t)b * (W / 16) + s / 16];
+      bad += (page < 0 || page >= num_pages);
+    }
   }
   if (bad) atomicAdd(violations, bad);
 }
@@ -137,8 +149,10 @@ SplitPlan plan_decode(const swa_cache& c) {
 hipError_t launch_reset(const swa_cache& c, hipStream_t s) {
   const int64_t n = (int64_t)c.B * c.W > (int64_t)c.B * c.H * (c.W / 16) ? (int64_t)c.B * c.W
                                                                           : (int64_t)c.B * c.H * (c.W / 16);
+  // Pools of a paged cache may be shared with other caches: leave them alone.
+  const int clear_scales = c.kind == SWA_KV_INT8 && c.layout == SWA_LAYOUT_RING ? 1 : 0;
   hipLaunchKernelGGL(reset_kernel, dim3(grid_for(n > c.B ? n : c.B, 256, 1 << 16)), dim3(256), 0, s, c.pos,
-                     c.next_position, c.k_scale, c.v_scale, c.B, c.H, c.W, c.kind == SWA_KV_INT8 ? 1 : 0);
+                     c.next_position, c.k_scale, c.v_scale, c.B, c.H, c.W, clear_scales);
   return hipGetLastError();
 }
 
@@ -151,7 +165,8 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 hipError_t launch_validate(const swa_cache& c, int32_t* violations, hipStream_t s) {
   hipLaunchKernelGGL(validate_kernel, dim3(grid_for((int64_t)c.B * c.W, 256, 1 << 16)), dim3(256), 0, s,
-                     c.pos, c.next_position, violations, c.B, c.W, c.kind == SWA_KV_INT8 ? 1 : 0);
+                     c.pos, c.next_position, c.layout == SWA_LAYOUT_PAGED ? c.block_table : nullptr,
+                     c.num_pages, violations, c.B, c.W, c.kind == SWA_KV_INT8 ? 1 : 0);
   return hipGetLastError();
 }
 

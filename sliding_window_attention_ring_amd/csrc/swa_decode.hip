@@ -88,11 +88,11 @@ constexpr float kNegBig = -1e30f;  // finite start value of the running max
 #define SWA_ROW_U 4
 #endif
 
-template <typename T, int D, int NW, int U>
+template <typename T, int D, int NW, int U, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
-    const uint4* __restrict__ q, float* __restrict__ out, float* __restrict__ part,
-    int H, int W, int chunk, int nsplit_max) {
+    const int32_t* __restrict__ table, int64_t num_pages, const uint4* __restrict__ q, float* __restrict__ out,
+    float* __restrict__ part, int H, int W, int chunk, int nsplit_max) {
   using F = RowFmt<T>;
   constexpr int EPV = F::kEpv;
   constexpr int VPR = D / EPV;          // 16-byte vectors per row
@@ -123,6 +123,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   // offsets from a wave-uniform base.
   const char* Kbh = reinterpret_cast<const char*>(K + bh * (int64_t)W * VPR);
   const char* Vbh = reinterpret_cast<const char*>(V + bh * (int64_t)W * VPR);
+  // Paged rows: the pages of this split's 16-slot blocks, staged in LDS once.
+  extern __shared__ int32_t sm_pages[];
+  const int pb0 = r0 >> 4;
+  if constexpr (PAGED) {
+    const int npb = ((r1 + 15) >> 4) - pb0;
+    const int32_t* tb = table + (int64_t)b * (W / 16) + pb0;
+    for (int i = threadIdx.x; i < npb; i += NW * 64) sm_pages[i] = (int32_t)clamp_page(tb[i], num_pages);
+    __syncthreads();
+  }
 
   const float qscale = kLog2e / sqrtf((float)D);  // base-2 softmax of q.k/sqrt(D)
   const typename F::Q qv = F::load_q(q[bh * VPR + vec], qscale);
@@ -136,9 +145,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     for (int u = 0; u < U; ++u) {
       int row = base + u * RPL + g;
       row = row < r1 ? row : r1 - 1;  // past the end: re-read a live row, masked below
-      const uint32_t off = (uint32_t)(row * VPR + vec) * 16u;
-      kb[u] = load_stream(reinterpret_cast<const uint4*>(Kbh + off));
-      vb[u] = load_stream(reinterpret_cast<const uint4*>(Vbh + off));
+      if constexpr (PAGED) {
+        const int64_t page = sm_pages[(row >> 4) - pb0];
+        const int64_t off = (((page * H + h) * 16 + (row & 15)) * VPR + vec) * 16;
+        kb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(K) + off));
+        vb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(V) + off));
+      } else {
+        const uint32_t off = (uint32_t)(row * VPR + vec) * 16u;
+        kb[u] = load_stream(reinterpret_cast<const uint4*>(Kbh + off));
+        vb[u] = load_stream(reinterpret_cast<const uint4*>(Vbh + off));
+      }
     }
   };
   auto step = [&](const uint4 (&kb)[U], const uint4 (&vb)[U], int base) {
@@ -261,10 +277,20 @@ hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, c
                       hipStream_t s) {
   constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
   float* part = reinterpret_cast<float*>(ws);
-  hipLaunchKernelGGL((decode_kernel<T, D, NW, U>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
-                     reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v),
-                     c.next_position, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,
-                     plan.unit_per_split, plan.nsplit_max);
+  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  if (c.layout == SWA_LAYOUT_PAGED) {
+    // one int per 16-slot block of a split, plus one for a split start inside a block
+    const size_t lds = ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t);
+    hipLaunchKernelGGL((decode_kernel<T, D, NW, U, true>), grid, block, lds, s,
+                       reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v), c.next_position,
+                       c.block_table, c.num_pages, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,
+                       plan.unit_per_split, plan.nsplit_max);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<T, D, NW, U, false>), grid, block, 0, s,
+                       reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v), c.next_position,
+                       nullptr, (int64_t)0, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,
+                       plan.unit_per_split, plan.nsplit_max);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<D>), dim3(c.H, c.B), dim3(D), 0, s, c.next_position, part, out, c.H, c.W,

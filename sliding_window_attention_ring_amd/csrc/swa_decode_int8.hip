@@ -124,12 +124,12 @@ struct KeyDot {
 };
 #endif
 
-template <int NW, int UB>
+template <int NW, int UB, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const int32_t* __restrict__ np,
-    const uint16_t* __restrict__ q, float* __restrict__ c_all, float* __restrict__ part, int H, int W, int cb,
-    int nsplit_max) {
+    const int32_t* __restrict__ table, int64_t num_pages, const uint16_t* __restrict__ q,
+    float* __restrict__ c_all, float* __restrict__ part, int H, int W, int cb, int nsplit_max) {
   __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
   __shared__ float sm_acc[NW][D];
 
@@ -185,19 +185,50 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
   const char* Wbh = reinterpret_cast<const char*>(wit + bh * (int64_t)W * 16);
   const float* ksbh = ksc + bh * wblocks;
   const float* vsbh = vsc + bh * wblocks;
+  // Paged cache: block kb lives in page table[b][kb mod W/16]; this split's
+  // pages are staged in LDS once.
+  extern __shared__ int32_t sm_pages[];
+  if constexpr (PAGED) {
+    const int32_t* tb = table + (int64_t)b * wblocks;
+    for (int i = threadIdx.x; i < bhi - blo; i += NW * 64)
+      sm_pages[i] = (int32_t)clamp_page(tb[(blo + i) % wblocks], num_pages);
+    __syncthreads();
+  }
+  // Byte offset of the first row of block kb in the code arrays, and the
+  // index of its scale.
+  auto block_row0 = [&](int kb) -> int64_t {
+    if constexpr (PAGED) return ((int64_t)sm_pages[kb - blo] * H + h) * 16;
+    else return bh * W + (int64_t)(kb % wblocks) * 16;
+  };
+  auto block_scale_idx = [&](int kb) -> int64_t {
+    if constexpr (PAGED) return (int64_t)sm_pages[kb - blo] * H + h;
+    else return bh * wblocks + (kb % wblocks);
+  };
 
   auto load = [&](Blk (&bk)[UB], int kb0) {
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       int kb = kb0 + ub;
       kb = kb < bhi ? kb : bhi - 1;  // past the end: re-read a live block, masked below
-      const uint32_t sb = (uint32_t)(kb % wblocks) * 16u;  // first slot of the block
-      const uint32_t ok = sb * D + (uint32_t)lane * 16u;
-      bk[ub].k0 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok));
-      bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok + 1024u));
-      bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok));
-      bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok + 1024u));
-      bk[ub].w = load_stream(reinterpret_cast<const uint2*>(Wbh + sb * 32u + (uint32_t)lane * 8u));
+      if constexpr (PAGED) {
+        const int64_t r0w = block_row0(kb);
+        const char* kp = reinterpret_cast<const char*>(Kc) + r0w * D + lane * 16;
+        const char* vp = reinterpret_cast<const char*>(Vc) + r0w * D + lane * 16;
+        bk[ub].k0 = load_stream(reinterpret_cast<const uint4*>(kp));
+        bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(kp + 1024));
+        bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(vp));
+        bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(vp + 1024));
+        bk[ub].w = load_stream(reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(wit) + r0w * 32 +
+                                                              lane * 8));
+      } else {
+        const uint32_t sb = (uint32_t)(kb % wblocks) * 16u;  // first slot of the block
+        const uint32_t ok = sb * D + (uint32_t)lane * 16u;
+        bk[ub].k0 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok));
+        bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok + 1024u));
+        bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok));
+        bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok + 1024u));
+        bk[ub].w = load_stream(reinterpret_cast<const uint2*>(Wbh + sb * 32u + (uint32_t)lane * 8u));
+      }
     }
   };
 
@@ -209,8 +240,15 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
       const bool live = kb < bhi;
       const int kbc = live ? kb : bhi - 1;
       const int sbk = kbc % wblocks;
-      const float sk = ksbh[sbk];
-      sv[ub] = vsbh[sbk];
+      float sk;
+      if constexpr (PAGED) {
+        const int64_t si = block_scale_idx(kbc);
+        sk = ksc[si];
+        sv[ub] = vsc[si];
+      } else {
+        sk = ksbh[sbk];
+        sv[ub] = vsbh[sbk];
+      }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float d = kd.dot(half ? cur[ub].k1 : cur[ub].k0);
@@ -412,10 +450,21 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
     if (e != hipSuccess) return e;
   }
   float* part = reinterpret_cast<float*>(ws);
-  hipLaunchKernelGGL((decode_int8_kernel<NW, UB>), dim3(plan.nsplit_max, c.H, c.B), dim3(NW * 64), 0, s,
-                     reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
-                     c.v_scale, c.witness, c.next_position, reinterpret_cast<const uint16_t*>(q), c_all, part,
-                     c.H, c.W, plan.unit_per_split, plan.nsplit_max);
+  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  if (c.layout == SWA_LAYOUT_PAGED) {
+    const size_t lds = ((size_t)plan.unit_per_split + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL((decode_int8_kernel<NW, UB, true>), grid, block, lds, s,
+                       reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
+                       c.v_scale, c.witness, c.next_position, c.block_table, c.num_pages,
+                       reinterpret_cast<const uint16_t*>(q), c_all, part, c.H, c.W, plan.unit_per_split,
+                       plan.nsplit_max);
+  } else {
+    hipLaunchKernelGGL((decode_int8_kernel<NW, UB, false>), grid, block, 0, s,
+                       reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
+                       c.v_scale, c.witness, c.next_position, nullptr, (int64_t)0,
+                       reinterpret_cast<const uint16_t*>(q), c_all, part, c.H, c.W, plan.unit_per_split,
+                       plan.nsplit_max);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_int8_kernel, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part,

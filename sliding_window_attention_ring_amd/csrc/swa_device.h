@@ -95,6 +95,35 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+// A page id read from a caller-filled block table, clamped into the pool so
+// that a bad entry can never address memory outside it (swa_validate
+// reports such entries).
+__device__ __forceinline__ int64_t clamp_page(int32_t page, int64_t num_pages) {
+  const int64_t p = page < 0 ? 0 : page;
+  return p < num_pages ? p : num_pages - 1;
+}
+
+// Where row `slot` of (b, h) lives: the contiguous ring [B][H][W] (table
+// null) or row slot%16 of page block_table[b][slot/16] in a pool
+// [pages][H][16].  row() is in units of rows; block() indexes per-block
+// values ([B][H][W/16] or [pages][H]).
+struct RowMap {
+  const int32_t* table;
+  int64_t num_pages;
+  int H, W;
+  __device__ __forceinline__ int64_t page(int b, int64_t slot) const {
+    return clamp_page(table[(int64_t)b * (W / 16) + (slot >> 4)], num_pages);
+  }
+  __device__ __forceinline__ int64_t row(int b, int h, int64_t slot) const {
+    if (table == nullptr) return ((int64_t)b * H + h) * W + slot;
+    return (page(b, slot) * H + h) * 16 + (slot & 15);
+  }
+  __device__ __forceinline__ int64_t block(int b, int h, int64_t slot) const {
+    if (table == nullptr) return ((int64_t)b * H + h) * (W / 16) + (slot >> 4);
+    return page(b, slot) * H + h;
+  }
+};
+
 // Log-sum-exp merge of split partials laid out as [nsplit][PF] floats with
 // m at 0, l at 1 and acc at 4.. (base-2 scores): M = max m_s, L = sum
 // 2^(m_s-M) l_s, A = sum 2^(m_s-M) acc_s[t].  Loads are issued eight splits

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/swa.h"
+#include "swa_device.h"
 
 namespace swa {
 
@@ -18,6 +19,10 @@ struct SplitPlan {
 };
 
 SplitPlan plan_decode(const swa_cache& c);
+
+inline RowMap row_map(const swa_cache& c) {
+  return RowMap{c.layout == SWA_LAYOUT_PAGED ? c.block_table : nullptr, c.num_pages, c.H, c.W};
+}
 
 // Floats per split partial: m, l, cmax, pad, acc[D].
 inline int partial_floats(int D) { return D + 4; }

@@ -39,9 +39,40 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return bits.to_f64(host_bits(t))
 
 
+class RingView:
+    """A cache's storage in ring layout: the tensors themselves for a ring
+    cache, gathered through the block table for a paged one."""
+
+    def __init__(self, cache):
+        self.B, self.H, self.W, self.kind = cache.B, cache.H, cache.W, cache.kind
+        self.pos, self.next_position = cache.pos, cache.next_position
+        self.k_stage, self.v_stage = cache.k_stage, cache.v_stage
+        if cache.layout == "ring":
+            self.k, self.v = cache.k, cache.v
+            self.k_scale, self.v_scale, self.witness = cache.k_scale, cache.v_scale, cache.witness
+            return
+        tbl = cache.block_table.long()                       # [B, W/16]
+        slots = torch.arange(cache.W, device=tbl.device)
+        pages = tbl[:, slots // 16]                          # [B, W]
+        rows = (slots % 16).expand_as(pages)
+
+        def gather(pool):                                    # [P, H, 16, X] -> [B, H, W, X]
+            return pool[pages, :, rows].permute(0, 2, 1, 3).contiguous()
+
+        self.k, self.v = gather(cache.k), gather(cache.v)
+        if cache.kind == "int8":
+            self.witness = gather(cache.witness)
+            self.k_scale = cache.k_scale[tbl].permute(0, 2, 1).contiguous()  # [B, H, W/16]
+            self.v_scale = cache.v_scale[tbl].permute(0, 2, 1).contiguous()
+        else:
+            self.k_scale = self.v_scale = self.witness = None
+
+
 def check_ring_rows(cache, k_in: np.ndarray, v_in: np.ndarray, n: np.ndarray):
     """bf16/fp32 cache: pos, next_position and every live slot's K/V bits equal
     what the ring must hold after n[b] appends of rows k_in[b][h][p] (bits)."""
+    if not isinstance(cache, RingView) and getattr(cache, "layout", "ring") == "paged":
+        cache = RingView(cache)
     pos = host_bits(cache.pos)
     npos = host_bits(cache.next_position)
     kk, vv = host_bits(cache.k), host_bits(cache.v)
@@ -73,6 +104,8 @@ def check_int8_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, n:
     """INT8 cache of (b, h): codes, scales, slot positions bit-exact vs the
     oracle; stored witness never below the exact band norm and within one
     fp16 step above it; staging rows equal the input bits."""
+    if getattr(cache, "layout", "ring") == "paged":
+        cache = RingView(cache)
     st = decoder.expected_int8_store(k64, v64, n, cache.W)
     kc = host_bits(cache.k[b, h]); vc = host_bits(cache.v[b, h])
     ks = host_bits(cache.k_scale[b, h]); vs = host_bits(cache.v_scale[b, h])

@@ -35,9 +35,9 @@ def test_header_and_exports_agree():
 
 def desc(**kw):
     from sliding_window_attention_ring_amd._capi import SwaCacheDesc
-    base = dict(kind=0, B=2, H=4, D=128, W=64, reserved=0, k=0x10000, v=0x20000, pos=0x30000,
+    base = dict(kind=0, B=2, H=4, D=128, W=64, layout=0, k=0x10000, v=0x20000, pos=0x30000,
                 next_position=0x40000, k_scale=0x50000, v_scale=0x60000, witness=0x70000,
-                k_stage=0x80000, v_stage=0x90000)
+                k_stage=0x80000, v_stage=0x90000, block_table=0xC0000, num_pages=8)
     base.update(kw)
     return SwaCacheDesc(**base)
 
@@ -58,7 +58,12 @@ def test_argument_checks_return_codes():
     ws = ctypes.c_void_p(0xB0000)
     assert L.kv_append(None, A16, A16, 1, None) == -2                       # NULL cache
     assert L.kv_append(p(desc(B=0)), A16, A16, 1, None) == -1               # B < 1
-    assert L.kv_append(p(desc(reserved=1)), A16, A16, 1, None) == -1
+    assert L.kv_append(p(desc(layout=2)), A16, A16, 1, None) == -1              # unknown layout
+    assert L.kv_append(p(desc(layout=1, W=20)), A16, A16, 1, None) == -1        # paged W % 16
+    assert L.kv_append(p(desc(layout=1, num_pages=0)), A16, A16, 1, None) == -1
+    assert L.kv_append(p(desc(layout=1, block_table=None)), A16, A16, 1, None) == -2
+    assert L.kv_append(p(desc(layout=1, block_table=0xC0002)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(layout=1)), A16, A16, 0, None) == 0
     assert L.kv_append(p(desc(D=100)), A16, A16, 1, None) == -4             # head_dim
     assert L.kv_append(p(desc(kind=7)), A16, A16, 1, None) == -4
     assert L.kv_append(p(desc(kind=2, W=20)), A16, A16, 1, None) == -1      # INT8 W % 16

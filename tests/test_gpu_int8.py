@@ -22,7 +22,7 @@ def _gpu():
     require_gpu()
 
 
-def run(W, Ts, B=2, H=2, steps_total=None, seed=0, check_store_every=1):
+def run(W, Ts, B=2, H=2, steps_total=None, seed=0, check_store_every=1, layout="ring"):
     import sliding_window_attention_ring_amd as swa
     D = 128
     g = torch.Generator().manual_seed(seed)
@@ -31,7 +31,7 @@ def run(W, Ts, B=2, H=2, steps_total=None, seed=0, check_store_every=1):
     k = torch.randn((B, H, N, D), generator=g).to(torch.bfloat16)
     v = torch.randn((B, H, N, D), generator=g).to(torch.bfloat16)
     k64, v64 = f64(k), f64(v)
-    cache = swa.KVCache("int8", B, H, D, W)
+    cache = swa.KVCache("int8", B, H, D, W, layout=layout)
     n, i = 0, 0
     while n < total:
         T = Ts[i % len(Ts)]
