@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+from dataclasses import replace
 import json
 import os
 import sys
@@ -65,22 +66,26 @@ def read_traffic(workload: str, kind: str):
         return None
 
 
-def step_bytes(wl, n_after: int):
+def step_bytes(wl, n_after):
     """Algorithmic HBM bytes of one step whose append brings next_position to
-    n_after: (decode bytes, append bytes, visible tokens per (b, h))."""
+    n_after (an int, or one int per sequence): (decode bytes, append bytes,
+    visible tokens summed over sequences, per head)."""
+    if not isinstance(n_after, int):
+        parts = [step_bytes(replace(wl, B=1), int(n)) for n in n_after]
+        return tuple(sum(p[i] for p in parts) for i in range(3))
     BH, D = wl.B * wl.H, wl.D
-    vis = min(wl.W, n_after)
+    vis = min(wl.W, n_after) * wl.B
     q_out = BH * D * 2 + BH * D * 4
     if wl.kind == "int8":
         staged = n_after % 16
-        quant = vis - staged
+        quant = min(wl.W, n_after) - staged
         dec = BH * (quant * (2 * D + 2 * D // 8 + 2 * 4 / 16) + staged * 2 * D * 2) + q_out + BH * 4
         app = BH * 2 * D * 2 * 2  # read the new rows, write them to staging
         if n_after % 16 == 0:     # a block completes: read 16 staged rows, write codes/witness/scales
             app += BH * 16 * (2 * D * 2 + 2 * D + 2 * D // 8) + BH * 2 * 4
     else:
         esz = 4 if wl.kind == "fp32" else 2
-        dec = BH * vis * 2 * D * esz + (BH * D * esz + BH * D * 4)
+        dec = BH * min(wl.W, n_after) * 2 * D * esz + (BH * D * esz + BH * D * 4)
         app = BH * 2 * D * esz * 2 + wl.B * 4
     return dec, app, vis
 
@@ -156,17 +161,22 @@ def main():
     n_steps = args.warmup + args.steps
     prefill = wl.prefill or wl.W
     total = prefill + n_steps
+    lens = gen.ragged_lengths(wl) if wl.ragged else None  # per-sequence prefill lengths
     log(f"[bench] workload {wl.name}: B={wl.B} H={wl.H} D={wl.D} W={wl.W} prefill={prefill} "
         f"steps={args.steps} warmup={args.warmup}")
 
     t0 = time.time()
     k_all = gen.tokens(wl, "k", total, device=dev)
     v_all = gen.tokens(wl, "v", total, device=dev)
-    cache = swa.KVCache(wl.kind, wl.B, wl.H, wl.D, wl.W, device=dev)
-    chunk = wl.prefill_chunk or prefill
-    for c0 in range(0, prefill, chunk):
-        c1 = min(prefill, c0 + chunk)
-        swa.kv_append(cache, k_all[:, :, c0:c1].contiguous(), v_all[:, :, c0:c1].contiguous())
+    cache = swa.KVCache(wl.kind, wl.B, wl.H, wl.D, wl.W, device=dev, layout=wl.layout)
+    if lens is not None:
+        for b, n in enumerate(lens):
+            swa.kv_append(cache.seq_view(b), k_all[b:b + 1, :, :n].contiguous(), v_all[b:b + 1, :, :n].contiguous())
+    else:
+        chunk = wl.prefill_chunk or prefill
+        for c0 in range(0, prefill, chunk):
+            c1 = min(prefill, c0 + chunk)
+            swa.kv_append(cache, k_all[:, :, c0:c1].contiguous(), v_all[:, :, c0:c1].contiguous())
     ks = [k_all[:, :, p:p + 1].contiguous() for p in range(prefill, total)]
     vs = [v_all[:, :, p:p + 1].contiguous() for p in range(prefill, total)]
     qs = [gen.query(wl, p, device=dev) for p in range(prefill, total)]
@@ -200,7 +210,8 @@ def main():
            for _ in range(args.steps)]
     dec_bytes = app_bytes = vis_tokens = 0.0
     for i in range(args.steps):
-        d, a, vis = step_bytes(wl, prefill + args.warmup + i + 1)
+        done = args.warmup + i + 1
+        d, a, vis = step_bytes(wl, prefill + done if lens is None else [int(n) + done for n in lens])
         dec_bytes, app_bytes, vis_tokens = dec_bytes + d, app_bytes + a, vis_tokens + vis
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -235,12 +246,13 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "head_dim": wl.D, "window": wl.W,
-                   "context": min(wl.W, prefill), "kv_dtype": wl.kind,
+                   "context": min(wl.W, prefill) if lens is None else [int(n) for n in lens],
+                   "kv_dtype": wl.kind, "layout": wl.layout,
                    "positions": [prefill + args.warmup, prefill + n_steps - 1],
                    "step": "kv_append(T=1) + " + ("decode_attn_int8_witness" if wl.kind == "int8"
                                                   else "decode_attn")},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
-        "kv_token_heads_per_s": vis_tokens * BH / elapsed,
+        "kv_token_heads_per_s": vis_tokens * wl.H / elapsed,
         "query_token_heads_per_s": BH * args.steps / elapsed,
         "roofline": {
             "bound": "hbm",
@@ -255,7 +267,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and lens is None:
         log("[bench] timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(wl, k_all, v_all, lambda p: gen.query(wl, p), prefill)
     print(json.dumps(result), flush=True)

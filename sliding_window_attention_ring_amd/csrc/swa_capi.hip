@@ -53,12 +53,14 @@ int check_cache(const swa_cache* c) {
   return SWA_OK;
 }
 
-// Target number of decode work-groups per launch: two per compute unit of
-// the device (512 on MI355X).  Measured on MI355X, fewer and longer splits
-// stream HBM better than many short ones (each split pays a query load and
-// a partial write, and the merge reads every partial), and two 4-wave
-// work-groups per CU already keep enough loads in flight.  SWA_TARGET_WGS
-// overrides it; read once per process so workspace sizes stay consistent.
+// Target number of decode work-groups per launch: one per compute unit of
+// the device (256 on MI355X); the split size is then rounded to whole
+// iteration rounds and capped at the window, so shapes with many (b, h)
+// pairs still get one split per pair (512 work-groups at B*H = 512).
+// Measured on MI355X, fewer and longer splits stream HBM better than many
+// short ones: each split pays a query load, its pipeline fill and a partial
+// write, and the merge reads every partial.  SWA_TARGET_WGS overrides it;
+// read once per process so workspace sizes stay consistent.
 int target_wgs() {
   static int v = [] {
     const char* s = getenv("SWA_TARGET_WGS");
@@ -68,7 +70,7 @@ int target_wgs() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    return 2 * cus;
+    return cus;
   }();
   return v;
 }

@@ -28,6 +28,7 @@ class Workload:
     spike_mul: float = 8.0
     rope_base: Optional[float] = None
     prefill_chunk: int = 0   # 0 = one chunk
+    layout: str = "ring"     # "ring" | "paged" (16-token pages through a block table)
     note: str = field(default="", compare=False)
 
 
@@ -49,4 +50,12 @@ BF16_32K = Workload(6, "bf16-ctx32768", "bf16", B=16, H=32, D=128, W=32768, pref
                     rope_base=10000.0, prefill_chunk=8192,
                     note="bf16 companion of the INT8 32k workload")
 
-ALL = {w.name: w for w in (TINY, FULL_RAGGED, RING, LONG, INT8_32K, BF16_32K)}
+# Same inputs as the ring workloads above (same seed namespace), paged storage.
+INT8_32K_PAGED = Workload(5, "int8-witness-ctx32768-paged", "int8", B=16, H=32, D=128, W=32768,
+                          prefill=32768, steps=20, rope_base=10000.0, prefill_chunk=8192, layout="paged",
+                          note="the INT8 32k workload in 16-token pages")
+BF16_32K_PAGED = Workload(6, "bf16-ctx32768-paged", "bf16", B=16, H=32, D=128, W=32768, prefill=32768,
+                          rope_base=10000.0, prefill_chunk=8192, layout="paged",
+                          note="the bf16 32k workload in 16-token pages")
+
+ALL = {w.name: w for w in (TINY, FULL_RAGGED, RING, LONG, INT8_32K, BF16_32K, INT8_32K_PAGED, BF16_32K_PAGED)}
