@@ -101,6 +101,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   constexpr int RPI = RPL * U;          // rows per wave iteration
   constexpr int PF = D + 4;             // floats per split partial
   static_assert(LPR >= 2 && LPR <= 32, "row must span 2..32 lanes");
+  static_assert(16 % RPL == 0, "a wave load must not straddle a 16-row page");
 
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
@@ -146,10 +147,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       int row = base + u * RPL + g;
       row = row < r1 ? row : r1 - 1;  // past the end: re-read a live row, masked below
       if constexpr (PAGED) {
-        const int64_t page = sm_pages[(row >> 4) - pb0];
-        const int64_t off = (((page * H + h) * 16 + (row & 15)) * VPR + vec) * 16;
-        kb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(K) + off));
-        vb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(V) + off));
+        // The RPL rows of load u lie in one 16-row page (RPL divides 16 and
+        // the split starts on a page), also after clamping at the end, so the
+        // page is wave-uniform: a scalar base plus a 32-bit lane offset.
+        int first = base + u * RPL;
+        first = first < r1 ? first : r1 - 1;
+        const int64_t page = __builtin_amdgcn_readfirstlane(sm_pages[(first >> 4) - pb0]);
+        const int64_t pbase = (page * H + h) * (16 * VPR * 16);
+        const uint32_t off = (uint32_t)((row & 15) * VPR + vec) * 16u;
+        kb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(K) + pbase + off));
+        vb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(V) + pbase + off));
       } else {
         const uint32_t off = (uint32_t)(row * VPR + vec) * 16u;
         kb[u] = load_stream(reinterpret_cast<const uint4*>(Kbh + off));

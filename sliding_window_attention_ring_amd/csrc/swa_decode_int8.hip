@@ -48,9 +48,12 @@ constexpr float kNegBig = -1e30f;
 // band norms of q, the 16-term sum and 1/sqrt(D) (each well below 2^-20).
 constexpr float kBoundPad = 1.0f + 0x1p-12f;
 
+// One 16-token block in flight: codes, witness and the two block scales
+// (loaded with the codes so their latency is hidden by the prefetch too).
 struct Blk {
   uint4 k0, k1, v0, v1;
   uint2 w;
+  float sk, sv;
 };
 
 // Dot product of this lane's 16 query dims with 16 int8 key codes, in
@@ -196,13 +199,9 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
   }
   // Byte offset of the first row of block kb in the code arrays, and the
   // index of its scale.
-  auto block_row0 = [&](int kb) -> int64_t {
-    if constexpr (PAGED) return ((int64_t)sm_pages[kb - blo] * H + h) * 16;
-    else return bh * W + (int64_t)(kb % wblocks) * 16;
-  };
-  auto block_scale_idx = [&](int kb) -> int64_t {
-    if constexpr (PAGED) return (int64_t)sm_pages[kb - blo] * H + h;
-    else return bh * wblocks + (kb % wblocks);
+  // Page of block kb (wave-uniform, so the address math stays scalar).
+  auto block_page = [&](int kb) -> int64_t {
+    return (int64_t)__builtin_amdgcn_readfirstlane(sm_pages[kb - blo]);
   };
 
   auto load = [&](Blk (&bk)[UB], int kb0) {
@@ -211,15 +210,17 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
       int kb = kb0 + ub;
       kb = kb < bhi ? kb : bhi - 1;  // past the end: re-read a live block, masked below
       if constexpr (PAGED) {
-        const int64_t r0w = block_row0(kb);
-        const char* kp = reinterpret_cast<const char*>(Kc) + r0w * D + lane * 16;
-        const char* vp = reinterpret_cast<const char*>(Vc) + r0w * D + lane * 16;
-        bk[ub].k0 = load_stream(reinterpret_cast<const uint4*>(kp));
-        bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(kp + 1024));
-        bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(vp));
-        bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(vp + 1024));
-        bk[ub].w = load_stream(reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(wit) + r0w * 32 +
-                                                              lane * 8));
+        const int64_t pi = block_page(kb) * H + h;  // (page, head) index
+        const char* kp = reinterpret_cast<const char*>(Kc) + pi * (16 * D);
+        const char* vp = reinterpret_cast<const char*>(Vc) + pi * (16 * D);
+        const char* wp = reinterpret_cast<const char*>(wit) + pi * (16 * 32);
+        bk[ub].k0 = load_stream(reinterpret_cast<const uint4*>(kp + lane * 16));
+        bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(kp + 1024 + lane * 16));
+        bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(vp + lane * 16));
+        bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(vp + 1024 + lane * 16));
+        bk[ub].w = load_stream(reinterpret_cast<const uint2*>(wp + lane * 8));
+        bk[ub].sk = ksc[pi];
+        bk[ub].sv = vsc[pi];
       } else {
         const uint32_t sb = (uint32_t)(kb % wblocks) * 16u;  // first slot of the block
         const uint32_t ok = sb * D + (uint32_t)lane * 16u;
@@ -228,6 +229,8 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
         bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok));
         bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok + 1024u));
         bk[ub].w = load_stream(reinterpret_cast<const uint2*>(Wbh + sb * 32u + (uint32_t)lane * 8u));
+        bk[ub].sk = ksbh[kb % wblocks];
+        bk[ub].sv = vsbh[kb % wblocks];
       }
     }
   };
@@ -240,15 +243,8 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
       const bool live = kb < bhi;
       const int kbc = live ? kb : bhi - 1;
       const int sbk = kbc % wblocks;
-      float sk;
-      if constexpr (PAGED) {
-        const int64_t si = block_scale_idx(kbc);
-        sk = ksc[si];
-        sv[ub] = vsc[si];
-      } else {
-        sk = ksbh[sbk];
-        sv[ub] = vsbh[sbk];
-      }
+      const float sk = cur[ub].sk;
+      sv[ub] = cur[ub].sv;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float d = kd.dot(half ? cur[ub].k1 : cur[ub].k0);
