@@ -88,7 +88,9 @@ constexpr float kNegBig = -1e30f;  // finite start value of the running max
 #define SWA_ROW_U 4
 #endif
 
-template <typename T, int D, int NW, int U, bool PAGED>
+// FINAL: the host plan has one split per (b, h), so the work-group writes
+// the output itself (zeros for an empty sequence) and no merge kernel runs.
+template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
     const int32_t* __restrict__ table, int64_t num_pages, const uint4* __restrict__ q, float* __restrict__ out,
@@ -112,7 +114,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   const int64_t bh = (int64_t)b * H + h;
   const int n = np[b];
   const int len = n < W ? n : W;
-  if (len <= 0) return;  // empty cache: the merge kernel writes zeros
+  if (len <= 0) {  // empty cache: zeros, written here or by the merge kernel
+    if constexpr (FINAL) {
+      for (int t = threadIdx.x; t < D; t += NW * 64) out[bh * D + t] = 0.f;
+    }
+    return;
+  }
   const int nsplit = (len + chunk - 1) / chunk;
   if (split >= nsplit) return;
   const int r0 = split * chunk;
@@ -285,21 +292,26 @@ hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, c
   constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
   float* part = reinterpret_cast<float*>(ws);
   const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
-  if (c.layout == SWA_LAYOUT_PAGED) {
-    // one int per 16-slot block of a split, plus one for a split start inside a block
-    const size_t lds = ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t);
-    hipLaunchKernelGGL((decode_kernel<T, D, NW, U, true>), grid, block, lds, s,
-                       reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v), c.next_position,
-                       c.block_table, c.num_pages, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,
-                       plan.unit_per_split, plan.nsplit_max);
+  const bool paged = c.layout == SWA_LAYOUT_PAGED;
+  // paged: one int per 16-slot block of a split, plus slack
+  const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
+  const uint4* kp = reinterpret_cast<const uint4*>(c.k);
+  const uint4* vp = reinterpret_cast<const uint4*>(c.v);
+  const uint4* qp = reinterpret_cast<const uint4*>(q);
+  const int32_t* table = paged ? c.block_table : nullptr;
+  const int64_t npages = paged ? c.num_pages : 0;
+#define SWA_ROW_LAUNCH(P, F)                                                                                     \
+  hipLaunchKernelGGL((decode_kernel<T, D, NW, U, P, F>), grid, block, lds, s, kp, vp, c.next_position, table,    \
+                     npages, qp, out, part, c.H, c.W, plan.unit_per_split, plan.nsplit_max)
+  const bool final_pass = plan.nsplit_max == 1;
+  if (paged) {
+    if (final_pass) SWA_ROW_LAUNCH(true, true); else SWA_ROW_LAUNCH(true, false);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, NW, U, false>), grid, block, 0, s,
-                       reinterpret_cast<const uint4*>(c.k), reinterpret_cast<const uint4*>(c.v), c.next_position,
-                       nullptr, (int64_t)0, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,
-                       plan.unit_per_split, plan.nsplit_max);
+    if (final_pass) SWA_ROW_LAUNCH(false, true); else SWA_ROW_LAUNCH(false, false);
   }
+#undef SWA_ROW_LAUNCH
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || final_pass) return e;
   hipLaunchKernelGGL((merge_kernel<D>), dim3(c.H, c.B), dim3(D), 0, s, c.next_position, part, out, c.H, c.W,
                      plan.unit_per_split, plan.nsplit_max);
   return hipGetLastError();

@@ -127,14 +127,77 @@ struct KeyDot {
 };
 #endif
 
-template <int NW, int UB, bool PAGED>
+// Last stage of one (b, h), run by >= 256 threads of a work-group (thread t
+// < D owns output dim t and holds the merged M, L, A of the committed
+// blocks; CM is their max c_t): fold in the exact staging tokens
+// (positions 16*(n/16) .. n-1, row = position mod 16, c_t = 0), normalize,
+// and write out, cmax and the optional TV bound and gate.
+// Optional epilogue (tv != null): every visible logit moved by at most
+// E = cmax, so the attention weights moved by at most tanh(E/2) in total
+// variation (page "WitCert", section 为什么在线监控 KV 误差如此困难 gives the
+// looser tanh(E) form); gate = tv > tau.
+__device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, float L, float A, float CM,
+                                            float* sm_s, const uint16_t* __restrict__ kst,
+                                            const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q,
+                                            float* __restrict__ out, float* __restrict__ cmax_out,
+                                            float* __restrict__ tv, int32_t* __restrict__ gate, float tau) {
+  const float qscale = kLog2e / sqrtf((float)D);
+  const int ns = n - (n / 16) * 16;
+  if (ns > 0) {
+    // Scores: 16 lanes per staged token, 8 bf16 each (threads 0..255 = 16 tokens).
+    const int tok = t >> 4, v16 = t & 15;
+    float d = 0.f;
+    if (tok < ns) {
+      float f[8], qv[8];
+      unpack8(reinterpret_cast<const uint4*>(kst + (bh * 16 + tok) * D)[v16], f);
+      unpack8(reinterpret_cast<const uint4*>(q + bh * D)[v16], qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qv[e] * qscale, f[e], d);
+    }
+    d = group_sum<16>(d);
+    if (v16 == 0 && tok < 16) sm_s[tok] = tok < ns ? d : -INFINITY;
+    __syncthreads();
+    if (t < D) {
+      float ms = -INFINITY;
+      for (int i = 0; i < ns; ++i) ms = fmaxf(ms, sm_s[i]);
+      const float Mn = fmaxf(M, ms);
+      const float sc = exp2_fast(M - Mn);
+      L *= sc;
+      A *= sc;
+      for (int i = 0; i < ns; ++i) {
+        const float p = exp2_fast(sm_s[i] - Mn);
+        L += p;
+        A = fmaf(p, bf16_to_f32(vst[(bh * 16 + i) * D + t]), A);
+      }
+    }
+  }
+  if (t < D) out[bh * D + t] = L > 0.f ? A / L : 0.f;
+  if (t == 0) {
+    const float cm = CM * kBoundPad;
+    cmax_out[bh] = cm;
+    if (tv != nullptr) {
+      // tanhf is within a few ulp; the 2^-20 pad keeps the value an upper bound.
+      const float bnd = fminf(tanhf(0.5f * cm) * (1.0f + 0x1p-20f), 1.0f);
+      tv[bh] = bnd;
+      if (gate != nullptr) gate[bh] = bnd > tau ? 1 : 0;
+    }
+  }
+}
+
+// FINAL: every (b, h) has a single split (the host plan has nsplit_max ==
+// 1), so the work-group finishes the (b, h) itself and no merge kernel runs.
+template <int NW, int UB, bool PAGED, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const int32_t* __restrict__ np,
     const int32_t* __restrict__ table, int64_t num_pages, const uint16_t* __restrict__ q,
-    float* __restrict__ c_all, float* __restrict__ part, int H, int W, int cb, int nsplit_max) {
+    float* __restrict__ c_all, float* __restrict__ part, int H, int W, int cb, int nsplit_max,
+    const uint16_t* __restrict__ kst, const uint16_t* __restrict__ vst, float* __restrict__ out,
+    float* __restrict__ cmax_out, float* __restrict__ tv, int32_t* __restrict__ gate, float tau) {
+  static_assert(NW * 64 >= 256, "the staging fold needs 256 threads");
   __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
   __shared__ float sm_acc[NW][D];
+  __shared__ float sm_s[16];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -347,18 +410,18 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     }
   }
 
-  float* my = part + (bh * nsplit_max + split) * PF;
-  if (t < D) my[4 + t] = A;
-  if (t == 0) { my[0] = M; my[1] = L; my[2] = CM; }
+  if constexpr (FINAL) {
+    finish_int8(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau);
+  } else {
+    float* my = part + (bh * nsplit_max + split) * PF;
+    if (t < D) my[4 + t] = A;
+    if (t == 0) { my[0] = M; my[1] = L; my[2] = CM; }
+  }
 }
 
-// Merge of one (b, h): log-sum-exp over the split partials, then the exact
-// staging tokens (positions 16*nb .. n-1, row = position mod 16, c_t = 0),
-// then normalization.  256 threads; thread t < D owns output dim t.
-// Optional epilogue (tv != null): every visible logit moved by at most
-// E = cmax, so the attention weights moved by at most tanh(E/2) in total
-// variation (page "WitCert", section 为什么在线监控 KV 误差如此困难 gives the
-// looser tanh(E) form); gate = tv > tau.
+// Merge of one (b, h): log-sum-exp over the split partials, then the
+// staging fold, normalization and bound epilogue of finish_int8.  256
+// threads; thread t < D owns output dim t.
 __global__ __launch_bounds__(256) void merge_int8_kernel(
     const int32_t* __restrict__ np, const float* __restrict__ part, const uint16_t* __restrict__ kst,
     const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q, float* __restrict__ out,
@@ -374,54 +437,13 @@ __global__ __launch_bounds__(256) void merge_int8_kernel(
   const int nbr = nb > k0 ? nb - k0 : 0;
   int nsplit = (nbr + cb - 1) / cb;
   if (nsplit < 1) nsplit = 1;
-  const float qscale = kLog2e / sqrtf((float)D);
-
   float M = kNegBig, L = 0.f, A = 0.f, CM = 0.f;
   if (t < D) {
     const float* pp = part + bh * nsplit_max * PF;
     merge_partials<PF>(pp, nsplit, t, M, L, A);
     for (int sp = 0; sp < nsplit; ++sp) CM = fmaxf(CM, pp[sp * PF + 2]);
   }
-  const int ns = n - nb * 16;
-  if (ns > 0) {
-    // Scores: 16 lanes per staged token, 8 bf16 each (256 threads = 16 tokens).
-    const int tok = t >> 4, v16 = t & 15;
-    float d = 0.f;
-    if (tok < ns) {
-      float f[8], qv[8];
-      unpack8(reinterpret_cast<const uint4*>(kst + (bh * 16 + tok) * D)[v16], f);
-      unpack8(reinterpret_cast<const uint4*>(q + bh * D)[v16], qv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qv[e] * qscale, f[e], d);
-    }
-    d = group_sum<16>(d);
-    if (v16 == 0) sm_s[tok] = tok < ns ? d : -INFINITY;
-    __syncthreads();
-    if (t < D) {
-      float ms = -INFINITY;
-      for (int i = 0; i < ns; ++i) ms = fmaxf(ms, sm_s[i]);
-      const float Mn = fmaxf(M, ms);
-      const float sc = exp2_fast(M - Mn);
-      L *= sc;
-      A *= sc;
-      for (int i = 0; i < ns; ++i) {
-        const float p = exp2_fast(sm_s[i] - Mn);
-        L += p;
-        A = fmaf(p, bf16_to_f32(vst[(bh * 16 + i) * D + t]), A);
-      }
-    }
-  }
-  if (t < D) out[bh * D + t] = L > 0.f ? A / L : 0.f;
-  if (t == 0) {
-    const float cm = CM * kBoundPad;
-    cmax_out[bh] = cm;
-    if (tv != nullptr) {
-      // tanhf is within a few ulp; the 2^-20 pad keeps the value an upper bound.
-      const float b = fminf(tanhf(0.5f * cm) * (1.0f + 0x1p-20f), 1.0f);
-      tv[bh] = b;
-      if (gate != nullptr) gate[bh] = b > tau ? 1 : 0;
-    }
-  }
+  finish_int8(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau);
 }
 
 __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
@@ -447,26 +469,30 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
   }
   float* part = reinterpret_cast<float*>(ws);
   const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
-  if (c.layout == SWA_LAYOUT_PAGED) {
-    const size_t lds = ((size_t)plan.unit_per_split + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL((decode_int8_kernel<NW, UB, true>), grid, block, lds, s,
-                       reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
-                       c.v_scale, c.witness, c.next_position, c.block_table, c.num_pages,
-                       reinterpret_cast<const uint16_t*>(q), c_all, part, c.H, c.W, plan.unit_per_split,
-                       plan.nsplit_max);
+  const bool paged = c.layout == SWA_LAYOUT_PAGED;
+  const size_t lds = paged ? ((size_t)plan.unit_per_split + 1) * sizeof(int32_t) : 0;
+  const int8_t* kc = reinterpret_cast<const int8_t*>(c.k);
+  const int8_t* vc = reinterpret_cast<const int8_t*>(c.v);
+  const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+  const uint16_t* kst = reinterpret_cast<const uint16_t*>(c.k_stage);
+  const uint16_t* vst = reinterpret_cast<const uint16_t*>(c.v_stage);
+  const int32_t* table = paged ? c.block_table : nullptr;
+  const int64_t npages = paged ? c.num_pages : 0;
+#define SWA_INT8_LAUNCH(P, F)                                                                                    \
+  hipLaunchKernelGGL((decode_int8_kernel<NW, UB, P, F>), grid, block, lds, s, kc, vc, c.k_scale, c.v_scale,     \
+                     c.witness, c.next_position, table, npages, q16, c_all, part, c.H, c.W, plan.unit_per_split, \
+                     plan.nsplit_max, kst, vst, out, cmax, tv, gate, tau)
+  const bool final_pass = plan.nsplit_max == 1;
+  if (paged) {
+    if (final_pass) SWA_INT8_LAUNCH(true, true); else SWA_INT8_LAUNCH(true, false);
   } else {
-    hipLaunchKernelGGL((decode_int8_kernel<NW, UB, false>), grid, block, 0, s,
-                       reinterpret_cast<const int8_t*>(c.k), reinterpret_cast<const int8_t*>(c.v), c.k_scale,
-                       c.v_scale, c.witness, c.next_position, nullptr, (int64_t)0,
-                       reinterpret_cast<const uint16_t*>(q), c_all, part, c.H, c.W, plan.unit_per_split,
-                       plan.nsplit_max);
+    if (final_pass) SWA_INT8_LAUNCH(false, true); else SWA_INT8_LAUNCH(false, false);
   }
+#undef SWA_INT8_LAUNCH
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_int8_kernel, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part,
-                     reinterpret_cast<const uint16_t*>(c.k_stage), reinterpret_cast<const uint16_t*>(c.v_stage),
-                     reinterpret_cast<const uint16_t*>(q), out, cmax, tv, gate, tau, c.H, c.W,
-                     plan.unit_per_split, plan.nsplit_max);
+  if (e != hipSuccess || final_pass) return e;
+  hipLaunchKernelGGL(merge_int8_kernel, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst, q16, out,
+                     cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max);
   return hipGetLastError();
 }
 

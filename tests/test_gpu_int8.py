@@ -149,3 +149,30 @@ def test_int8_tv_bound_and_gate():
             assert t <= r["bound"] * (1 + 2.0 ** -8) + 1e-7, (t, r["bound"])
             assert gate[b, h] == (1 if t > 0.2 else 0)
             assert gate[b, h] == (1 if (b, h) == (1, 2) else 0)
+
+
+@pytest.mark.parametrize("W", [16, 512])
+def test_int8_empty_and_short_sequences(W):
+    """n = 0 gives zero output and cmax 0; n < 16 (staging only) gives exact
+    attention over the staged rows with cmax 0 -- on the single-split path
+    (W=16) and with a merge kernel (W=512)."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, D = 3, 2, 128
+    g = torch.Generator().manual_seed(W + 1)
+    lens = [0, 7, 40]
+    k = torch.randn((B, H, max(lens), D), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, max(lens), D), generator=g).to(torch.bfloat16)
+    cache = swa.KVCache("int8", B, H, D, W)
+    for b, n in enumerate(lens):
+        if n:
+            swa.kv_append(cache.seq_view(b), k[b:b + 1, :, :n].contiguous().cuda(), v[b:b + 1, :, :n].contiguous().cuda())
+    q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+    out, cmax, c_all = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
+    out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
+    assert not out[0].any() and not cmax[0].any() and not c_all[0].any()
+    assert not cmax[1].any()
+    k64, v64, q64 = f64(k), f64(v), f64(q)
+    for b in (1, 2):
+        for h in range(H):
+            check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, q64[b, h], k64[b, h], v64[b, h], lens[b], W,
+                              what=f"W={W}")

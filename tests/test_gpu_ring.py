@@ -130,3 +130,25 @@ def test_decode_is_repeatable_and_workspace_reusable():
     assert torch.equal(a, b)
     ref = oracle_out(f64(k[1]), f64(v[1]), f64(q[1]), W, W)
     assert_close(a[1].cpu().numpy(), ref, "repeat")
+
+
+@pytest.mark.parametrize("W", [64, 640])
+def test_empty_sequence_single_and_multi_split(W):
+    """An empty sequence outputs zeros both when the plan has one split per
+    (b, h) (W=64: the decode kernel finishes each (b, h) itself) and when a
+    merge kernel runs (W=640)."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, D = 3, 2, 128
+    g = torch.Generator().manual_seed(W)
+    lens = [0, 5, W + 3]
+    k = torch.randn((B, H, max(lens), D), generator=g).to(torch.bfloat16)
+    cache = swa.KVCache("bf16", B, H, D, W)
+    for b, n in enumerate(lens):
+        if n:
+            swa.kv_append(cache.seq_view(b), k[b:b + 1, :, :n].contiguous().cuda(), k[b:b + 1, :, :n].contiguous().cuda())
+    q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+    out = swa.decode_attn(cache, q.cuda()).cpu().numpy()
+    assert not out[0].any()
+    k64, q64 = f64(k), f64(q)
+    for b in (1, 2):
+        assert_close(out[b], oracle_out(k64[b], k64[b], q64[b], lens[b], W), f"W={W} b={b}")
