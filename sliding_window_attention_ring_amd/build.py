@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libswa.so")
+EXAMPLE = os.path.join(PKG, "swa_example")
 SOURCES = ["swa_capi.hip", "swa_append.hip", "swa_decode.hip", "swa_decode_int8.hip", "swa_reuse.hip"]
 ARCH = "gfx950"
 
@@ -37,6 +38,23 @@ def command(out: str = LIB, defines=()) -> list:
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]
+
+
+def build_example(verbose: bool = True) -> str:
+    """Compile csrc/swa_example.c, a plain C program that uses libswa.so
+    through include/swa.h only."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+           os.path.join(CSRC, "swa_example.c"), "-o", EXAMPLE,
+           "-L", PKG, "-lswa", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"building the C example failed:\n{res.stderr}")
+    return EXAMPLE
 
 
 def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
@@ -68,3 +86,5 @@ if __name__ == "__main__":
     ap.add_argument("-D", dest="defines", action="append", default=[])
     a = ap.parse_args()
     build(out=a.out, defines=a.defines)
+    if a.out == LIB:
+        build_example()

@@ -1,0 +1,91 @@
+"""Seeded fuzz of mixed operations against per-sequence oracle histories:
+appends of random sizes (whole batch or one sequence through a view),
+truncations (exact or fallback) and decodes, on bf16 and INT8 caches of
+both layouts.  After every operation the ring state is compared
+bit-exactly and every decode output with the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import reuse
+from tests.gpu_util import (assert_close, check_int8_decode, check_int8_store, check_ring_rows, f64, host_bits,
+                            oracle_out, require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("kind,layout,W,seed", [("bf16", "ring", 48, 1), ("bf16", "paged", 64, 2),
+                                                ("int8", "ring", 64, 3), ("int8", "paged", 48, 4)])
+def test_mixed_operation_fuzz(kind, layout, W, seed):
+    import sliding_window_attention_ring_amd as swa
+    rng = np.random.default_rng(seed)
+    g = torch.Generator().manual_seed(seed)
+    B, H, D = 3, 2, 128
+    cache = swa.KVCache(kind, B, H, D, W, layout=layout)
+    hist_k = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
+    hist_v = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
+    for op in range(40):
+        r = rng.random()
+        if r < 0.45:  # whole-batch append
+            T = int(rng.choice([1, 1, 1, 2, 15, 16, 17, W - 1, W + 5, 2 * W + 3]))
+            k = torch.randn((B, H, T, D), generator=g).to(torch.bfloat16)
+            v = torch.randn((B, H, T, D), generator=g).to(torch.bfloat16)
+            swa.kv_append(cache, k.cuda(), v.cuda())
+            for b in range(B):
+                hist_k[b] = torch.cat([hist_k[b], k[b]], dim=1)
+                hist_v[b] = torch.cat([hist_v[b], v[b]], dim=1)
+        elif r < 0.7:  # one sequence through a view
+            b = int(rng.integers(B))
+            T = int(rng.integers(1, 2 * W))
+            k = torch.randn((1, H, T, D), generator=g).to(torch.bfloat16)
+            v = torch.randn((1, H, T, D), generator=g).to(torch.bfloat16)
+            swa.kv_append(cache.seq_view(b), k.cuda(), v.cuda())
+            hist_k[b] = torch.cat([hist_k[b], k[0]], dim=1)
+            hist_v[b] = torch.cat([hist_v[b], v[0]], dim=1)
+        elif r < 0.8:  # truncation
+            ns = [h.shape[1] for h in hist_k]
+            cuts = [int(rng.integers(0, n + 1)) for n in ns]
+            ok = swa.kv_truncate(cache, torch.tensor(cuts, dtype=torch.int32, device="cuda")).cpu().numpy()
+            for b in range(B):
+                assert bool(ok[b]) == reuse.truncation_exact(ns[b], cuts[b], W, int8=(kind == "int8"))
+                if ok[b]:
+                    hist_k[b] = hist_k[b][:, :cuts[b]]
+                    hist_v[b] = hist_v[b][:, :cuts[b]]
+        # state check after every operation
+        assert swa.validate(cache) == 0, f"op {op}"
+        ns = [h.shape[1] for h in hist_k]
+        if kind == "int8":
+            for b in range(B):
+                for h in range(H):
+                    check_int8_store(cache, b, h, f64(hist_k[b][h]), f64(hist_v[b][h]), ns[b])
+        else:
+            N = max(max(ns), 1)
+            kb = np.zeros((B, H, N, D), dtype=np.uint16)
+            vb = np.zeros_like(kb)
+            for b in range(B):
+                kb[b, :, :ns[b]] = host_bits(hist_k[b])
+                vb[b, :, :ns[b]] = host_bits(hist_v[b])
+            check_ring_rows(cache, kb, vb, np.array(ns))
+        if rng.random() < 0.6:  # decode
+            q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+            q64 = f64(q)
+            if kind == "int8":
+                out, cmax, c_all = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
+                out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
+                for b in range(B):
+                    for h in range(H):
+                        check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, q64[b, h], f64(hist_k[b][h]),
+                                          f64(hist_v[b][h]), ns[b], W, what=f"op {op}")
+            else:
+                out = swa.decode_attn(cache, q.cuda()).cpu().numpy()
+                for b in range(B):
+                    if ns[b] == 0:
+                        assert not out[b].any()
+                    else:
+                        assert_close(out[b], oracle_out(f64(hist_k[b]), f64(hist_v[b]), q64[b], ns[b], W), f"op {op}")
