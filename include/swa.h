@@ -38,7 +38,7 @@ extern "C" {
 enum {
   SWA_OK = 0,
   SWA_EINVAL = -1,       /* B, H, W < 1, T < 0, W*D*elem >= 2^32, unknown layout, or W not a
-                            multiple of 16 for INT8 or PAGED */
+                            multiple of 16 for INT8 kinds or PAGED */
   SWA_ENULL = -2,        /* a required pointer is NULL */
   SWA_EALIGN = -3,       /* a K/V/q/out/staging/workspace pointer is not 16-byte aligned */
   SWA_EUNSUPPORTED = -4, /* head_dim or kind not supported by this entry point */
@@ -49,7 +49,8 @@ enum {
 enum {
   SWA_KV_BF16 = 0, /* K/V rows bf16; q and new rows bf16 */
   SWA_KV_FP32 = 1, /* K/V rows fp32; q and new rows fp32 */
-  SWA_KV_INT8 = 2  /* K/V INT8 codes per 16-token block + fp16 band witness; q, new rows bf16 */
+  SWA_KV_INT8 = 2, /* K/V INT8 codes per 16-token block + fp16 band witness; q, new rows bf16 */
+  SWA_KV_INT8_DITHER = 3 /* K/V INT8 codes with subtractive dither, no witness; q, new rows bf16 */
 };
 
 /* Physical layout of the rows (the logical cache is the same either way:
@@ -61,20 +62,26 @@ enum {
 enum { SWA_LAYOUT_RING = 0, SWA_LAYOUT_PAGED = 1 };
 
 /* Cache descriptor.  Supported head_dim D: BF16 {64, 128, 256}; FP32
- * {16, 32, 64, 128}; INT8 {128} (16 bands of 8 dims).
+ * {16, 32, 64, 128}; INT8 and INT8_DITHER {128} (16 bands of 8 dims).
  *
  *  RING layout                   PAGED layout (P = num_pages)
  *  k, v       [B][H][W][D]       [P][H][16][D]    bf16 | fp32 | int8 codes
- *  INT8 only:
+ *  INT8 and INT8_DITHER:
  *  k_scale,   [B][H][W/16] fp32  [P][H] fp32      absmax/127 of the block
  *  v_scale
+ *  INT8 only (ignored by INT8_DITHER, may be NULL there):
  *  witness    [B][H][W][D/8]     [P][H][16][D/8]  fp16 bits: band norms of the
  *                                                 key residual, rounded up
+ *  INT8_DITHER only (ignored otherwise):
+ *  request_id [B] uint64 (device) request id of each sequence, the first
+ *                                member of the dither's five-tuple key
+ *  layer      uint32             layer id of this cache, another member
  *  Both layouts:
  *  pos            [B][W]  int32  absolute position held by each slot, -1 if
- *                                none (INT8: position of the committed code row)
+ *                                none (INT8 kinds: position of the committed
+ *                                code row)
  *  next_position  [B]     int32  position the next appended token receives
- *  k_stage,v_stage [B][H][16][D] bf16 (INT8) rows of the incomplete newest
+ *  k_stage,v_stage [B][H][16][D] bf16 (INT8 kinds) rows of the incomplete newest
  *                                block, row index = position mod 16
  *  block_table    [B][W/16] int32 (PAGED) page of each 16-slot ring block;
  *                                entries for blocks the sequence uses must be
@@ -92,10 +99,12 @@ typedef struct swa_cache {
   void *k_stage, *v_stage;
   int32_t *block_table; /* PAGED only */
   int64_t num_pages;    /* PAGED only */
+  uint64_t *request_id; /* INT8_DITHER only */
+  uint32_t layer;       /* INT8_DITHER only */
 } swa_cache;
 
 /* Empty the cache: next_position[b] = 0 and pos[b][*] = -1 for every b (a
- * RING INT8 cache also clears its block scales; PAGED pools, which other
+ * RING cache of an INT8 kind also clears its block scales; PAGED pools, which other
  * caches may share, are not touched).  Row contents are left as they are; no
  * slot is visible until written.  Errors: SWA_EINVAL, SWA_ENULL, SWA_EHIP. */
 int swa_cache_reset(const swa_cache *c, void *stream);
@@ -104,7 +113,7 @@ int swa_cache_reset(const swa_cache *c, void *stream);
  * framerc.cn §2.2 and §3.3-§3.4: write, evict the oldest when over W;
  * airsota.com §三 step 1 (write at the current position); huhohoo.com
  * (next_position advances with the rows).
- *  k_new, v_new  [B][H][T][D] in the cache's input dtype (INT8 kind: bf16).
+ *  k_new, v_new  [B][H][T][D] in the cache's input dtype (INT8 kinds: bf16).
  * Token j of sequence b gets position p = next_position[b] + j and slot
  * p mod W; pos[b][slot] = p; afterwards next_position[b] += T.  Only the last
  * min(T, W) tokens are stored (the others would be overwritten).
@@ -113,7 +122,17 @@ int swa_cache_reset(const swa_cache *c, void *stream);
  * goes to the staging rows; when the block of positions [16m, 16m+16) is
  * complete it is quantized into slots (16m mod W).. with one fp32 absmax/127
  * scale per block and tensor, codes rint(x/s) clamped to +-127, and the key
- * residual's 16 band norms written rounded up to fp16.  T = 0 is a no-op. */
+ * residual's 16 band norms written rounded up to fp16.
+ * INT8_DITHER kind (WitCert, section 频带酉性与双层证书, Tier B: a uniform
+ * pseudo-random dither is added before rounding at write time and subtracted
+ * at read time; section SGLang 生产级落地: Philox keyed by request, layer,
+ * KV head, token and channel): the same blocks and scales, and
+ * code = rint(f32(x/s) + u) with u = (m + 1/2)/256 - 1/2, where m is byte
+ * c mod 16 of Philox-4x32-10 (Salmon et al., SC 2011) with key
+ * (request_id mod 2^32, request_id div 2^32) and counter (position, c / 16,
+ * head, layer); the words are taken in order, each little-endian.  Keys and
+ * values of one token share u.  request_id must be set.  No witness is
+ * written.  T = 0 is a no-op. */
 int kv_append(const swa_cache *c, const void *k_new, const void *v_new, int32_t T, void *stream);
 
 /* Decode attention for one query per sequence over the last min(W, n) tokens,
@@ -161,6 +180,36 @@ int decode_attn_int8_witness_tv(const swa_cache *c, const void *q, float *out, f
                                 int32_t *gate, float tau, float *c_all, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Tier B decode (WitCert, section 频带酉性与双层证书: with dithered INT8 the
+ * residual is uniform and independent of the data, so a sub-Gaussian
+ * concentration bound with a failure budget replaces the stored witness).
+ * INT8_DITHER kind.  Committed tokens are read as s * (code - u), with u
+ * regenerated from the same Philox stream; the newest n mod 16 tokens are
+ * exact.  For every visible quantized token j the logit error e_j =
+ * q.(k^_j - k_j)/sqrt(D) is, over the dither, a sum of independent terms: per
+ * channel the residual is uniform on a 256-point grid (variance proxy 1/12,
+ * mean within beta = 2^-9 + 2^-16 of zero in code units).  A union bound over
+ * the n_q visible quantized tokens gives, with probability >= 1 - delta,
+ *   max_j |e_j| <= cert = (S/sqrt(D)) (||q||_2 sqrt(ln(2 n_q/delta)/6)
+ *                                      + ||q||_1 beta),
+ * S the largest key scale among those tokens (cert = 0 when n_q = 0).
+ *  q      [B][H][D] bf16
+ *  out    [B][H][D] fp32
+ *  cert   [B][H]    fp32: the bound above, times (1 + 2^-12) for float32
+ *                   rounding
+ *  tv     NULL, or [B][H] fp32: tanh(cert/2), the TV bound on the attention
+ *         weights that holds together with cert
+ *  gate   NULL, or [B][H] int32: 1 where tv > tau (needs tv)
+ *  delta  failure budget of one (sequence, head) query, in (0, 1]; a
+ *         request's budget is split over its steps, layers and heads by the
+ *         caller (union bound)
+ *  ws, ws_bytes: as for decode_attn.
+ * Errors: descriptor errors, SWA_EUNSUPPORTED for another kind, SWA_ENULL,
+ * SWA_EALIGN, SWA_EINVAL for delta outside (0, 1] or a NaN tau,
+ * SWA_EWORKSPACE, SWA_EHIP. */
+int decode_attn_int8_dither(const swa_cache *c, const void *q, float *out, float *cert, float *tv,
+                            int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes the decode entry points need for this cache shape (the
  * split partials: B*H*nsplit*(D+4) floats).  0 for an invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);
@@ -173,7 +222,7 @@ int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * 為什麼滑窗部分命中必須回退): truncate sequence b to its first cut[b] tokens,
  * so the next appended token gets position cut[b] -- when that is exact.
  * It is exact iff every row of the shorter history's window is still
- * stored: 0 <= cut <= n and (n <= W, or cut == n, or cut == 0); an INT8 cache
+ * stored: 0 <= cut <= n and (n <= W, or cut == n, or cut == 0); an INT8 (either kind) cache
  * also needs cut % 16 == 0 or cut >= 16*(n/16) (committed blocks keep only
  * codes).  Exact: slots holding positions >= cut become empty (pos = -1)
  * and next_position[b] = cut.  Otherwise sequence b is left unchanged and the
@@ -186,7 +235,7 @@ int kv_truncate(const swa_cache *c, const int32_t *cut, int32_t *ok, void *strea
 /* Debug check of the position invariant (framerc.cn §3.2 PositionInvariant,
  * §6.3 the invariant as a runtime assertion): adds to *violations (device
  * int32, caller zeroes it) the number of slots whose pos differs from the
- * newest position p < n (INT8: p < 16*(n/16)) with p mod W == slot, or -1;
+ * newest position p < n (INT8 kinds: p < 16*(n/16)) with p mod W == slot, or -1;
  * PAGED: also each live slot whose block_table entry is outside [0, P). */
 int swa_validate(const swa_cache *c, int32_t *violations, void *stream);
 

@@ -11,12 +11,12 @@ LIB_PATH = os.environ.get("SWA_LIB") or os.path.join(os.path.dirname(os.path.abs
 SWA_OK = 0
 STATUS = {0: "SWA_OK", -1: "SWA_EINVAL", -2: "SWA_ENULL", -3: "SWA_EALIGN", -4: "SWA_EUNSUPPORTED",
           -5: "SWA_EWORKSPACE", -6: "SWA_EHIP"}
-KIND = {"bf16": 0, "fp32": 1, "int8": 2}
+KIND = {"bf16": 0, "fp32": 1, "int8": 2, "int8_dither": 3}
 LAYOUT = {"ring": 0, "paged": 1}
 
 # Every symbol include/swa.h declares.
 EXPORTS = ("swa_cache_reset", "kv_append", "decode_attn", "decode_attn_int8_witness",
-           "decode_attn_int8_witness_tv", "kv_truncate",
+           "decode_attn_int8_witness_tv", "decode_attn_int8_dither", "kv_truncate",
            "swa_workspace_bytes", "swa_workspace_init", "swa_validate", "swa_status_string")
 
 
@@ -32,6 +32,7 @@ class SwaCacheDesc(ctypes.Structure):
         ("witness", ctypes.c_void_p),
         ("k_stage", ctypes.c_void_p), ("v_stage", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("num_pages", ctypes.c_int64),
+        ("request_id", ctypes.c_void_p), ("layer", ctypes.c_uint32),
     ]
 
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "decode_attn_int8_witness": (ctypes.c_int, [P, VP, VP, VP, VP, VP, SZ, VP]),
             "decode_attn_int8_witness_tv": (ctypes.c_int, [P, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP, SZ,
                                                            VP]),
+            "decode_attn_int8_dither": (ctypes.c_int, [P, VP, VP, VP, VP, VP, ctypes.c_float, ctypes.c_float, VP,
+                                                       SZ, VP]),
             "kv_truncate": (ctypes.c_int, [P, VP, VP, VP]),
             "swa_workspace_bytes": (SZ, [P]),
             "swa_workspace_init": (ctypes.c_int, [VP, SZ, VP]),

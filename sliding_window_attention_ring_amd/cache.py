@@ -16,8 +16,9 @@ import torch
 from . import _capi
 from ._capi import KIND, LAYOUT, SwaCacheDesc, check, lib
 
-_INPUT_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.bfloat16}
-_STORE_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.int8}
+_INPUT_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.bfloat16,
+                "int8_dither": torch.bfloat16}
+_STORE_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "int8": torch.int8, "int8_dither": torch.int8}
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -43,7 +44,10 @@ def _need(t: torch.Tensor, shape, dtype, name: str) -> None:
 class KVCache:
     """Device tensors of one sliding-window cache and its descriptor.
 
-    kind: "bf16" | "fp32" | "int8"; B sequences, H heads, head_dim D, window W.
+    kind: "bf16" | "fp32" | "int8" | "int8_dither"; B sequences, H heads,
+    head_dim D, window W.  "int8_dither" is INT8 with subtractive dither and
+    no witness; its ``request_id`` [B] (int64 bits of the uint64 ids,
+    default 0..B-1) and ``layer`` key the dither stream.
     layout "ring": ``k``, ``v`` are [B, H, W, D] (INT8: ``k_scale``/``v_scale``
     [B, H, W/16], ``witness`` [B, H, W, D/8] fp16).  layout "paged": they are
     pools of ``num_pages`` 16-token pages ([P, H, 16, D], [P, H], [P, H, 16,
@@ -54,7 +58,8 @@ class KVCache:
     """
 
     def __init__(self, kind: str, B: int, H: int, D: int, W: int, device="cuda", layout: str = "ring",
-                 num_pages: Optional[int] = None, block_table: Optional[torch.Tensor] = None):
+                 num_pages: Optional[int] = None, block_table: Optional[torch.Tensor] = None,
+                 request_id: Optional[torch.Tensor] = None, layer: int = 0):
         if kind not in KIND:
             raise ValueError(f"kind must be one of {sorted(KIND)}")
         if layout not in LAYOUT:
@@ -75,13 +80,21 @@ class KVCache:
         self.pos = torch.empty((B, W), dtype=torch.int32, device=dev)
         self.next_position = torch.empty((B,), dtype=torch.int32, device=dev)
         self.k_scale = self.v_scale = self.witness = self.k_stage = self.v_stage = None
-        if kind == "int8":
+        if kind in ("int8", "int8_dither"):
             scales = (self.num_pages, H) if paged else (B, H, W // 16)
             self.k_scale = torch.empty(scales, dtype=torch.float32, device=dev)
             self.v_scale = torch.empty_like(self.k_scale)
-            self.witness = torch.empty(rows + (D // 8,), dtype=torch.float16, device=dev)
+            if kind == "int8":
+                self.witness = torch.empty(rows + (D // 8,), dtype=torch.float16, device=dev)
             self.k_stage = torch.empty((B, H, 16, D), dtype=torch.bfloat16, device=dev)
             self.v_stage = torch.empty_like(self.k_stage)
+        self.request_id, self.layer = None, int(layer)
+        if kind == "int8_dither":
+            if request_id is None:
+                request_id = torch.arange(B, dtype=torch.int64)
+            if tuple(request_id.shape) != (B,) or request_id.dtype != torch.int64:
+                raise ValueError("request_id must be an int64 tensor of shape [B] (the uint64 bits)")
+            self.request_id = request_id.to(dev).contiguous()
         self.block_table = None
         if paged:
             if block_table is None:
@@ -111,7 +124,8 @@ class KVCache:
                             LAYOUT[self.layout], pool(self.k), pool(self.v), per_seq(self.pos),
                             per_seq(self.next_position), pool(self.k_scale), pool(self.v_scale),
                             pool(self.witness), per_seq(self.k_stage), per_seq(self.v_stage),
-                            per_seq(self.block_table), self.num_pages)
+                            per_seq(self.block_table), self.num_pages, per_seq(self.request_id),
+                            self.layer & 0xFFFFFFFF)
 
     def seq_view(self, b: int) -> "SeqView":
         """Descriptor of sequence ``b`` alone (B = 1), for ragged appends."""
@@ -229,6 +243,34 @@ def decode_attn_int8_witness_tv(cache, q: torch.Tensor, tau: float = 0.2, out: O
                                             ws.numel() * ws.element_size(), _stream(stream)),
           "decode_attn_int8_witness_tv")
     return out, cmax, tv, gate, c_all
+
+
+def decode_attn_int8_dither(cache, q: torch.Tensor, delta: float, tau: float = 0.2,
+                            out: Optional[torch.Tensor] = None, cert: Optional[torch.Tensor] = None,
+                            tv: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                            want_tv: bool = True, ws: Optional[torch.Tensor] = None, stream=None):
+    """``decode_attn_int8_dither``: returns (out [B,H,D], cert [B,H], tv, gate) -- tv and gate
+    are None when ``want_tv`` is false.  ``delta`` is the failure budget of one (sequence, head)."""
+    _need(q, (cache.B, cache.H, cache.D), torch.bfloat16, "q")
+    dev = q.device
+    BH = (cache.B, cache.H)
+    out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=dev) if out is None else out
+    cert = torch.empty(BH, dtype=torch.float32, device=dev) if cert is None else cert
+    if want_tv:
+        tv = torch.empty(BH, dtype=torch.float32, device=dev) if tv is None else tv
+        gate = torch.empty(BH, dtype=torch.int32, device=dev) if gate is None else gate
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    _need(cert, BH, torch.float32, "cert")
+    if tv is not None:
+        _need(tv, BH, torch.float32, "tv")
+    if gate is not None:
+        _need(gate, BH, torch.int32, "gate")
+    ws = cache.workspace() if ws is None else ws
+    check(lib().decode_attn_int8_dither(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(cert), _ptr(tv),
+                                        _ptr(gate), float(tau), float(delta), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)),
+          "decode_attn_int8_dither")
+    return out, cert, tv, gate
 
 
 def kv_truncate(cache, cut: torch.Tensor, stream=None) -> torch.Tensor:

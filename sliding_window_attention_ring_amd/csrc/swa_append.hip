@@ -68,6 +68,20 @@ constexpr int kD8 = 128;
 // Chunks up to this many tokens take the single-launch path.
 constexpr int kSmallT = 16;
 
+// Tier B subtractive dither (page "WitCert", section 频带酉性与双层证书,
+// second tier; section SGLang 生产级落地 for the Philox five-tuple).  req ==
+// nullptr selects Tier A (plain rounding plus the witness).  Otherwise the
+// element of channel c of the token at position p in head h gets
+// u = (m + 1/2)/256 - 1/2, m = byte c mod 16 of Philox-4x32-10 with key
+// (req[b] low word, high word) and counter (p, c / 16, h, layer), words in
+// order, least significant byte first; code = rint(f32(x / s) + u).  Since
+// |u| <= 1/2 - 2^-9 the sum stays inside +-127.5 and the clamp never acts.
+// Keys and values use the same u, and no witness is written.
+struct Dither {
+  const uint64_t* req;
+  uint32_t layer;
+};
+
 // One wave quantizes one 16-token block (index kb) of one tensor of one
 // (b, h).  Lane l handles token l/4 of the block and dims [32*(l%4), +32).
 // Rows come from the staging area for positions below n0 (the old
@@ -77,7 +91,8 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
                                                   const uint16_t* __restrict__ src_stage, int64_t n0, int T,
                                                   int64_t kb, int b, int h, const RowMap& map,
                                                   int8_t* __restrict__ codes, float* __restrict__ scale,
-                                                  uint16_t* __restrict__ witness, int32_t* __restrict__ pos_b) {
+                                                  uint16_t* __restrict__ witness, int32_t* __restrict__ pos_b,
+                                                  Dither dz) {
   const int W = map.W;
   const int64_t bh = (int64_t)b * map.H + h;
   const int r = lane >> 2;        // token within the block
@@ -100,12 +115,27 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
   amax = group_max<64>(amax);
   const float s = __fdiv_rn(amax, 127.0f);
 
+  // Dither bytes of this lane's 32 channels: Philox blocks 2*part and 2*part+1.
+  const bool dith = dz.req != nullptr;
+  uint32_t dw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (dith) {
+    const uint64_t rid = dz.req[b];
+    const uint32_t k0 = (uint32_t)rid, k1 = (uint32_t)(rid >> 32);
+    const uint4 d0 = philox4x32_10(make_uint4((uint32_t)p, 2u * part, (uint32_t)h, dz.layer), k0, k1);
+    const uint4 d1 = philox4x32_10(make_uint4((uint32_t)p, 2u * part + 1u, (uint32_t)h, dz.layer), k0, k1);
+    dw[0] = d0.x; dw[1] = d0.y; dw[2] = d0.z; dw[3] = d0.w;
+    dw[4] = d1.x; dw[5] = d1.y; dw[6] = d1.z; dw[7] = d1.w;
+  }
   int8_t cq[32];
   float cf[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
     float c = 0.f;
-    if (s > 0.f) c = fminf(fmaxf(rintf(__fdiv_rn(x[e], s)), -127.f), 127.f);
+    if (s > 0.f) {
+      float y = __fdiv_rn(x[e], s);
+      if (dith) y = y + fmaf(u8f(dw[e >> 2], e & 3), 1.0f / 256.0f, -255.0f / 512.0f);  // u is exact
+      c = fminf(fmaxf(rintf(y), -127.f), 127.f);
+    }
     cf[e] = c;
     cq[e] = (int8_t)(int)c;
   }
@@ -122,7 +152,8 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
   reinterpret_cast<uint4*>(dst)[0] = packed[0];
   reinterpret_cast<uint4*>(dst)[1] = packed[1];
   if (lane == 0) scale[map.block(b, h, slot)] = s;
-  if (key) {
+  if (key && pos_b != nullptr && part == 0) pos_b[slot] = (int32_t)p;
+  if (key && !dith) {
     uint16_t wb[4];
 #pragma unroll
     for (int band = 0; band < 4; ++band) {
@@ -139,7 +170,6 @@ __device__ __forceinline__ void commit_block_wave(int lane, bool key, const uint
     o.x = (uint32_t)wb[0] | ((uint32_t)wb[1] << 16);
     o.y = (uint32_t)wb[2] | ((uint32_t)wb[3] << 16);
     reinterpret_cast<uint2*>(witness + row_idx * (kD8 / 8))[part] = o;
-    if (pos_b != nullptr && part == 0) pos_b[slot] = (int32_t)p;
   }
 }
 
@@ -150,7 +180,7 @@ __global__ __launch_bounds__(128) void append_int8_blocks_kernel(
     const uint16_t* __restrict__ k_stage, const uint16_t* __restrict__ v_stage,
     int8_t* __restrict__ Kc, int8_t* __restrict__ Vc, float* __restrict__ k_scale,
     float* __restrict__ v_scale, uint16_t* __restrict__ witness, int32_t* __restrict__ pos,
-    const int32_t* __restrict__ np, RowMap map, int H, int W, int T) {
+    const int32_t* __restrict__ np, RowMap map, int H, int W, int T, Dither dz) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int64_t n0 = np[b];
   if (n0 < 0) return;  // precondition violated: write nothing (swa_validate reports it)
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(128) void append_int8_blocks_kernel(
   const bool key = (threadIdx.x >> 6) == 0;
   commit_block_wave(threadIdx.x & 63, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, b, h, map,
                     key ? Kc : Vc, key ? k_scale : v_scale, witness,
-                    h == 0 ? pos + (int64_t)b * W : nullptr);
+                    h == 0 ? pos + (int64_t)b * W : nullptr, dz);
 }
 
 // Decode-sized INT8 append (T <= 16) in one launch: one work-group of 16
@@ -176,7 +206,7 @@ __global__ __launch_bounds__(1024) void append_int8_small_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_stage,
     uint16_t* __restrict__ v_stage, int8_t* __restrict__ Kc, int8_t* __restrict__ Vc,
     float* __restrict__ k_scale, float* __restrict__ v_scale, uint16_t* __restrict__ witness,
-    int32_t* __restrict__ pos, int32_t* __restrict__ np, RowMap map, int H, int W, int T) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ np, RowMap map, int H, int W, int T, Dither dz) {
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t n0 = np[b];
@@ -191,7 +221,7 @@ __global__ __launch_bounds__(1024) void append_int8_small_kernel(
       const bool key = (task & 1) == 0;
       commit_block_wave(lane, key, key ? k_new : v_new, key ? k_stage : v_stage, n0, T, kb, b, h, map,
                         key ? Kc : Vc, key ? k_scale : v_scale, witness,
-                        h == 0 ? pos + (int64_t)b * W : nullptr);
+                        h == 0 ? pos + (int64_t)b * W : nullptr, dz);
     }
   }
   __syncthreads();
@@ -298,12 +328,13 @@ hipError_t launch_append_rows(const swa_cache& c, const void* k_new, const void*
 
 hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void* v_new, int T,
                               hipStream_t s, bool* advanced) {
+  const Dither dz{c.kind == SWA_KV_INT8_DITHER ? c.request_id : nullptr, c.layer};
   if (T <= kSmallT) {
     hipLaunchKernelGGL(append_int8_small_kernel, dim3(c.B), dim3(1024), 0, s,
                        reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new),
                        reinterpret_cast<uint16_t*>(c.k_stage), reinterpret_cast<uint16_t*>(c.v_stage),
                        reinterpret_cast<int8_t*>(c.k), reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale,
-                       c.witness, c.pos, c.next_position, row_map(c), c.H, c.W, T);
+                       c.witness, c.pos, c.next_position, row_map(c), c.H, c.W, T, dz);
     *advanced = true;
     return hipGetLastError();
   }
@@ -316,7 +347,7 @@ hipError_t launch_append_int8(const swa_cache& c, const void* k_new, const void*
                      reinterpret_cast<const uint16_t*>(c.k_stage),
                      reinterpret_cast<const uint16_t*>(c.v_stage), reinterpret_cast<int8_t*>(c.k),
                      reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale, c.witness, c.pos,
-                     c.next_position, row_map(c), c.H, c.W, T);
+                     c.next_position, row_map(c), c.H, c.W, T, dz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int vpr = c.D * 2 / 16;

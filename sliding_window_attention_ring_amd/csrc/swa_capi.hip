@@ -15,11 +15,14 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool is_int8(int kind) { return kind == SWA_KV_INT8 || kind == SWA_KV_INT8_DITHER; }
+
 bool head_dim_supported(int kind, int D) {
   switch (kind) {
     case SWA_KV_BF16: return D == 64 || D == 128 || D == 256;
     case SWA_KV_FP32: return D == 16 || D == 32 || D == 64 || D == 128;
-    case SWA_KV_INT8: return D == 128;
+    case SWA_KV_INT8:
+    case SWA_KV_INT8_DITHER: return D == 128;
   }
   return false;
 }
@@ -27,12 +30,12 @@ bool head_dim_supported(int kind, int D) {
 // Descriptor checks common to every entry point.
 int check_cache(const swa_cache* c) {
   if (c == nullptr) return SWA_ENULL;
-  if (c->kind != SWA_KV_BF16 && c->kind != SWA_KV_FP32 && c->kind != SWA_KV_INT8) return SWA_EUNSUPPORTED;
+  if (c->kind != SWA_KV_BF16 && c->kind != SWA_KV_FP32 && !is_int8(c->kind)) return SWA_EUNSUPPORTED;
   if (c->B < 1 || c->H < 1 || c->W < 1) return SWA_EINVAL;
   if (c->layout != SWA_LAYOUT_RING && c->layout != SWA_LAYOUT_PAGED) return SWA_EINVAL;
   if (c->B > 65535 || c->H > 65535) return SWA_EINVAL;  // grid y/z limits
   if (!head_dim_supported(c->kind, c->D)) return SWA_EUNSUPPORTED;
-  if (c->kind == SWA_KV_INT8 && c->W % 16 != 0) return SWA_EINVAL;
+  if (is_int8(c->kind) && c->W % 16 != 0) return SWA_EINVAL;
   // The decode kernels address one (b, h) region with 32-bit byte offsets.
   const int64_t esz = c->kind == SWA_KV_FP32 ? 4 : c->kind == SWA_KV_BF16 ? 2 : 1;
   if ((int64_t)c->W * c->D * esz >= ((int64_t)1 << 32)) return SWA_EINVAL;
@@ -45,10 +48,18 @@ int check_cache(const swa_cache* c) {
     if (c->block_table == nullptr) return SWA_ENULL;
     if ((uintptr_t)c->block_table & 3u) return SWA_EALIGN;
   }
-  if (c->kind == SWA_KV_INT8) {
-    if (!c->k_scale || !c->v_scale || !c->witness || !c->k_stage || !c->v_stage) return SWA_ENULL;
-    if (!aligned16(c->k_stage) || !aligned16(c->v_stage) || !aligned16(c->witness)) return SWA_EALIGN;
+  if (is_int8(c->kind)) {
+    if (!c->k_scale || !c->v_scale || !c->k_stage || !c->v_stage) return SWA_ENULL;
+    if (!aligned16(c->k_stage) || !aligned16(c->v_stage)) return SWA_EALIGN;
     if (((uintptr_t)c->k_scale & 3u) || ((uintptr_t)c->v_scale & 3u)) return SWA_EALIGN;
+  }
+  if (c->kind == SWA_KV_INT8) {
+    if (!c->witness) return SWA_ENULL;
+    if (!aligned16(c->witness)) return SWA_EALIGN;
+  }
+  if (c->kind == SWA_KV_INT8_DITHER) {
+    if (!c->request_id) return SWA_ENULL;
+    if ((uintptr_t)c->request_id & 7u) return SWA_EALIGN;
   }
   return SWA_OK;
 }
@@ -130,7 +141,7 @@ unsigned grid_for(int64_t n, int threads, int64_t cap) {
 SplitPlan plan_decode(const swa_cache& c) {
   SplitPlan p;
   const int64_t tgt = target_wgs();
-  if (c.kind == SWA_KV_INT8) {
+  if (is_int8(c.kind)) {
     const int64_t rb = decode_int8_round_blocks();
     const int64_t wb = c.W / 16;
     int64_t cb = round_up(((int64_t)c.B * c.H * wb + tgt - 1) / tgt, rb);
@@ -152,7 +163,7 @@ hipError_t launch_reset(const swa_cache& c, hipStream_t s) {
   const int64_t n = (int64_t)c.B * c.W > (int64_t)c.B * c.H * (c.W / 16) ? (int64_t)c.B * c.W
                                                                           : (int64_t)c.B * c.H * (c.W / 16);
   // Pools of a paged cache may be shared with other caches: leave them alone.
-  const int clear_scales = c.kind == SWA_KV_INT8 && c.layout == SWA_LAYOUT_RING ? 1 : 0;
+  const int clear_scales = is_int8(c.kind) && c.layout == SWA_LAYOUT_RING ? 1 : 0;
   hipLaunchKernelGGL(reset_kernel, dim3(grid_for(n > c.B ? n : c.B, 256, 1 << 16)), dim3(256), 0, s, c.pos,
                      c.next_position, c.k_scale, c.v_scale, c.B, c.H, c.W, clear_scales);
   return hipGetLastError();
@@ -168,7 +179,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 hipError_t launch_validate(const swa_cache& c, int32_t* violations, hipStream_t s) {
   hipLaunchKernelGGL(validate_kernel, dim3(grid_for((int64_t)c.B * c.W, 256, 1 << 16)), dim3(256), 0, s,
                      c.pos, c.next_position, c.layout == SWA_LAYOUT_PAGED ? c.block_table : nullptr,
-                     c.num_pages, violations, c.B, c.W, c.kind == SWA_KV_INT8 ? 1 : 0);
+                     c.num_pages, violations, c.B, c.W, is_int8(c.kind) ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -219,8 +230,8 @@ int kv_append(const swa_cache* c, const void* k_new, const void* v_new, int32_t 
   if (!aligned16(k_new) || !aligned16(v_new)) return SWA_EALIGN;
   const hipStream_t s = (hipStream_t)stream;
   bool advanced = false;
-  hipError_t e = c->kind == SWA_KV_INT8 ? launch_append_int8(*c, k_new, v_new, T, s, &advanced)
-                                        : launch_append_rows(*c, k_new, v_new, T, s, &advanced);
+  hipError_t e = is_int8(c->kind) ? launch_append_int8(*c, k_new, v_new, T, s, &advanced)
+                                   : launch_append_rows(*c, k_new, v_new, T, s, &advanced);
   if (e == hipSuccess && !advanced) e = launch_advance(*c, T, s);
   return e == hipSuccess ? SWA_OK : SWA_EHIP;
 }
@@ -228,7 +239,7 @@ int kv_append(const swa_cache* c, const void* k_new, const void* v_new, int32_t 
 int decode_attn(const swa_cache* c, const void* q, float* out, void* ws, size_t ws_bytes, void* stream) {
   int st = check_cache(c);
   if (st != SWA_OK) return st;
-  if (c->kind == SWA_KV_INT8) return SWA_EUNSUPPORTED;
+  if (is_int8(c->kind)) return SWA_EUNSUPPORTED;
   if (q == nullptr || out == nullptr || ws == nullptr) return SWA_ENULL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return SWA_EALIGN;
   if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
@@ -249,7 +260,26 @@ int decode_attn_int8_witness_tv(const swa_cache* c, const void* q, float* out, f
   if (!(tau == tau)) return SWA_EINVAL;  // NaN threshold
   if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
   const SplitPlan p = plan_decode(*c);
-  return launch_decode_int8(*c, q, out, cmax, c_all, tv, gate, tau, ws, p, (hipStream_t)stream) == hipSuccess
+  return launch_decode_int8(*c, q, out, cmax, c_all, tv, gate, tau, 1.0f, ws, p, (hipStream_t)stream) == hipSuccess
+             ? SWA_OK
+             : SWA_EHIP;
+}
+
+int decode_attn_int8_dither(const swa_cache* c, const void* q, float* out, float* cert, float* tv, int32_t* gate,
+                            float tau, float delta, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (c->kind != SWA_KV_INT8_DITHER) return SWA_EUNSUPPORTED;
+  if (q == nullptr || out == nullptr || cert == nullptr || ws == nullptr) return SWA_ENULL;
+  if (gate != nullptr && tv == nullptr) return SWA_ENULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return SWA_EALIGN;
+  if (((uintptr_t)cert & 3u) || ((uintptr_t)tv & 3u) || ((uintptr_t)gate & 3u)) return SWA_EALIGN;
+  if (!(tau == tau)) return SWA_EINVAL;                 // NaN threshold
+  if (!(delta > 0.f && delta <= 1.f)) return SWA_EINVAL;  // also rejects NaN
+  if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
+  const SplitPlan p = plan_decode(*c);
+  return launch_decode_int8(*c, q, out, cert, nullptr, tv, gate, tau, delta, ws, p, (hipStream_t)stream) ==
+                 hipSuccess
              ? SWA_OK
              : SWA_EHIP;
 }

@@ -23,6 +23,27 @@
 // the XCDs' L2 caches without any device-wide fence.  Per block a
 // lane loads 2x16 B of key codes and 2x16 B of value codes (8 lanes per
 // 128-byte row, rows g and g+8) and 8 B of witness (4 lanes per token).
+//
+// Tier B (DITHER; same page, section 频带酉性与双层证书, second tier): the
+// codes carry a subtractive dither u = (m + 1/2)/256 - 1/2 that is
+// regenerated here from the Philox stream the write path used (key = the
+// request id, counter = (position, channel / 16, head, layer); section SGLang
+// 生产级落地 for the five-tuple).  A token is read as s * (code - u), with no
+// witness.  The lane that holds dims [16*(lane%8), +16) of rows g and g+8
+// needs exactly one Philox block per row, shared by the key and the value.
+// Since code - u = code - m/256 + 255/512, the key dot is
+// sum q code - (1/256) sum q m + (255/512) sum q, and the value sum gets
+// -(p s_V/256) m per element plus (255/512) times the running weight sum,
+// added once at the end.  The bound is probabilistic: with probability at
+// least 1 - delta every visible logit error is at most
+// cert = (S / sqrt(D)) (||q||_2 sqrt(ln(2 n_q / delta) / 6) + ||q||_1 beta),
+// where S is the largest key scale of a visible block and n_q the number of
+// visible quantized tokens.  Per channel the residual is uniform on 256 grid
+// points: variance proxy 1/12, |mean| <= beta = 2^-9 + 2^-16 in code
+// units.  A union bound over the n_q tokens gives the ln term.  The kernel
+// tracks S as its running maximum.
+#include <type_traits>
+
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -127,6 +148,46 @@ struct KeyDot {
 };
 #endif
 
+// Tier B key dot of 16 dims: sum q (code - u) with u = m/256 - 255/512,
+// as sum q code + sum (-q/256) m + (255/512) sum q (the query pre-scaled by
+// log2(e)/sqrt(D); -q/256 is exact).
+struct DitherKeyDot {
+  float qf[16], qn[16], qc;
+  __device__ __forceinline__ void init(const uint4* qv, float qscale) {
+    float t8[8];
+    unpack8(qv[0], t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] = t8[e] * qscale;
+    unpack8(qv[1], t8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[8 + e] = t8[e] * qscale;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      qn[e] = qf[e] * (-1.0f / 256.0f);
+      sum += qf[e];
+    }
+    qc = sum * (255.0f / 512.0f);
+  }
+  __device__ __forceinline__ float dot(const uint4 c, const uint4 m) const {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
+    float d = qc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d = fmaf(qf[4 * i + j], s8(cw[i], j), d);
+        d = fmaf(qn[4 * i + j], u8f(mw[i], j), d);
+      }
+    return d;
+  }
+};
+
+// Bias bound of the dither residual in code units (grid half-step plus the
+// float32 roundings that can move the rounding threshold).
+constexpr float kDitherBeta = 0x1p-9f + 0x1p-16f;
+
 // Last stage of one (b, h), run by >= 256 threads of a work-group (thread t
 // < D owns output dim t and holds the merged M, L, A of the committed
 // blocks; CM is their max c_t): fold in the exact staging tokens
@@ -136,11 +197,17 @@ struct KeyDot {
 // E = cmax, so the attention weights moved by at most tanh(E/2) in total
 // variation (page "WitCert", section 为什么在线监控 KV 误差如此困难 gives the
 // looser tanh(E) form); gate = tv > tau.
+//
+// DITHER: CM is the largest key scale S of the visible blocks, and the bound
+// written to cmax_out is the Tier B certificate built from S, the query
+// norms, n_q and delta (see the top of this file).
+template <bool DITHER>
 __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, float L, float A, float CM,
                                             float* sm_s, const uint16_t* __restrict__ kst,
                                             const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q,
                                             float* __restrict__ out, float* __restrict__ cmax_out,
-                                            float* __restrict__ tv, int32_t* __restrict__ gate, float tau) {
+                                            float* __restrict__ tv, int32_t* __restrict__ gate, float tau,
+                                            int W, float delta) {
   const float qscale = kLog2e / sqrtf((float)D);
   const int ns = n - (n / 16) * 16;
   if (ns > 0) {
@@ -172,6 +239,25 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
     }
   }
   if (t < D) out[bh * D + t] = L > 0.f ? A / L : 0.f;
+  if constexpr (DITHER) {
+    // ||q||_1 and ||q||_2^2 over the 128 dims: two per lane of the first wave.
+    float a1 = 0.f, a2 = 0.f;
+    if (t < 64) {
+      const float f0 = bf16_to_f32(q[bh * D + t]), f1 = bf16_to_f32(q[bh * D + t + 64]);
+      a1 = fabsf(f0) + fabsf(f1);
+      a2 = fmaf(f0, f0, f1 * f1);
+    }
+    a1 = group_sum<64>(a1);
+    a2 = group_sum<64>(a2);
+    const int len = n < W ? n : W;
+    const int nq = (n / 16) * 16 - (n - len);  // visible tokens in committed blocks
+    if (nq > 0) {
+      const float lg = logf(2.0f * (float)nq) - logf(delta);
+      CM *= (sqrtf(a2) * sqrtf(lg * (1.0f / 6.0f)) + a1 * kDitherBeta) / sqrtf((float)D);
+    } else {
+      CM = 0.f;
+    }
+  }
   if (t == 0) {
     const float cm = CM * kBoundPad;
     cmax_out[bh] = cm;
@@ -186,15 +272,17 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
 
 // FINAL: every (b, h) has a single split (the host plan has nsplit_max ==
 // 1), so the work-group finishes the (b, h) itself and no merge kernel runs.
-template <int NW, int UB, bool PAGED, bool FINAL>
+template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER>
 __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const int32_t* __restrict__ np,
     const int32_t* __restrict__ table, int64_t num_pages, const uint16_t* __restrict__ q,
     float* __restrict__ c_all, float* __restrict__ part, int H, int W, int cb, int nsplit_max,
     const uint16_t* __restrict__ kst, const uint16_t* __restrict__ vst, float* __restrict__ out,
-    float* __restrict__ cmax_out, float* __restrict__ tv, int32_t* __restrict__ gate, float tau) {
+    float* __restrict__ cmax_out, float* __restrict__ tv, int32_t* __restrict__ gate, float tau,
+    const uint64_t* __restrict__ req, uint32_t layer, float delta) {
   static_assert(NW * 64 >= 256, "the staging fold needs 256 threads");
+  static_assert(!DITHER || !SWA_INT8_KDOT_F16, "Tier B uses the byte-convert key dot");
   __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
   __shared__ float sm_acc[NW][D];
   __shared__ float sm_s[16];
@@ -222,8 +310,15 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 
   // Key-dot mapping: lane covers dims [16*(lane%8), +16) of row lane/8 (+8).
   const int g = lane >> 3, vq = lane & 7;
-  KeyDot kd;
+  typename std::conditional<DITHER, DitherKeyDot, KeyDot>::type kd;
   kd.init(reinterpret_cast<const uint4*>(q + bh * D) + 2 * vq, qscale);
+  // Tier B Philox key: the request id of this sequence (wave-uniform).
+  uint32_t rk0 = 0, rk1 = 0;
+  if constexpr (DITHER) {
+    const uint64_t rid = req[b];
+    rk0 = __builtin_amdgcn_readfirstlane((uint32_t)rid);
+    rk1 = __builtin_amdgcn_readfirstlane((uint32_t)(rid >> 32));
+  }
   // Witness mapping: lane covers bands [4*(lane%4), +4) of token lane/4.
   // nq[i] = ||q_band|| / sqrt(D) for those bands.
   const int wt = lane >> 2, wq = lane & 3;
@@ -241,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     }
   }
 
-  float m = kNegBig, l = 0.f, cm = 0.f, acc[16];
+  float m = kNegBig, l = 0.f, cm = 0.f, su = 0.f, acc[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 
@@ -281,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
         bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(kp + 1024 + lane * 16));
         bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(vp + lane * 16));
         bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(vp + 1024 + lane * 16));
-        bk[ub].w = load_stream(reinterpret_cast<const uint2*>(wp + lane * 8));
+        if constexpr (!DITHER) bk[ub].w = load_stream(reinterpret_cast<const uint2*>(wp + lane * 8));
         bk[ub].sk = ksc[pi];
         bk[ub].sv = vsc[pi];
       } else {
@@ -291,7 +386,8 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
         bk[ub].k1 = load_stream(reinterpret_cast<const uint4*>(Kbh + ok + 1024u));
         bk[ub].v0 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok));
         bk[ub].v1 = load_stream(reinterpret_cast<const uint4*>(Vbh + ok + 1024u));
-        bk[ub].w = load_stream(reinterpret_cast<const uint2*>(Wbh + sb * 32u + (uint32_t)lane * 8u));
+        if constexpr (!DITHER)
+          bk[ub].w = load_stream(reinterpret_cast<const uint2*>(Wbh + sb * 32u + (uint32_t)lane * 8u));
         bk[ub].sk = ksbh[kb % wblocks];
         bk[ub].sv = vsbh[kb % wblocks];
       }
@@ -300,6 +396,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 
   auto step = [&](const Blk (&cur)[UB], int kb0) {
     float s[2 * UB], sv[UB];
+    uint4 dm[2 * UB];  // Tier B dither bytes of rows g and g+8 of each block
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       const int kb = kb0 + ub;
@@ -310,13 +407,24 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
       sv[ub] = cur[ub].sv;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float d = kd.dot(half ? cur[ub].k1 : cur[ub].k0);
-        d = kd.finish(group_sum<8>(d)) * sk;  // key scale folded into the finished dot
         const int pos = kb * 16 + g + 8 * half;
+        float d;
+        if constexpr (DITHER) {
+          dm[2 * ub + half] = philox4x32_10(make_uint4((uint32_t)(kbc * 16 + g + 8 * half), (uint32_t)vq,
+                                                       (uint32_t)h, layer), rk0, rk1);
+          d = kd.dot(half ? cur[ub].k1 : cur[ub].k0, dm[2 * ub + half]);
+          d = group_sum<8>(d) * sk;
+        } else {
+          d = kd.dot(half ? cur[ub].k1 : cur[ub].k0);
+          d = kd.finish(group_sum<8>(d)) * sk;  // key scale folded into the finished dot
+        }
         s[2 * ub + half] = (live && pos >= p0) ? d : -INFINITY;
       }
-      // Witness bound of token wt of this block.
-      {
+      if constexpr (DITHER) {
+        // every live block holds at least one visible token
+        if (live) cm = fmaxf(cm, sk);
+      } else {
+        // Witness bound of token wt of this block.
         const uint2 w = cur[ub].w;
         float cp = nq[0] * f16_to_f32((uint16_t)(w.x & 0xffff));
         cp = fmaf(nq[1], f16_to_f32((uint16_t)(w.x >> 16)), cp);
@@ -335,6 +443,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     for (int i = 0; i < 2 * UB; ++i) mx = fmaxf(mx, s[i]);
     const float alpha = exp2_fast(m - mx);
     l *= alpha;
+    if constexpr (DITHER) su *= alpha;
 #pragma unroll
     for (int e2 = 0; e2 < 16; ++e2) acc[e2] *= alpha;
 #pragma unroll
@@ -350,6 +459,16 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pv, s8(cw[i], j), acc[4 * i + j]);
+        if constexpr (DITHER) {
+          const uint4 mm = dm[2 * ub + half];
+          const uint32_t mw[4] = {mm.x, mm.y, mm.z, mm.w};
+          const float pvn = pv * (-1.0f / 256.0f);
+          su += pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pvn, u8f(mw[i], j), acc[4 * i + j]);
+        }
       }
     }
     m = mx;
@@ -374,6 +493,11 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     }
   }
 
+  if constexpr (DITHER) {
+    // the (255/512) sum p s_V term of every element (code - u = code - m/256 + 255/512)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = fmaf(su, 255.0f / 512.0f, acc[e]);
+  }
   // Merge the 8 lane groups of the wave (lanes with equal lane%8 share dims).
   float mw = m;
 #pragma unroll
@@ -411,7 +535,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
   }
 
   if constexpr (FINAL) {
-    finish_int8(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau);
+    finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta);
   } else {
     float* my = part + (bh * nsplit_max + split) * PF;
     if (t < D) my[4 + t] = A;
@@ -422,11 +546,12 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 // Merge of one (b, h): log-sum-exp over the split partials, then the
 // staging fold, normalization and bound epilogue of finish_int8.  256
 // threads; thread t < D owns output dim t.
+template <bool DITHER>
 __global__ __launch_bounds__(256) void merge_int8_kernel(
     const int32_t* __restrict__ np, const float* __restrict__ part, const uint16_t* __restrict__ kst,
     const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q, float* __restrict__ out,
     float* __restrict__ cmax_out, float* __restrict__ tv, int32_t* __restrict__ gate, float tau, int H, int W,
-    int cb, int nsplit_max) {
+    int cb, int nsplit_max, float delta) {
   __shared__ float sm_s[16];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int64_t bh = (int64_t)b * H + h;
@@ -443,7 +568,7 @@ __global__ __launch_bounds__(256) void merge_int8_kernel(
     merge_partials<PF>(pp, nsplit, t, M, L, A);
     for (int sp = 0; sp < nsplit; ++sp) CM = fmaxf(CM, pp[sp * PF + 2]);
   }
-  finish_int8(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau);
+  finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta);
 }
 
 __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
@@ -456,8 +581,10 @@ __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
 int decode_int8_round_blocks() { return SWA_INT8_NW * SWA_INT8_UB; }
 
 hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax, float* c_all,
-                              float* tv, int32_t* gate, float tau, void* ws, const SplitPlan& plan,
+                              float* tv, int32_t* gate, float tau, float delta, void* ws, const SplitPlan& plan,
                               hipStream_t s) {
+  const bool dither = c.kind == SWA_KV_INT8_DITHER;
+  if (dither) c_all = nullptr;
   constexpr int NW = SWA_INT8_NW, UB = SWA_INT8_UB;
   if (c_all != nullptr) {
     const int64_t n = (int64_t)c.B * c.H * c.W;
@@ -478,21 +605,33 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
   const uint16_t* vst = reinterpret_cast<const uint16_t*>(c.v_stage);
   const int32_t* table = paged ? c.block_table : nullptr;
   const int64_t npages = paged ? c.num_pages : 0;
-#define SWA_INT8_LAUNCH(P, F)                                                                                    \
-  hipLaunchKernelGGL((decode_int8_kernel<NW, UB, P, F>), grid, block, lds, s, kc, vc, c.k_scale, c.v_scale,     \
+  const uint64_t* req = dither ? c.request_id : nullptr;
+#define SWA_INT8_LAUNCH(P, F, DI)                                                                                \
+  hipLaunchKernelGGL((decode_int8_kernel<NW, UB, P, F, DI>), grid, block, lds, s, kc, vc, c.k_scale, c.v_scale, \
                      c.witness, c.next_position, table, npages, q16, c_all, part, c.H, c.W, plan.unit_per_split, \
-                     plan.nsplit_max, kst, vst, out, cmax, tv, gate, tau)
-  const bool final_pass = plan.nsplit_max == 1;
-  if (paged) {
-    if (final_pass) SWA_INT8_LAUNCH(true, true); else SWA_INT8_LAUNCH(true, false);
-  } else {
-    if (final_pass) SWA_INT8_LAUNCH(false, true); else SWA_INT8_LAUNCH(false, false);
+                     plan.nsplit_max, kst, vst, out, cmax, tv, gate, tau, req, c.layer, delta)
+#define SWA_INT8_LAUNCH_PF(DI)                                                              \
+  if (paged) {                                                                              \
+    if (final_pass) SWA_INT8_LAUNCH(true, true, DI); else SWA_INT8_LAUNCH(true, false, DI);    \
+  } else {                                                                                  \
+    if (final_pass) SWA_INT8_LAUNCH(false, true, DI); else SWA_INT8_LAUNCH(false, false, DI);  \
   }
+  const bool final_pass = plan.nsplit_max == 1;
+  if (dither) {
+    SWA_INT8_LAUNCH_PF(true)
+  } else {
+    SWA_INT8_LAUNCH_PF(false)
+  }
+#undef SWA_INT8_LAUNCH_PF
 #undef SWA_INT8_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || final_pass) return e;
-  hipLaunchKernelGGL(merge_int8_kernel, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst, q16, out,
-                     cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max);
+  if (dither)
+    hipLaunchKernelGGL(merge_int8_kernel<true>, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst,
+                       q16, out, cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max, delta);
+  else
+    hipLaunchKernelGGL(merge_int8_kernel<false>, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst,
+                       q16, out, cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max, delta);
   return hipGetLastError();
 }
 

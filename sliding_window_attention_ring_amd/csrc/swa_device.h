@@ -71,6 +71,27 @@ __device__ __forceinline__ float s8(uint32_t w, int j) {
   return (float)(int32_t)(int8_t)(w >> (8 * j));
 }
 
+// Unsigned byte j of a 32-bit word as fp32 (one byte convert).
+__device__ __forceinline__ float u8f(uint32_t w, int j) { return (float)((w >> (8 * j)) & 0xffu); }
+
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC 2011).  Each round forms the 64-bit
+// products M0*c0 and M1*c2 and maps the counter to
+// (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key
+// then advances by the Weyl constants.  With a wave-uniform key the key
+// schedule stays in scalar registers.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

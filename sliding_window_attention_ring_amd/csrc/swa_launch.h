@@ -38,8 +38,9 @@ hipError_t launch_advance(const swa_cache& c, int T, hipStream_t s);
 
 hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws,
                          const SplitPlan& plan, hipStream_t s);
+// INT8 kinds; delta is the Tier B failure budget (ignored for SWA_KV_INT8).
 hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax,
-                              float* c_all, float* tv, int32_t* gate, float tau, void* ws,
+                              float* c_all, float* tv, int32_t* gate, float tau, float delta, void* ws,
                               const SplitPlan& plan, hipStream_t s);
 
 hipError_t launch_reset(const swa_cache& c, hipStream_t s);

@@ -9,7 +9,7 @@
 //
 // On the ring the truncation is exact iff every row the shorter history's
 // window needs is still stored: 0 <= cut <= n and (n <= W, or cut == n, or
-// cut == 0).  An INT8 cache also needs cut on a 16-token block boundary or
+// cut == 0).  An INT8 cache (either kind) also needs cut on a 16-token block boundary or
 // inside the exact staging tail (cut >= 16*(n/16)), since committed blocks
 // keep only codes.
 #include "swa_device.h"
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void truncate_kernel(int32_t* __restrict__ pos
 
 hipError_t launch_truncate(const swa_cache& c, const int32_t* cut, int32_t* ok, hipStream_t s) {
   hipLaunchKernelGGL(truncate_kernel, dim3(c.B), dim3(256), 0, s, c.pos, c.next_position, cut, ok, c.W,
-                     c.kind == SWA_KV_INT8 ? 1 : 0);
+                     (c.kind == SWA_KV_INT8 || c.kind == SWA_KV_INT8_DITHER) ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import bits, decoder, int8 as oint8
+from oracle import bits, decoder, dither as odither, int8 as oint8
 
 TOL = 2e-3  # max abs error of outputs vs the float64 oracle on the same inputs
 
@@ -60,12 +60,12 @@ class RingView:
             return pool[pages, :, rows].permute(0, 2, 1, 3).contiguous()
 
         self.k, self.v = gather(cache.k), gather(cache.v)
-        if cache.kind == "int8":
-            self.witness = gather(cache.witness)
+        self.k_scale = self.v_scale = self.witness = None
+        if cache.kind in ("int8", "int8_dither"):
             self.k_scale = cache.k_scale[tbl].permute(0, 2, 1).contiguous()  # [B, H, W/16]
             self.v_scale = cache.v_scale[tbl].permute(0, 2, 1).contiguous()
-        else:
-            self.k_scale = self.v_scale = self.witness = None
+        if cache.kind == "int8":
+            self.witness = gather(cache.witness)
 
 
 def check_ring_rows(cache, k_in: np.ndarray, v_in: np.ndarray, n: np.ndarray):
@@ -146,4 +146,59 @@ def check_int8_decode(out, cmax, c_all, b, h, q64, k64, v64, n, W, what=""):
         vis = np.zeros(W, dtype=bool)
         vis[slots[quant]] = True
         assert not np.any(np.asarray(c_all)[~vis]), "slots without a visible quantized token must be 0"
+    return err
+
+
+def request_ids(cache) -> np.ndarray:
+    """The cache's request ids as Python ints (uint64 values)."""
+    return [int(x) & ((1 << 64) - 1) for x in cache.request_id.cpu().tolist()]
+
+
+def check_dither_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, n: int):
+    """Tier B cache of (b, h): slot positions, codes and scales of every
+    committed block in the ring bit-exact vs the oracle (which draws the same
+    Philox dither itself); staging rows equal the input bits."""
+    req, layer = request_ids(cache)[b], cache.layer
+    view = RingView(cache) if getattr(cache, "layout", "ring") == "paged" else cache
+    W = cache.W
+    nb = n // 16
+    pos = host_bits(view.pos[b])
+    kc = host_bits(view.k[b, h]); vc = host_bits(view.v[b, h])
+    ks = host_bits(view.k_scale[b, h]); vs = host_bits(view.v_scale[b, h])
+    exp_pos = np.full(W, -1, dtype=np.int64)
+    for kb in range(max(0, nb - W // 16), nb):
+        rows = np.arange(kb * 16, kb * 16 + 16)
+        u = odither.dither(req, layer, h, rows, k64.shape[-1])
+        sk, ck = odither.quantize_block(k64[rows], u)
+        sv, cv = odither.quantize_block(v64[rows], u)
+        slot0 = (kb * 16) % W
+        exp_pos[slot0:slot0 + 16] = rows
+        np.testing.assert_array_equal(kc[slot0:slot0 + 16], ck, err_msg=f"key codes b={b} h={h} block {kb}")
+        np.testing.assert_array_equal(vc[slot0:slot0 + 16], cv, err_msg=f"value codes b={b} h={h} block {kb}")
+        assert ks[slot0 // 16] == sk and vs[slot0 // 16] == sv, (kb, ks[slot0 // 16], sk)
+    np.testing.assert_array_equal(pos, exp_pos)
+    ksg = host_bits(cache.k_stage[b, h]); vsg = host_bits(cache.v_stage[b, h])
+    for p in range(16 * nb, n):
+        np.testing.assert_array_equal(bits.to_f64(ksg[p % 16]), k64[p])
+        np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])
+
+
+def check_dither_decode(out, cert, b, h, q64, k64, v64, n, W, req, layer, delta, tv=None, gate=None,
+                        tau=0.2, what=""):
+    """Tier B decode of (b, h) vs the oracle: output within TOL; the
+    certificate equal to the oracle's up to its float32 pad, and (an event of
+    probability >= 1 - delta) not below the true largest logit error; tv =
+    tanh(cert/2) padded, and gate = tv > tau."""
+    res = odither.int8_dither_decode(q64, k64, v64, n, W, req, layer, h, float(np.float32(delta)))
+    err = assert_close(out, res["out"], f"dither out {what} b={b} h={h}")
+    ref = res["cert"]
+    assert cert >= ref, (what, b, h, cert, ref)
+    assert cert <= ref * (1 + 2.0 ** -10) + 1e-30, (what, b, h, cert, ref)
+    emax = float(np.max(res["e"])) if res["e"].size else 0.0
+    assert cert >= emax, f"{what} b={b} h={h}: certificate {cert} below the logit error {emax}"
+    if tv is not None:
+        t = float(np.tanh(cert / 2))
+        assert t <= tv <= min(t * (1 + 2.0 ** -18) + 1e-30, 1.0), (tv, t)
+        if gate is not None:
+            assert int(gate) == int(tv > tau)
     return err

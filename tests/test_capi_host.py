@@ -37,7 +37,7 @@ def desc(**kw):
     from sliding_window_attention_ring_amd._capi import SwaCacheDesc
     base = dict(kind=0, B=2, H=4, D=128, W=64, layout=0, k=0x10000, v=0x20000, pos=0x30000,
                 next_position=0x40000, k_scale=0x50000, v_scale=0x60000, witness=0x70000,
-                k_stage=0x80000, v_stage=0x90000, block_table=0xC0000, num_pages=8)
+                k_stage=0x80000, v_stage=0x90000, block_table=0xC0000, num_pages=8, request_id=None, layer=0)
     base.update(kw)
     return SwaCacheDesc(**base)
 
@@ -86,6 +86,25 @@ def test_argument_checks_return_codes():
     assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, A16, A16, float("nan"), None, ws, 1 << 30,
                                          None) == -1
     assert L.decode_attn_int8_witness_tv(p(d), A16, A16, A16, A16, A16, 0.2, None, ws, 1 << 30, None) == -4
+    # Tier B kind: no witness needed, request ids required, delta in (0, 1]
+    dz = desc(kind=3, witness=None, request_id=0xD0000)
+    nz = L.swa_workspace_bytes(p(dz))
+    assert nz == L.swa_workspace_bytes(p(desc(kind=2)))
+    assert L.kv_append(p(dz), A16, A16, 0, None) == 0
+    assert L.kv_append(p(desc(kind=3, request_id=None)), A16, A16, 1, None) == -2
+    assert L.kv_append(p(desc(kind=3, request_id=0xD0004)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(kind=3, request_id=0xD0000, D=64)), A16, A16, 1, None) == -4
+    dd = L.decode_attn_int8_dither
+    assert dd(p(dz), A16, A16, A16, A16, A16, 0.2, 0.0, ws, nz, None) == -1        # delta = 0
+    assert dd(p(dz), A16, A16, A16, A16, A16, 0.2, 1.5, ws, nz, None) == -1        # delta > 1
+    assert dd(p(dz), A16, A16, A16, A16, A16, 0.2, float("nan"), ws, nz, None) == -1
+    assert dd(p(dz), A16, A16, A16, A16, A16, float("nan"), 0.1, ws, nz, None) == -1
+    assert dd(p(dz), A16, A16, A16, None, A16, 0.2, 0.1, ws, nz, None) == -2       # gate without tv
+    assert dd(p(dz), A16, A16, None, None, None, 0.2, 0.1, ws, nz, None) == -2     # cert NULL
+    assert dd(p(dz), A16, A16, A16, None, None, 0.2, 0.1, ws, nz - 1, None) == -5
+    assert dd(p(i8), A16, A16, A16, None, None, 0.2, 0.1, ws, nz, None) == -4      # Tier A cache
+    assert L.decode_attn_int8_witness(p(dz), A16, A16, A16, None, ws, nz, None) == -4
+    assert L.decode_attn(p(dz), A16, A16, ws, nz, None) == -4
     assert L.swa_validate(p(d), None, None) == -2
     assert L.swa_workspace_init(None, 64, None) == -2
     assert L.swa_workspace_init(ODD, 64, None) == -3

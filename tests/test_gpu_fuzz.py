@@ -9,8 +9,8 @@ import pytest
 import torch
 
 from oracle import reuse
-from tests.gpu_util import (assert_close, check_int8_decode, check_int8_store, check_ring_rows, f64, host_bits,
-                            oracle_out, require_gpu)
+from tests.gpu_util import (assert_close, check_dither_decode, check_dither_store, check_int8_decode,
+                            check_int8_store, check_ring_rows, f64, host_bits, oracle_out, request_ids, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("kind,layout,W,seed", [("bf16", "ring", 48, 1), ("bf16", "paged", 64, 2),
-                                                ("int8", "ring", 64, 3), ("int8", "paged", 48, 4)])
+                                                ("int8", "ring", 64, 3), ("int8", "paged", 48, 4),
+                                                ("int8_dither", "ring", 48, 5), ("int8_dither", "paged", 64, 6)])
 def test_mixed_operation_fuzz(kind, layout, W, seed):
     import sliding_window_attention_ring_amd as swa
     rng = np.random.default_rng(seed)
@@ -53,7 +54,7 @@ def test_mixed_operation_fuzz(kind, layout, W, seed):
             cuts = [int(rng.integers(0, n + 1)) for n in ns]
             ok = swa.kv_truncate(cache, torch.tensor(cuts, dtype=torch.int32, device="cuda")).cpu().numpy()
             for b in range(B):
-                assert bool(ok[b]) == reuse.truncation_exact(ns[b], cuts[b], W, int8=(kind == "int8"))
+                assert bool(ok[b]) == reuse.truncation_exact(ns[b], cuts[b], W, int8=kind.startswith("int8"))
                 if ok[b]:
                     hist_k[b] = hist_k[b][:, :cuts[b]]
                     hist_v[b] = hist_v[b][:, :cuts[b]]
@@ -64,6 +65,10 @@ def test_mixed_operation_fuzz(kind, layout, W, seed):
             for b in range(B):
                 for h in range(H):
                     check_int8_store(cache, b, h, f64(hist_k[b][h]), f64(hist_v[b][h]), ns[b])
+        elif kind == "int8_dither":
+            for b in range(B):
+                for h in range(H):
+                    check_dither_store(cache, b, h, f64(hist_k[b][h]), f64(hist_v[b][h]), ns[b])
         else:
             N = max(max(ns), 1)
             kb = np.zeros((B, H, N, D), dtype=np.uint16)
@@ -75,7 +80,19 @@ def test_mixed_operation_fuzz(kind, layout, W, seed):
         if rng.random() < 0.6:  # decode
             q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
             q64 = f64(q)
-            if kind == "int8":
+            if kind == "int8_dither":
+                out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q.cuda(), delta=1e-3)
+                out, cert, tv, gate = out.cpu().numpy(), cert.cpu().numpy(), tv.cpu().numpy(), gate.cpu().numpy()
+                reqs = request_ids(cache)
+                for b in range(B):
+                    for h in range(H):
+                        if ns[b] == 0:
+                            assert not out[b, h].any() and cert[b, h] == 0
+                            continue
+                        check_dither_decode(out[b, h], cert[b, h], b, h, q64[b, h], f64(hist_k[b][h]),
+                                            f64(hist_v[b][h]), ns[b], W, reqs[b], cache.layer, 1e-3, tv[b, h],
+                                            gate[b, h], what=f"op {op}")
+            elif kind == "int8":
                 out, cmax, c_all = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
                 out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
                 for b in range(B):

@@ -21,7 +21,7 @@ def _gpu():
     require_gpu()
 
 
-@pytest.mark.parametrize("kind,W,prefill", [("int8", 256, 250), ("bf16", 200, 390)])
+@pytest.mark.parametrize("kind,W,prefill", [("int8", 256, 250), ("bf16", 200, 390), ("int8_dither", 128, 300)])
 def test_captured_step_replays_match_eager(kind, W, prefill):
     import sliding_window_attention_ring_amd as swa
     B, H, D, steps = 3, 4, 128, 20
@@ -39,6 +39,8 @@ def test_captured_step_replays_match_eager(kind, W, prefill):
     static_q = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
     out_g = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
     cmax_g = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    tv_g = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    gate_g = torch.empty((B, H), dtype=torch.int32, device="cuda")
     ws_g = cg.workspace()
     torch.cuda.synchronize()
 
@@ -47,6 +49,9 @@ def test_captured_step_replays_match_eager(kind, W, prefill):
         swa.kv_append(cg, static_k, static_v)
         if kind == "int8":
             swa.decode_attn_int8_witness(cg, static_q, out=out_g, cmax=cmax_g, ws=ws_g)
+        elif kind == "int8_dither":
+            swa.decode_attn_int8_dither(cg, static_q, delta=1e-3, out=out_g, cert=cmax_g, tv=tv_g, gate=gate_g,
+                                        ws=ws_g)
         else:
             swa.decode_attn(cg, static_q, out=out_g, ws=ws_g)
     torch.cuda.synchronize()
@@ -60,12 +65,17 @@ def test_captured_step_replays_match_eager(kind, W, prefill):
         swa.kv_append(ce, k[:, :, p:p + 1].contiguous(), v[:, :, p:p + 1].contiguous())
         if kind == "int8":
             out_e, cmax_e, _ = swa.decode_attn_int8_witness(ce, qs[i])
+        elif kind == "int8_dither":
+            out_e, cmax_e, tv_e, gate_e = swa.decode_attn_int8_dither(ce, qs[i], delta=1e-3)
         else:
             out_e = swa.decode_attn(ce, qs[i])
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), f"replay {i}"
-        if kind == "int8":
+        if kind.startswith("int8"):
             assert torch.equal(cmax_g, cmax_e), f"replay {i}"
+        if kind == "int8_dither":
+            assert torch.equal(tv_g, tv_e) and torch.equal(gate_g, gate_e), f"replay {i}"
+            assert torch.equal(cg.k, ce.k) and torch.equal(cg.k_scale, ce.k_scale), f"replay {i}"
         assert torch.equal(cg.next_position, ce.next_position)
         assert (host_bits(cg.pos) == host_bits(ce.pos)).all()
     assert int(cg.next_position[0]) == prefill + steps

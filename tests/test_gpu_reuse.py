@@ -12,7 +12,8 @@ import pytest
 import torch
 
 from oracle import reuse
-from tests.gpu_util import (assert_close, check_int8_decode, check_int8_store, check_ring_rows, f64, host_bits,
+from tests.gpu_util import (assert_close, check_dither_decode, check_dither_store, check_int8_decode,
+                            check_int8_store, check_ring_rows, f64, host_bits, request_ids,
                             oracle_out, require_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -100,3 +101,33 @@ def test_truncate_int8():
             check_int8_store(cache, b, h, k64[h], v64[h], n_eff)
             check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, q64[b, h], k64[h], v64[h], n_eff, W,
                               what=f"truncate int8 b={b}")
+
+
+def test_truncate_int8_dither():
+    """Tier B follows the INT8 rule; tokens appended after a cut reuse the
+    positions, hence the dither stream, of the tokens they replace."""
+    import sliding_window_attention_ring_amd as swa
+    W = 64
+    ns = [40, 40, 40, 100, 48, 40]
+    cuts = [32, 35, 20, 100, 0, 16]
+    cache, k, v, g = build(swa, "int8_dither", W, ns, 200, seed=4)
+    ok = swa.kv_truncate(cache, torch.tensor(cuts, dtype=torch.int32, device="cuda")).cpu().numpy()
+    assert list(ok) == [1, 1, 0, 1, 1, 1]
+    assert swa.validate(cache) == 0
+    T = 20
+    new_k = torch.randn((len(ns), 2, T, 128), generator=g).to(torch.bfloat16)
+    new_v = torch.randn((len(ns), 2, T, 128), generator=g).to(torch.bfloat16)
+    swa.kv_append(cache, new_k.cuda(), new_v.cuda())
+    q = torch.randn((len(ns), 2, 128), generator=g).to(torch.bfloat16)
+    out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q.cuda(), delta=1e-3)
+    out, cert, tv, gate = out.cpu().numpy(), cert.cpu().numpy(), tv.cpu().numpy(), gate.cpu().numpy()
+    assert swa.validate(cache) == 0
+    q64 = f64(q)
+    reqs = request_ids(cache)
+    for b, (n, c) in enumerate(zip(ns, cuts)):
+        kk, vv, n_eff = effective(k, v, b, n, c, ok[b], new_k, new_v)
+        k64, v64 = f64(kk), f64(vv)
+        for h in range(2):
+            check_dither_store(cache, b, h, k64[h], v64[h], n_eff)
+            check_dither_decode(out[b, h], cert[b, h], b, h, q64[b, h], k64[h], v64[h], n_eff, W, reqs[b],
+                                cache.layer, 1e-3, tv[b, h], gate[b, h], what=f"truncate dither b={b}")
