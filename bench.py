@@ -2,8 +2,9 @@
 
 A step is one pass of the decode hot path over the whole batch: append one
 token per sequence (``kv_append``), then one query per sequence attends to
-the cache (``decode_attn_int8_witness`` for INT8 workloads, ``decode_attn``
-otherwise).  The default workload is the INT8 cache with the witness bound at
+the cache (``decode_attn_int8_witness`` for INT8 workloads,
+``decode_attn_int8_dither`` with its TV bound and gate for the dithered INT8
+workload, ``decode_attn`` otherwise).  The default workload is the INT8 cache with the witness bound at
 32768 context (B=16, H=32, D=128), prefilled with 32768 rotary keys.
 
 Prints ONE JSON line on stdout.  ``value`` is the whole step's algorithmic
@@ -30,6 +31,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + tokens·heads/s at 32k ctx"
 PEAK_GBS = 8000.0  # MI355X HBM3E peak
+# Per-query failure budget of the dithered INT8 certificate (one (b, h)).
+DITHER_DELTA = 1e-6
 CSRC = os.path.join(ROOT, "sliding_window_attention_ring_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -39,7 +42,7 @@ def log(*a):
 
 
 def kernel_source_hash(kind: str) -> str:
-    files = ["swa_device.h", "swa_decode_int8.hip" if kind == "int8" else "swa_decode.hip"]
+    files = ["swa_device.h", "swa_decode_int8.hip" if kind.startswith("int8") else "swa_decode.hip"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -76,13 +79,15 @@ def step_bytes(wl, n_after):
     BH, D = wl.B * wl.H, wl.D
     vis = min(wl.W, n_after) * wl.B
     q_out = BH * D * 2 + BH * D * 4
-    if wl.kind == "int8":
+    if wl.kind in ("int8", "int8_dither"):
+        wit = 2 * D // 8 if wl.kind == "int8" else 0   # fp16 band norms per token-head (Tier A only)
+        outs = 4 if wl.kind == "int8" else 12           # cmax, or cert + tv + gate
         staged = n_after % 16
         quant = min(wl.W, n_after) - staged
-        dec = BH * (quant * (2 * D + 2 * D // 8 + 2 * 4 / 16) + staged * 2 * D * 2) + q_out + BH * 4
+        dec = BH * (quant * (2 * D + wit + 2 * 4 / 16) + staged * 2 * D * 2) + q_out + BH * outs
         app = BH * 2 * D * 2 * 2  # read the new rows, write them to staging
         if n_after % 16 == 0:     # a block completes: read 16 staged rows, write codes/witness/scales
-            app += BH * 16 * (2 * D * 2 + 2 * D + 2 * D // 8) + BH * 2 * 4
+            app += BH * 16 * (2 * D * 2 + 2 * D + wit) + BH * 2 * 4
     else:
         esz = 4 if wl.kind == "fp32" else 2
         dec = BH * min(wl.W, n_after) * 2 * D * esz + (BH * D * esz + BH * D * 4)
@@ -95,7 +100,7 @@ def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0):
     workload at next_position n, one thread; GB/s of algorithmic bytes."""
     import numpy as np
     from threadpoolctl import threadpool_limits
-    from oracle import attention, bits, int8 as oint8
+    from oracle import attention, bits, dither as odither, int8 as oint8
     from workloads import gen
 
     rng = np.random.default_rng(2026)
@@ -113,6 +118,8 @@ def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0):
             t0 = time.perf_counter()
             if wl.kind == "int8":
                 oint8.int8_decode(qq, kk, vv, n, wl.W)
+            elif wl.kind == "int8_dither":
+                odither.int8_dither_decode(qq, kk, vv, n, wl.W, b, 0, h, DITHER_DELTA)
             else:
                 attention.masked_attention(qq, np.arange(n), kk, vv, n - 1, wl.W)
             t_used += time.perf_counter() - t0
@@ -183,6 +190,16 @@ def main():
     ws = cache.workspace()
     out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.float32, device=dev)
     cmax = torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev)
+    tv = torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev)
+    gate = torch.empty((wl.B, wl.H), dtype=torch.int32, device=dev)
+
+    def decode(q):
+        if wl.kind == "int8":
+            swa.decode_attn_int8_witness(cache, q, out=out, cmax=cmax, ws=ws)
+        elif wl.kind == "int8_dither":
+            swa.decode_attn_int8_dither(cache, q, delta=DITHER_DELTA, out=out, cert=cmax, tv=tv, gate=gate, ws=ws)
+        else:
+            swa.decode_attn(cache, q, out=out, ws=ws)
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t0:.1f} s")
 
@@ -196,10 +213,7 @@ def main():
 
     def step(i):
         swa.kv_append(cache, ks[i], vs[i])
-        if wl.kind == "int8":
-            swa.decode_attn_int8_witness(cache, qs[i], out=out, cmax=cmax, ws=ws)
-        else:
-            swa.decode_attn(cache, qs[i], out=out, ws=ws)
+        decode(qs[i])
 
     for i in range(args.warmup):
         step(i)
@@ -219,10 +233,7 @@ def main():
         j = args.warmup + i
         swa.kv_append(cache, ks[j], vs[j])
         evs[i][0].record(stream)
-        if wl.kind == "int8":
-            swa.decode_attn_int8_witness(cache, qs[j], out=out, cmax=cmax, ws=ws)
-        else:
-            swa.decode_attn(cache, qs[j], out=out, ws=ws)
+        decode(qs[j])
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -249,8 +260,9 @@ def main():
                    "context": min(wl.W, prefill) if lens is None else [int(n) for n in lens],
                    "kv_dtype": wl.kind, "layout": wl.layout,
                    "positions": [prefill + args.warmup, prefill + n_steps - 1],
-                   "step": "kv_append(T=1) + " + ("decode_attn_int8_witness" if wl.kind == "int8"
-                                                  else "decode_attn")},
+                   "step": "kv_append(T=1) + " + {"int8": "decode_attn_int8_witness",
+                                                  "int8_dither": "decode_attn_int8_dither (cert, tv, gate; "
+                                                                 f"delta={DITHER_DELTA})"}.get(wl.kind, "decode_attn")},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "kv_token_heads_per_s": vis_tokens * wl.H / elapsed,
         "query_token_heads_per_s": BH * args.steps / elapsed,
@@ -261,7 +273,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": read_traffic(wl.name, wl.kind),
-            "kernel": "decode_int8_kernel" if wl.kind == "int8" else "decode_kernel",
+            "kernel": "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel",
             "kernel_ms": round(kern_ms, 4),
             "algorithmic_bytes_per_launch": dec_bytes / args.steps,
         },

@@ -31,10 +31,12 @@
 // 生产级落地 for the five-tuple).  A token is read as s * (code - u), with no
 // witness.  The lane that holds dims [16*(lane%8), +16) of rows g and g+8
 // needs exactly one Philox block per row, shared by the key and the value.
-// Since code - u = code - m/256 + 255/512, the key dot is
-// sum q code - (1/256) sum q m + (255/512) sum q, and the value sum gets
-// -(p s_V/256) m per element plus (255/512) times the running weight sum,
-// added once at the end.  The bound is probabilistic: with probability at
+// With t = 256 code + 255 - m, a signed 16-bit integer that one byte
+// permute builds from the code byte and the complemented dither byte (two
+// elements per permute), code - u = (t - 127.5)/256.  So the key dot is
+// (1/256) sum q t - (127.5/256) sum q, and the value sum gets (p s_V/256) t
+// per element, with -(127.5/256) times the running weight sum added once
+// at the end.  The bound is probabilistic: with probability at
 // least 1 - delta every visible logit error is at most
 // cert = (S / sqrt(D)) (||q||_2 sqrt(ln(2 n_q / delta) / 6) + ||q||_1 beta),
 // where S is the largest key scale of a visible block and n_q the number of
@@ -60,6 +62,16 @@ namespace {
 // 1: key dots on packed fp16 (codes as 1024+u, query in fp16) with v_dot2_f32_f16.
 #ifndef SWA_INT8_KDOT_F16
 #define SWA_INT8_KDOT_F16 0
+#endif
+// Nonzero: ask the compiler for at least this many waves per SIMD (caps the
+// registers per lane at 512 / waves).
+#ifndef SWA_INT8_WAVES
+#define SWA_INT8_WAVES 0
+#endif
+#if SWA_INT8_WAVES
+#define SWA_INT8_WAVES_ATTR __attribute__((amdgpu_waves_per_eu(SWA_INT8_WAVES)))
+#else
+#define SWA_INT8_WAVES_ATTR
 #endif
 
 constexpr int D = 128;
@@ -148,13 +160,24 @@ struct KeyDot {
 };
 #endif
 
-// Tier B key dot of 16 dims: sum q (code - u) with u = m/256 - 255/512,
-// as sum q code + sum (-q/256) m + (255/512) sum q (the query pre-scaled by
-// log2(e)/sqrt(D); -q/256 is exact).
+// Tier B element values t = 256 code + 255 - m for the 4 codes of word cw,
+// given nm = ~m: bytes (~m0, c0, ~m1, c1) and (~m2, c2, ~m3, c3) as two
+// signed 16-bit halves each (a byte permute takes bytes 0-3 from its second
+// operand and 4-7 from its first).
+__device__ __forceinline__ void dither_t(uint32_t cw, uint32_t nm, float (&t)[4]) {
+  const uint32_t lo = __builtin_amdgcn_perm(cw, nm, 0x05010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(cw, nm, 0x07030602u);
+  t[0] = s16lo(lo); t[1] = s16hi(lo);
+  t[2] = s16lo(hi); t[3] = s16hi(hi);
+}
+
+// Tier B key dot of 16 dims: sum q (code - u) = (1/256) sum q t -
+// (127.5/256) sum q, the query pre-scaled by log2(e)/sqrt(D) (q/256 is
+// exact).
 struct DitherKeyDot {
-  float qf[16], qn[16], qc;
+  float qt[16], qc;
   __device__ __forceinline__ void init(const uint4* qv, float qscale) {
-    float t8[8];
+    float t8[8], qf[16];
     unpack8(qv[0], t8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[e] = t8[e] * qscale;
@@ -164,22 +187,23 @@ struct DitherKeyDot {
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      qn[e] = qf[e] * (-1.0f / 256.0f);
+      qt[e] = qf[e] * (1.0f / 256.0f);
       sum += qf[e];
     }
-    qc = sum * (255.0f / 512.0f);
+    qc = sum * (-127.5f / 256.0f);
   }
-  __device__ __forceinline__ float dot(const uint4 c, const uint4 m) const {
+  // nm: the complemented dither bytes of the row
+  __device__ __forceinline__ float dot(const uint4 c, const uint4 nm) const {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
+    const uint32_t mw[4] = {nm.x, nm.y, nm.z, nm.w};
     float d = qc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      float t[4];
+      dither_t(cw[i], mw[i], t);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        d = fmaf(qf[4 * i + j], s8(cw[i], j), d);
-        d = fmaf(qn[4 * i + j], u8f(mw[i], j), d);
-      }
+      for (int j = 0; j < 4; ++j) d = fmaf(qt[4 * i + j], t[j], d);
+    }
     return d;
   }
 };
@@ -273,7 +297,7 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
 // FINAL: every (b, h) has a single split (the host plan has nsplit_max ==
 // 1), so the work-group finishes the (b, h) itself and no merge kernel runs.
 template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER>
-__global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
+__global__ SWA_INT8_WAVES_ATTR __launch_bounds__(NW * 64) void decode_int8_kernel(
     const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const int32_t* __restrict__ np,
     const int32_t* __restrict__ table, int64_t num_pages, const uint16_t* __restrict__ q,
@@ -396,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 
   auto step = [&](const Blk (&cur)[UB], int kb0) {
     float s[2 * UB], sv[UB];
-    uint4 dm[2 * UB];  // Tier B dither bytes of rows g and g+8 of each block
+    uint4 dm[2 * UB];  // Tier B complemented dither bytes of rows g and g+8 of each block
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       const int kb = kb0 + ub;
@@ -410,8 +434,9 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
         const int pos = kb * 16 + g + 8 * half;
         float d;
         if constexpr (DITHER) {
-          dm[2 * ub + half] = philox4x32_10(make_uint4((uint32_t)(kbc * 16 + g + 8 * half), (uint32_t)vq,
-                                                       (uint32_t)h, layer), rk0, rk1);
+          const uint4 r = philox4x32_10(make_uint4((uint32_t)(kbc * 16 + g + 8 * half), (uint32_t)vq,
+                                                   (uint32_t)h, layer), rk0, rk1);
+          dm[2 * ub + half] = make_uint4(~r.x, ~r.y, ~r.z, ~r.w);
           d = kd.dot(half ? cur[ub].k1 : cur[ub].k0, dm[2 * ub + half]);
           d = group_sum<8>(d) * sk;
         } else {
@@ -455,19 +480,23 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
         const float pv = p * sv[ub];  // value scale folded into the weight
         const uint4 c = half ? cur[ub].v1 : cur[ub].v0;
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pv, s8(cw[i], j), acc[4 * i + j]);
         if constexpr (DITHER) {
           const uint4 mm = dm[2 * ub + half];
           const uint32_t mw[4] = {mm.x, mm.y, mm.z, mm.w};
-          const float pvn = pv * (-1.0f / 256.0f);
+          const float pvt = pv * (1.0f / 256.0f);
           su += pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float t[4];
+            dither_t(cw[i], mw[i], t);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pvt, t[j], acc[4 * i + j]);
+          }
+        } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pvn, u8f(mw[i], j), acc[4 * i + j]);
+            for (int j = 0; j < 4; ++j) acc[4 * i + j] = fmaf(pv, s8(cw[i], j), acc[4 * i + j]);
         }
       }
     }
@@ -494,9 +523,9 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
   }
 
   if constexpr (DITHER) {
-    // the (255/512) sum p s_V term of every element (code - u = code - m/256 + 255/512)
+    // the -(127.5/256) sum p s_V term of every element (code - u = (t - 127.5)/256)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = fmaf(su, 255.0f / 512.0f, acc[e]);
+    for (int e = 0; e < 16; ++e) acc[e] = fmaf(su, -127.5f / 256.0f, acc[e]);
   }
   // Merge the 8 lane groups of the wave (lanes with equal lane%8 share dims).
   float mw = m;

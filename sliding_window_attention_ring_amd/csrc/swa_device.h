@@ -74,18 +74,24 @@ __device__ __forceinline__ float s8(uint32_t w, int j) {
 // Unsigned byte j of a 32-bit word as fp32 (one byte convert).
 __device__ __forceinline__ float u8f(uint32_t w, int j) { return (float)((w >> (8 * j)) & 0xffu); }
 
+// Signed low / high 16-bit half of a word as fp32.
+__device__ __forceinline__ float s16lo(uint32_t w) { return (float)(int32_t)(int16_t)(w & 0xffffu); }
+__device__ __forceinline__ float s16hi(uint32_t w) { return (float)((int32_t)w >> 16); }
+
 // Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random
 // Numbers: As Easy as 1, 2, 3", SC 2011).  Each round forms the 64-bit
 // products M0*c0 and M1*c2 and maps the counter to
 // (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key
 // then advances by the Weyl constants.  With a wave-uniform key the key
-// schedule stays in scalar registers.
+// schedule stays in scalar registers; each three-way xor is one gfx950
+// three-input bit operation (truth table 0x96).
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96), (uint32_t)p1,
+                   __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96), (uint32_t)p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }

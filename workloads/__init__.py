@@ -16,7 +16,7 @@ from typing import Optional
 class Workload:
     cid: int                 # seed namespace
     name: str
-    kind: str                # "fp32" | "bf16" | "int8"
+    kind: str                # "fp32" | "bf16" | "int8" | "int8_dither"
     B: int
     H: int
     D: int
@@ -58,4 +58,10 @@ BF16_32K_PAGED = Workload(6, "bf16-ctx32768-paged", "bf16", B=16, H=32, D=128, W
                           rope_base=10000.0, prefill_chunk=8192, layout="paged",
                           note="the bf16 32k workload in 16-token pages")
 
-ALL = {w.name: w for w in (TINY, FULL_RAGGED, RING, LONG, INT8_32K, BF16_32K, INT8_32K_PAGED, BF16_32K_PAGED)}
+# Same inputs as the INT8 32k workload, stored with subtractive dither and no witness.
+INT8_DITHER_32K = Workload(5, "int8-dither-ctx32768", "int8_dither", B=16, H=32, D=128, W=32768,
+                           prefill=32768, steps=20, rope_base=10000.0, prefill_chunk=8192,
+                           note="the INT8 32k workload with Philox subtractive dither (Tier B)")
+
+ALL = {w.name: w for w in (TINY, FULL_RAGGED, RING, LONG, INT8_32K, BF16_32K, INT8_32K_PAGED, BF16_32K_PAGED,
+                           INT8_DITHER_32K)}
