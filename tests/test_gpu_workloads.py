@@ -12,8 +12,8 @@ import torch
 import workloads
 from workloads import gen
 from oracle import attention, decoder
-from tests.gpu_util import (assert_close, check_int8_decode, check_int8_store, f64, host_bits,
-                            require_gpu, say)
+from tests.gpu_util import (assert_close, check_dither_decode, check_dither_store, check_int8_decode,
+                            check_int8_store, f64, host_bits, request_ids, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +183,49 @@ def test_int8_witness_ctx32768():
         check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]), c_all[b, h].cpu().numpy(), b, h,
                           f64(q[b, h]), k64, v64, n, wl.W, f"32k step n={n}")
     say("int8 32k steps ok, last n", n)
+
+
+def test_int8_dither_ctx32768():
+    """The INT8 32k inputs stored with subtractive dither (request ids 0..15,
+    layer 0), decoded with delta = 1e-6 as the benchmark does: after the
+    prefill, 2 sampled pairs get the full store check (codes and scales bit
+    for bit against the oracle's own Philox stream) and the decode check;
+    then 20 steps at positions 32768..32787, with the decode of one pair
+    checked at six of them, including both sides of the block commit at
+    32784."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.INT8_DITHER_32K
+    delta = 1e-6
+    dev = torch.device("cuda")
+    total = wl.prefill + wl.steps
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("int8_dither", wl.B, wl.H, wl.D, wl.W)
+    reqs = request_ids(cache)
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(9)
+    n = wl.prefill
+    q = gen.query(wl, n - 1, device=dev)
+    out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q, delta=delta)
+    assert swa.validate(cache) == 0
+    out, cert, tv, gate, qh = out.cpu().numpy(), cert.cpu().numpy(), tv.cpu().numpy(), gate.cpu().numpy(), f64(q)
+    for _ in range(2):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        say("dither 32k store check", b, h)
+        check_dither_store(cache, b, h, k64, v64, n)
+        check_dither_decode(out[b, h], cert[b, h], b, h, qh[b, h], k64, v64, n, wl.W, reqs[b], cache.layer, delta,
+                            tv[b, h], gate[b, h], what="32k")
+    for i in range(wl.steps):
+        swa.kv_append(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous())
+        n += 1
+        q = gen.query(wl, n - 1, device=dev)
+        out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q, delta=delta)
+        assert swa.validate(cache) == 0
+        if i not in (0, 7, 14, 15, 16, 19):
+            continue
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        check_dither_decode(out[b, h].cpu().numpy(), float(cert[b, h]), b, h, f64(q[b, h]), k64, v64, n, wl.W, reqs[b],
+                            cache.layer, delta, float(tv[b, h]), int(gate[b, h]), what=f"32k step n={n}")
+    say("dither 32k steps ok, last n", n)
