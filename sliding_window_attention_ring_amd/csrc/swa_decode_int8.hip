@@ -431,7 +431,9 @@ __global__ SWA_INT8_WAVES_ATTR __launch_bounds__(NW * 64) void decode_int8_kerne
       sv[ub] = cur[ub].sv;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int pos = kb * 16 + g + 8 * half;
+        // kbc, not kb: a past-the-end block index times 16 could pass 2^31
+        // near the position limit; such rows are masked by !live anyway.
+        const int pos = kbc * 16 + g + 8 * half;
         float d;
         if constexpr (DITHER) {
           const uint4 r = philox4x32_10(make_uint4((uint32_t)(kbc * 16 + g + 8 * half), (uint32_t)vq,
@@ -456,7 +458,7 @@ __global__ SWA_INT8_WAVES_ATTR __launch_bounds__(NW * 64) void decode_int8_kerne
         cp = fmaf(nq[2], f16_to_f32((uint16_t)(w.y & 0xffff)), cp);
         cp = fmaf(nq[3], f16_to_f32((uint16_t)(w.y >> 16)), cp);
         cp = group_sum<4>(cp);
-        const int pos = kb * 16 + wt;
+        const int pos = kbc * 16 + wt;
         if (live && pos >= p0) {
           cm = fmaxf(cm, cp);
           if (c_all != nullptr && wq == 0) c_all[bh * W + (int64_t)sbk * 16 + wt] = cp * kBoundPad;

@@ -154,10 +154,13 @@ def request_ids(cache) -> np.ndarray:
     return [int(x) & ((1 << 64) - 1) for x in cache.request_id.cpu().tolist()]
 
 
-def check_dither_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, n: int):
+def check_dither_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, n: int, position0: int = 0,
+                       first_block: int = 0):
     """Tier B cache of (b, h): slot positions, codes and scales of every
     committed block in the ring bit-exact vs the oracle (which draws the same
-    Philox dither itself); staging rows equal the input bits."""
+    Philox dither itself); staging rows equal the input bits.  Row j of the
+    history has position position0 + j (position0 a multiple of W); blocks
+    below first_block are not compared (their codes may predate position0)."""
     req, layer = request_ids(cache)[b], cache.layer
     view = RingView(cache) if getattr(cache, "layout", "ring") == "paged" else cache
     W = cache.W
@@ -168,11 +171,13 @@ def check_dither_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, 
     exp_pos = np.full(W, -1, dtype=np.int64)
     for kb in range(max(0, nb - W // 16), nb):
         rows = np.arange(kb * 16, kb * 16 + 16)
-        u = odither.dither(req, layer, h, rows, k64.shape[-1])
+        exp_pos[(kb * 16) % W:(kb * 16) % W + 16] = rows + position0
+        if kb < first_block:
+            continue
+        u = odither.dither(req, layer, h, rows + position0, k64.shape[-1])
         sk, ck = odither.quantize_block(k64[rows], u)
         sv, cv = odither.quantize_block(v64[rows], u)
         slot0 = (kb * 16) % W
-        exp_pos[slot0:slot0 + 16] = rows
         np.testing.assert_array_equal(kc[slot0:slot0 + 16], ck, err_msg=f"key codes b={b} h={h} block {kb}")
         np.testing.assert_array_equal(vc[slot0:slot0 + 16], cv, err_msg=f"value codes b={b} h={h} block {kb}")
         assert ks[slot0 // 16] == sk and vs[slot0 // 16] == sv, (kb, ks[slot0 // 16], sk)
@@ -184,12 +189,12 @@ def check_dither_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, 
 
 
 def check_dither_decode(out, cert, b, h, q64, k64, v64, n, W, req, layer, delta, tv=None, gate=None,
-                        tau=0.2, what=""):
+                        tau=0.2, what="", position0=0):
     """Tier B decode of (b, h) vs the oracle: output within TOL; the
     certificate equal to the oracle's up to its float32 pad, and (an event of
     probability >= 1 - delta) not below the true largest logit error; tv =
     tanh(cert/2) padded, and gate = tv > tau."""
-    res = odither.int8_dither_decode(q64, k64, v64, n, W, req, layer, h, float(np.float32(delta)))
+    res = odither.int8_dither_decode(q64, k64, v64, n, W, req, layer, h, float(np.float32(delta)), position0)
     err = assert_close(out, res["out"], f"dither out {what} b={b} h={h}")
     ref = res["cert"]
     assert cert >= ref, (what, b, h, cert, ref)

@@ -314,3 +314,19 @@ def test_decode_within_tv_of_exact_attention():
         vmax = float(np.max(np.abs(v[vis]))) + float(np.max(r["v_scales"]))
         bound = 2 * np.tanh(r["cert"] / 2) * vmax + float(np.max(r["v_scales"])) * (0.5 + dither.BETA)
         assert np.max(np.abs(r["out"] - exact)) <= bound
+
+
+def test_position_offset_is_the_same_history_further_on():
+    # Rows at positions P0 + j: with n >= W only the last W rows are visible,
+    # so this equals the history padded with P0 leading rows.
+    rng = np.random.default_rng(12)
+    d, w, p0, n = 128, 64, 48, 100
+    k = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    v = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    q = rng.standard_normal(d)
+    a = dither.int8_dither_decode(q, k, v, n, w, request=5, layer=2, head=1, delta=0.1, position0=p0)
+    pad = np.zeros((p0, d))
+    b = dither.int8_dither_decode(q, np.concatenate([pad, k]), np.concatenate([pad, v]), p0 + n, w, request=5, layer=2,
+                                  head=1, delta=0.1)
+    assert np.array_equal(a["out"], b["out"]) and a["cert"] == b["cert"]
+    assert np.array_equal(a["k_codes"][-w:], b["k_codes"][-w:])
