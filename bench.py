@@ -95,9 +95,27 @@ def step_bytes(wl, n_after):
     return dec, app, vis
 
 
-def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0):
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Threads for the all-cores oracle run: OMP_NUM_THREADS if set (the
+    box's CPU share), else the affinity core count."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return int(env) if env.isdigit() and int(env) > 0 else len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0, threads: int = 1):
     """Time the oracle (as it stands) on a sample of (b, h) pairs of the same
-    workload at next_position n, one thread; GB/s of algorithmic bytes."""
+    workload at next_position n with ``threads`` BLAS/OpenMP threads; GB/s
+    of algorithmic bytes."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import attention, bits, dither as odither, int8 as oint8
@@ -110,7 +128,7 @@ def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0):
     done, t_used, nbytes = 0, 0.0, 0.0
     per_pair, _, _ = step_bytes(wl, n)
     per_pair /= wl.B * wl.H
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         for b, h in pairs:
             kk = bits.to_f64(gen.to_bits(k_all[b, h, :n]))
             vv = bits.to_f64(gen.to_bits(v_all[b, h, :n]))
@@ -130,11 +148,18 @@ def cpu_baseline(wl, k_all, v_all, q_of, n: int, budget_s: float = 12.0):
     return {
         "value": nbytes / t_used / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} (b,h) pairs of {wl.name} at context {vis}, float64 NumPy, 1 thread, "
-                  f"{t_used:.1f} s ({done * vis / t_used:.3g} KV-token-heads/s)",
+        "sample": f"{done} (b,h) pairs of {wl.name} at context {vis}, float64 NumPy, {threads} thread(s) of "
+                  f"{len(os.sched_getaffinity(0))} affinity cores ({cpu_model()}), {t_used:.1f} s "
+                  f"({done * vis / t_used:.3g} KV-token-heads/s)",
     }
+
+
+def device_info(torch) -> dict:
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / (1 << 30), 1)}
 
 
 def main():
@@ -146,6 +171,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=INT8_32K.name, choices=sorted(ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
+                    help="write a 512 MiB scratch buffer before each timed step so no K/V bytes are served from "
+                         "the 256 MB MALL or L2; auto = on when a step reads under 2 GiB")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -220,24 +248,34 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # per step: start, after append, after decode
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     dec_bytes = app_bytes = vis_tokens = 0.0
     for i in range(args.steps):
         done = args.warmup + i + 1
         d, a, vis = step_bytes(wl, prefill + done if lens is None else [int(n) + done for n in lens])
         dec_bytes, app_bytes, vis_tokens = dec_bytes + d, app_bytes + a, vis_tokens + vis
+    flush = args.flush == "on" or (args.flush == "auto" and dec_bytes / args.steps < 2 * (1 << 30))
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         j = args.warmup + i
-        swa.kv_append(cache, ks[j], vs[j])
+        if flush:
+            scratch.fill_(i & 0xFF)
         evs[i][0].record(stream)
-        decode(qs[j])
+        swa.kv_append(cache, ks[j], vs[j])
         evs[i][1].record(stream)
+        decode(qs[j])
+        evs[i][2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    dec_ms = sorted(e1.elapsed_time(e2) for _, e1, e2 in evs)
+    kern_ms = sum(dec_ms) / args.steps
+    kern_median = dec_ms[args.steps // 2] if args.steps % 2 else 0.5 * (dec_ms[args.steps // 2 - 1] + dec_ms[args.steps // 2])
+    if flush:
+        # the flush writes are not part of the step: time the steps by their events
+        elapsed = sum(e0.elapsed_time(e2) for e0, _, e2 in evs) * 1e-3
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = (dec_bytes + app_bytes) / elapsed / 1e9
@@ -258,7 +296,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "head_dim": wl.D, "window": wl.W,
                    "context": min(wl.W, prefill) if lens is None else [int(n) for n in lens],
-                   "kv_dtype": wl.kind, "layout": wl.layout,
+                   "kv_dtype": wl.kind, "layout": wl.layout, "cache_flush": flush,
                    "positions": [prefill + args.warmup, prefill + n_steps - 1],
                    "step": "kv_append(T=1) + " + {"int8": "decode_attn_int8_witness",
                                                   "int8_dither": "decode_attn_int8_dither (cert, tv, gate; "
@@ -275,13 +313,19 @@ def main():
             "traffic": read_traffic(wl.name, wl.kind),
             "kernel": "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel",
             "kernel_ms": round(kern_ms, 4),
+            "kernel_ms_median": round(kern_median, 4),
             "algorithmic_bytes_per_launch": dec_bytes / args.steps,
         },
         "cpu_baseline": None,
+        "cpu_baseline_all_cores": None,
+        "device": device_info(torch),
     }
     if not args.no_cpu_baseline and lens is None:
-        log("[bench] timing the CPU oracle on a sample ...")
-        result["cpu_baseline"] = cpu_baseline(wl, k_all, v_all, lambda p: gen.query(wl, p), prefill)
+        log("[bench] timing the CPU oracle on a sample (1 thread, then all cores) ...")
+        q_of = lambda p: gen.query(wl, p)  # noqa: E731
+        result["cpu_baseline"] = cpu_baseline(wl, k_all, v_all, q_of, prefill)
+        result["cpu_baseline_all_cores"] = cpu_baseline(wl, k_all, v_all, q_of, prefill, budget_s=8.0,
+                                                        threads=host_threads())
     print(json.dumps(result), flush=True)
 
 
