@@ -70,20 +70,27 @@ int check_cache(const swa_cache* c) {
 // pairs still get one split per pair (512 work-groups at B*H = 512).
 // Measured on MI355X, fewer and longer splits stream HBM better than many
 // short ones: each split pays a query load, its pipeline fill and a partial
-// write, and the merge reads every partial.  SWA_TARGET_WGS overrides it;
-// read once per process so workspace sizes stay consistent.
-int target_wgs() {
-  static int v = [] {
+// write, and the merge reads every partial.  The dithered INT8 decode is the
+// exception: it carries about 1.5x the VALU work per byte of the witness
+// decode, and 8 work-groups per CU (more waves to interleave ALU and loads)
+// ran it 1.7% faster on MI355X.  SWA_TARGET_WGS overrides the target for
+// every kind; it is read once per process so workspace sizes stay
+// consistent.
+int target_wgs(int kind) {
+  static int env = [] {
     const char* s = getenv("SWA_TARGET_WGS");
-    int x = s ? atoi(s) : 0;
-    if (x > 0) return x;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    return cus;
+    const int x = s ? atoi(s) : 0;
+    return x > 0 ? x : 0;
   }();
-  return v;
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  if (env > 0) return env;
+  return kind == SWA_KV_INT8_DITHER ? 8 * cus : cus;
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -140,7 +147,7 @@ unsigned grid_for(int64_t n, int threads, int64_t cap) {
 
 SplitPlan plan_decode(const swa_cache& c) {
   SplitPlan p;
-  const int64_t tgt = target_wgs();
+  const int64_t tgt = target_wgs(c.kind);
   if (is_int8(c.kind)) {
     const int64_t rb = decode_int8_round_blocks();
     const int64_t wb = c.W / 16;

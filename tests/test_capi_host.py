@@ -89,7 +89,7 @@ def test_argument_checks_return_codes():
     # Tier B kind: no witness needed, request ids required, delta in (0, 1]
     dz = desc(kind=3, witness=None, request_id=0xD0000)
     nz = L.swa_workspace_bytes(p(dz))
-    assert nz == L.swa_workspace_bytes(p(desc(kind=2)))
+    assert nz > 0 and nz % (2 * 4 * (128 + 4) * 4) == 0  # B*H*nsplit*(D+4) floats
     assert L.kv_append(p(dz), A16, A16, 0, None) == 0
     assert L.kv_append(p(desc(kind=3, request_id=None)), A16, A16, 1, None) == -2
     assert L.kv_append(p(desc(kind=3, request_id=0xD0004)), A16, A16, 1, None) == -3
