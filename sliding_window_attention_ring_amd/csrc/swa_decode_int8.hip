@@ -63,16 +63,6 @@ namespace {
 #ifndef SWA_INT8_KDOT_F16
 #define SWA_INT8_KDOT_F16 0
 #endif
-// Nonzero: ask the compiler for at least this many waves per SIMD (caps the
-// registers per lane at 512 / waves).
-#ifndef SWA_INT8_WAVES
-#define SWA_INT8_WAVES 0
-#endif
-#if SWA_INT8_WAVES
-#define SWA_INT8_WAVES_ATTR __attribute__((amdgpu_waves_per_eu(SWA_INT8_WAVES)))
-#else
-#define SWA_INT8_WAVES_ATTR
-#endif
 
 constexpr int D = 128;
 constexpr int PF = D + 4;          // m, l, cmax, pad, acc[D]
@@ -297,7 +287,7 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
 // FINAL: every (b, h) has a single split (the host plan has nsplit_max ==
 // 1), so the work-group finishes the (b, h) itself and no merge kernel runs.
 template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER>
-__global__ SWA_INT8_WAVES_ATTR __launch_bounds__(NW * 64) void decode_int8_kernel(
+__global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     const int8_t* __restrict__ Kc, const int8_t* __restrict__ Vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, const uint16_t* __restrict__ wit, const int32_t* __restrict__ np,
     const int32_t* __restrict__ table, int64_t num_pages, const uint16_t* __restrict__ q,
@@ -387,12 +377,23 @@ __global__ SWA_INT8_WAVES_ATTR __launch_bounds__(NW * 64) void decode_int8_kerne
   };
 
   auto load = [&](Blk (&bk)[UB], int kb0) {
+    // Paged: all page ids first.  Their LDS reads share a wait counter with
+    // the scalar loads of the block scales, so reading them before any scale
+    // load keeps the address of the next block from waiting on a scale.
+    int64_t pis[UB];
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int ub = 0; ub < UB; ++ub) {
+        const int kb = kb0 + ub < bhi ? kb0 + ub : bhi - 1;
+        pis[ub] = block_page(kb) * H + h;  // (page, head) index
+      }
+    }
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       int kb = kb0 + ub;
       kb = kb < bhi ? kb : bhi - 1;  // past the end: re-read a live block, masked below
       if constexpr (PAGED) {
-        const int64_t pi = block_page(kb) * H + h;  // (page, head) index
+        const int64_t pi = pis[ub];
         const char* kp = reinterpret_cast<const char*>(Kc) + pi * (16 * D);
         const char* vp = reinterpret_cast<const char*>(Vc) + pi * (16 * D);
         const char* wp = reinterpret_cast<const char*>(wit) + pi * (16 * 32);
