@@ -248,7 +248,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    # per step: start, after append, after decode
+    # per step: start (flushed runs only), after append, after decode
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     dec_bytes = app_bytes = vis_tokens = 0.0
     for i in range(args.steps):
@@ -263,7 +263,7 @@ def main():
         j = args.warmup + i
         if flush:
             scratch.fill_(i & 0xFF)
-        evs[i][0].record(stream)
+            evs[i][0].record(stream)  # only needed to time a flushed step; each marker costs queue latency
         swa.kv_append(cache, ks[j], vs[j])
         evs[i][1].record(stream)
         decode(qs[j])
