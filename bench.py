@@ -42,7 +42,8 @@ def log(*a):
 
 
 def kernel_source_hash(kind: str) -> str:
-    files = ["swa_device.h", "swa_decode_int8.hip" if kind.startswith("int8") else "swa_decode.hip"]
+    files = (["swa_device.h", "swa_commit.h", "swa_decode_int8.hip"] if kind.startswith("int8")
+             else ["swa_device.h", "swa_decode.hip"])
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -171,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=INT8_32K.name, choices=sorted(ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="INT8 kinds: time kv_append + the decode call instead of the one decode_step_int8 call")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="write a 512 MiB scratch buffer before each timed step so no K/V bytes are served from "
                          "the 256 MB MALL or L2; auto = on when a step reads under 2 GiB")
@@ -239,9 +242,21 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # INT8 kinds: one call per step (kv_append of the token and the decode,
+    # fused into one launch when the plan has one split per (b, h)).
+    fuse = wl.kind in ("int8", "int8_dither") and not args.no_fuse
+    dither = wl.kind == "int8_dither"
+
+    def fused(i):
+        swa.decode_step_int8(cache, ks[i], vs[i], qs[i], tau=0.2, delta=DITHER_DELTA, out=out, cmax=cmax,
+                             tv=tv if dither else None, gate=gate if dither else None, ws=ws)
+
     def step(i):
-        swa.kv_append(cache, ks[i], vs[i])
-        decode(qs[i])
+        if fuse:
+            fused(i)
+        else:
+            swa.kv_append(cache, ks[i], vs[i])
+            decode(qs[i])
 
     for i in range(args.warmup):
         step(i)
@@ -264,9 +279,13 @@ def main():
         if flush:
             scratch.fill_(i & 0xFF)
             evs[i][0].record(stream)  # only needed to time a flushed step; each marker costs queue latency
-        swa.kv_append(cache, ks[j], vs[j])
-        evs[i][1].record(stream)
-        decode(qs[j])
+        if fuse:
+            evs[i][1].record(stream)
+            fused(j)
+        else:
+            swa.kv_append(cache, ks[j], vs[j])
+            evs[i][1].record(stream)
+            decode(qs[j])
         evs[i][2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -279,7 +298,9 @@ def main():
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = (dec_bytes + app_bytes) / elapsed / 1e9
-    achieved = (dec_bytes / args.steps) / (kern_ms * 1e-3) / 1e9
+    # the timed call: the decode, or with fuse the whole step (append included)
+    timed_bytes = (dec_bytes + app_bytes) if fuse else dec_bytes
+    achieved = (timed_bytes / args.steps) / (kern_ms * 1e-3) / 1e9
     BH = wl.B * wl.H
     result = {
         "metric": METRIC,
@@ -298,9 +319,11 @@ def main():
                    "context": min(wl.W, prefill) if lens is None else [int(n) for n in lens],
                    "kv_dtype": wl.kind, "layout": wl.layout, "cache_flush": flush,
                    "positions": [prefill + args.warmup, prefill + n_steps - 1],
-                   "step": "kv_append(T=1) + " + {"int8": "decode_attn_int8_witness",
-                                                  "int8_dither": "decode_attn_int8_dither (cert, tv, gate; "
-                                                                 f"delta={DITHER_DELTA})"}.get(wl.kind, "decode_attn")},
+                   "step": ("decode_step_int8 (kv_append of one token + the decode, one call; "
+                            + ("cert, tv, gate, delta=%g)" % DITHER_DELTA if dither else "witness bound)")) if fuse
+                   else "kv_append(T=1) + " + {"int8": "decode_attn_int8_witness",
+                                               "int8_dither": "decode_attn_int8_dither (cert, tv, gate; "
+                                                              f"delta={DITHER_DELTA})"}.get(wl.kind, "decode_attn")},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "kv_token_heads_per_s": vis_tokens * wl.H / elapsed,
         "query_token_heads_per_s": BH * args.steps / elapsed,
@@ -311,10 +334,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": read_traffic(wl.name, wl.kind),
-            "kernel": "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel",
+            "kernel": ("decode_step_int8 call" if fuse else
+                       "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel"),
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_median": round(kern_median, 4),
-            "algorithmic_bytes_per_launch": dec_bytes / args.steps,
+            "algorithmic_bytes_per_launch": timed_bytes / args.steps,
         },
         "cpu_baseline": None,
         "cpu_baseline_all_cores": None,

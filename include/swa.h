@@ -210,12 +210,41 @@ int decode_attn_int8_witness_tv(const swa_cache *c, const void *q, float *out, f
 int decode_attn_int8_dither(const swa_cache *c, const void *q, float *out, float *cert, float *tv,
                             int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes the decode entry points need for this cache shape (the
- * split partials: B*H*nsplit*(D+4) floats).  0 for an invalid descriptor. */
+/* One decode step in one call: kv_append of one token per sequence, then
+ * the INT8 decode of that sequence's query (airsota.com §三: write at the
+ * current position, then attend; WitCert, section SGLang 生产级落地: one
+ * fused pass per step).  INT8 kinds only.  The result is bit for bit that
+ * of kv_append(c, k_new, v_new, 1) followed by decode_attn_int8_witness_tv
+ * (INT8) or decode_attn_int8_dither (INT8_DITHER) with the same arguments.
+ * When the decode plan has one split per (b, h) this is one kernel launch:
+ * each (b, h) work-group appends its own token, quantizing the block it
+ * completes, then decodes; the last of the H work-groups of a sequence
+ * advances next_position.  Otherwise it is the two ordinary launches.
+ *  k_new, v_new  [B][H][1][D] bf16
+ *  q, out, cmax, tv, gate, tau  as for decode_attn_int8_witness_tv; cmax is
+ *                the certificate for INT8_DITHER
+ *  delta         INT8_DITHER failure budget, in (0, 1]; ignored for INT8
+ *  ws            the decode workspace; its B per-sequence counters (after
+ *                the split partials) must be zero before the first call --
+ *                swa_workspace_init does that -- and every call leaves them
+ *                zero.  Calls sharing a workspace must be ordered on one
+ *                stream.
+ * Errors: descriptor errors, SWA_EUNSUPPORTED for a non-INT8 kind,
+ * SWA_ENULL, SWA_EALIGN, SWA_EINVAL (NaN tau; delta outside (0, 1] for
+ * INT8_DITHER), SWA_EWORKSPACE, SWA_EHIP. */
+int decode_step_int8(const swa_cache *c, const void *k_new, const void *v_new, const void *q, float *out,
+                     float *cmax, float *tv, int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Workspace bytes the decode entry points need for this cache shape: the
+ * split partials (B*H*nsplit*(D+4) floats) padded to 256 bytes, then B
+ * int32 counters for decode_step_int8, padded to 256 bytes.  0 for an
+ * invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);
 
-/* Zero-fill a workspace (optional: the decode entry points overwrite what
- * they read).  Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
+/* Zero-fill a workspace.  The decode entry points overwrite the partials
+ * they read; decode_step_int8 needs its counters zero before its first call.
+ * Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
 int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Prefix reuse (huhohoo.com, sections 哪些東西必須一起裁剪 and

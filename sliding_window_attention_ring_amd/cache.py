@@ -273,6 +273,37 @@ def decode_attn_int8_dither(cache, q: torch.Tensor, delta: float, tau: float = 0
     return out, cert, tv, gate
 
 
+def decode_step_int8(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, tau: float = 0.2,
+                     delta: float = 1e-6, want_tv: bool = False, out: Optional[torch.Tensor] = None,
+                     cmax: Optional[torch.Tensor] = None, tv: Optional[torch.Tensor] = None,
+                     gate: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """``decode_step_int8``: append one token per sequence ([B, H, 1, D] bf16) and decode ``q``
+    in one call (INT8 kinds).  Returns (out [B,H,D], cmax [B,H], tv, gate); tv and gate are None
+    unless ``want_tv`` or passed in.  ``cmax`` is the certificate for "int8_dither"."""
+    shape = (cache.B, cache.H, 1, cache.D)
+    _need(k_new, shape, torch.bfloat16, "k_new")
+    _need(v_new, shape, torch.bfloat16, "v_new")
+    _need(q, (cache.B, cache.H, cache.D), torch.bfloat16, "q")
+    dev = q.device
+    BH = (cache.B, cache.H)
+    out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=dev) if out is None else out
+    cmax = torch.empty(BH, dtype=torch.float32, device=dev) if cmax is None else cmax
+    if want_tv:
+        tv = torch.empty(BH, dtype=torch.float32, device=dev) if tv is None else tv
+        gate = torch.empty(BH, dtype=torch.int32, device=dev) if gate is None else gate
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    _need(cmax, BH, torch.float32, "cmax")
+    if tv is not None:
+        _need(tv, BH, torch.float32, "tv")
+    if gate is not None:
+        _need(gate, BH, torch.int32, "gate")
+    ws = cache.workspace() if ws is None else ws
+    check(lib().decode_step_int8(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(cmax),
+                                 _ptr(tv), _ptr(gate), float(tau), float(delta), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "decode_step_int8")
+    return out, cmax, tv, gate
+
+
 def kv_truncate(cache, cut: torch.Tensor, stream=None) -> torch.Tensor:
     """``kv_truncate``: returns ok [B] int32 (1 truncated, 0 must recompute)."""
     _need(cut, (cache.B,), torch.int32, "cut")

@@ -211,8 +211,7 @@ const char* swa_status_string(int status) {
 
 size_t swa_workspace_bytes(const swa_cache* c) {
   if (check_cache(c) != SWA_OK) return 0;
-  const SplitPlan p = plan_decode(*c);
-  return (size_t)c->B * c->H * (size_t)p.nsplit_max * partial_floats(c->D) * sizeof(float);
+  return workspace_bytes_for(*c, plan_decode(*c));
 }
 
 int swa_cache_reset(const swa_cache* c, void* stream) {
@@ -294,6 +293,28 @@ int decode_attn_int8_dither(const swa_cache* c, const void* q, float* out, float
 int decode_attn_int8_witness(const swa_cache* c, const void* q, float* out, float* cmax, float* c_all,
                              void* ws, size_t ws_bytes, void* stream) {
   return decode_attn_int8_witness_tv(c, q, out, cmax, nullptr, nullptr, 0.f, c_all, ws, ws_bytes, stream);
+}
+
+int decode_step_int8(const swa_cache* c, const void* k_new, const void* v_new, const void* q, float* out,
+                     float* cmax, float* tv, int32_t* gate, float tau, float delta, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (!is_int8(c->kind)) return SWA_EUNSUPPORTED;
+  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || cmax == nullptr || ws == nullptr)
+    return SWA_ENULL;
+  if (gate != nullptr && tv == nullptr) return SWA_ENULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) || !aligned16(ws))
+    return SWA_EALIGN;
+  if (((uintptr_t)cmax & 3u) || ((uintptr_t)tv & 3u) || ((uintptr_t)gate & 3u)) return SWA_EALIGN;
+  if (!(tau == tau)) return SWA_EINVAL;
+  if (c->kind == SWA_KV_INT8_DITHER && !(delta > 0.f && delta <= 1.f)) return SWA_EINVAL;
+  if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
+  const SplitPlan p = plan_decode(*c);
+  return launch_decode_step_int8(*c, k_new, v_new, q, out, cmax, tv, gate, tau,
+                                 c->kind == SWA_KV_INT8_DITHER ? delta : 1.0f, ws, p, (hipStream_t)stream) == hipSuccess
+             ? SWA_OK
+             : SWA_EHIP;
 }
 
 int kv_truncate(const swa_cache* c, const int32_t* cut, int32_t* ok, void* stream) {

@@ -43,6 +43,25 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
                               float* c_all, float* tv, int32_t* gate, float tau, float delta, void* ws,
                               const SplitPlan& plan, hipStream_t s);
 
+// One decode step (kv_append of one token, then the INT8 decode) in one
+// launch when the plan has a single split per (b, h), else the two launches.
+hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
+                                   float* out, float* cmax, float* tv, int32_t* gate, float tau, float delta,
+                                   void* ws, const SplitPlan& plan, hipStream_t s);
+
+// Workspace layout: split partials (B*H*nsplit_max*(D+4) floats), padded to
+// 256 bytes, then B int32 counters of the fused step (zero between calls).
+inline size_t partials_bytes(const swa_cache& c, const SplitPlan& p) {
+  const size_t b = (size_t)c.B * c.H * (size_t)p.nsplit_max * partial_floats(c.D) * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+inline size_t workspace_bytes_for(const swa_cache& c, const SplitPlan& p) {
+  return partials_bytes(c, p) + ((size_t)c.B * sizeof(int32_t) + 255) / 256 * 256;
+}
+inline int32_t* step_counters(const swa_cache& c, const SplitPlan& p, void* ws) {
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + partials_bytes(c, p));
+}
+
 hipError_t launch_reset(const swa_cache& c, hipStream_t s);
 hipError_t launch_truncate(const swa_cache& c, const int32_t* cut, int32_t* ok, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -89,7 +89,7 @@ def test_argument_checks_return_codes():
     # Tier B kind: no witness needed, request ids required, delta in (0, 1]
     dz = desc(kind=3, witness=None, request_id=0xD0000)
     nz = L.swa_workspace_bytes(p(dz))
-    assert nz > 0 and nz % (2 * 4 * (128 + 4) * 4) == 0  # B*H*nsplit*(D+4) floats
+    assert nz > 0 and nz % 256 == 0  # partials and step counters, each padded to 256 bytes
     assert L.kv_append(p(dz), A16, A16, 0, None) == 0
     assert L.kv_append(p(desc(kind=3, request_id=None)), A16, A16, 1, None) == -2
     assert L.kv_append(p(desc(kind=3, request_id=0xD0004)), A16, A16, 1, None) == -3
@@ -105,6 +105,14 @@ def test_argument_checks_return_codes():
     assert dd(p(i8), A16, A16, A16, None, None, 0.2, 0.1, ws, nz, None) == -4      # Tier A cache
     assert L.decode_attn_int8_witness(p(dz), A16, A16, A16, None, ws, nz, None) == -4
     assert L.decode_attn(p(dz), A16, A16, ws, nz, None) == -4
+    st = L.decode_step_int8
+    assert st(p(d), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, need, None) == -4     # bf16 cache
+    assert st(p(i8), None, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, 1 << 30, None) == -2
+    assert st(p(i8), ODD, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, 1 << 30, None) == -3
+    assert st(p(i8), A16, A16, A16, A16, A16, None, A16, 0.2, 0.1, ws, 1 << 30, None) == -2   # gate without tv
+    assert st(p(i8), A16, A16, A16, A16, A16, None, None, float("nan"), 0.1, ws, 1 << 30, None) == -1
+    assert st(p(dz), A16, A16, A16, A16, A16, None, None, 0.2, 0.0, ws, nz, None) == -1       # Tier B delta
+    assert st(p(dz), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, nz - 1, None) == -5
     assert L.swa_validate(p(d), None, None) == -2
     assert L.swa_workspace_init(None, 64, None) == -2
     assert L.swa_workspace_init(ODD, 64, None) == -3
@@ -112,7 +120,8 @@ def test_argument_checks_return_codes():
 
 
 def test_workspace_size_follows_split_plan():
-    """Workspace = B*H*nsplit*(D+4) floats of split partials."""
+    """Workspace = B*H*nsplit*(D+4) floats of split partials, padded to 256
+    bytes, then B int32 step counters, padded to 256 bytes."""
     from sliding_window_attention_ring_amd._capi import lib
     L = lib()
     for kw in [dict(kind=0, B=16, H=32, D=128, W=32768), dict(kind=2, B=16, H=32, D=128, W=32768),
@@ -120,4 +129,7 @@ def test_workspace_size_follows_split_plan():
         d = desc(**kw)
         nb = L.swa_workspace_bytes(ctypes.byref(d))
         per = kw["B"] * kw["H"] * (kw["D"] + 4) * 4
-        assert nb % per == 0 and nb // per >= 1
+        counters = (kw["B"] * 4 + 255) // 256 * 256
+        assert nb % 256 == 0 and nb > counters
+        partials = nb - counters
+        assert any((ns * per + 255) // 256 * 256 == partials for ns in range(1, kw["W"] + 1))

@@ -1,0 +1,149 @@
+"""The fused decode step (decode_step_int8): one token appended per
+sequence and the INT8 decode, in one launch when the plan has one split per
+(b, h).
+
+Its result must be bit for bit that of kv_append(T=1) followed by the
+separate decode (decode_attn_int8_witness_tv, or decode_attn_int8_dither):
+every output, bound, TV value and gate, and the whole cache state (codes,
+scales, witness, staging rows, slot positions, next_position), after every
+step, on twin caches.  Ragged prefills make different sequences complete
+their blocks at different steps; the steps wrap the ring.  Shapes with
+B*H at or above the split target take the fused launch (one work-group per
+CU for INT8, eight for the dithered kind); a long-window shape takes the
+two-launch fallback.  A few decodes are also checked against the oracle,
+and a graph-captured step is replayed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import check_int8_decode, check_int8_store, f64, host_bits, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def state(c):
+    names = ["k", "v", "k_scale", "v_scale", "k_stage", "v_stage", "pos", "next_position"]
+    if c.kind == "int8":
+        names.append("witness")
+    return {n: host_bits(getattr(c, n)).copy() for n in names}
+
+
+def twins(kind, B, H, W, layout, lens, seed):
+    import sliding_window_attention_ring_amd as swa
+    g = torch.Generator().manual_seed(seed)
+    N = max(lens) + 64
+    k = torch.randn((B, H, N, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, N, 128), generator=g).to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache(kind, B, H, 128, W, layout=layout)
+        # rows never written would hold different garbage in the twins: start
+        # from zeros, so a stray write by either path still shows
+        for name in ("k", "v", "k_scale", "v_scale", "witness", "k_stage", "v_stage"):
+            if getattr(c, name) is not None:
+                getattr(c, name).zero_()
+        for b, n in enumerate(lens):
+            if n:
+                swa.kv_append(c.seq_view(b), k[b:b + 1, :, :n].contiguous().cuda(), v[b:b + 1, :, :n].contiguous().cuda())
+        caches.append(c)
+    return caches, k, v, g
+
+
+def separate(swa, c, kn, vn, q, tau, delta):
+    swa.kv_append(c, kn, vn)
+    if c.kind == "int8":
+        out, cmax, tv, gate, _ = swa.decode_attn_int8_witness_tv(c, q, tau=tau)
+    else:
+        out, cmax, tv, gate = swa.decode_attn_int8_dither(c, q, delta=delta, tau=tau)
+    return out, cmax, tv, gate
+
+
+@pytest.mark.parametrize("kind,B,H,W,layout", [("int8", 4, 64, 64, "ring"), ("int8", 4, 64, 64, "paged"),
+                                               ("int8_dither", 32, 64, 64, "ring"),
+                                               ("int8_dither", 32, 64, 64, "paged"),
+                                               ("int8", 1, 2, 2048, "ring")])
+def test_fused_step_equals_append_then_decode(kind, B, H, W, layout):
+    import sliding_window_attention_ring_amd as swa
+    say("fused step", kind, B, H, W, layout)
+    rng = np.random.default_rng(B * H + W)
+    lens = [int(x) for x in rng.integers(0, 3 * W, size=B)]
+    lens[0] = 13  # one sequence completes its first block at step 3
+    (cf, cs), k, v, g = twins(kind, B, H, W, layout, lens, seed=B + W)
+    tau, delta = 0.2, 1e-3
+    for i in range(40):
+        pos = [n + i for n in lens]
+        kn = torch.stack([k[b, :, p:p + 1] for b, p in enumerate(pos)]).contiguous().cuda()
+        vn = torch.stack([v[b, :, p:p + 1] for b, p in enumerate(pos)]).contiguous().cuda()
+        q = torch.randn((B, H, 128), generator=g).to(torch.bfloat16).cuda()
+        fo = swa.decode_step_int8(cf, kn, vn, q, tau=tau, delta=delta, want_tv=True)
+        so = separate(swa, cs, kn, vn, q, tau, delta)
+        for a, b_, name in zip(fo, so, ("out", "cmax", "tv", "gate")):
+            assert torch.equal(a, b_), f"step {i}: {name} differs"
+        sf, ss = state(cf), state(cs)
+        for name in sf:
+            np.testing.assert_array_equal(sf[name], ss[name], err_msg=f"step {i}: {name} differs")
+        assert host_bits(cf.next_position).tolist() == [n + 1 for n in pos]
+    assert swa.validate(cf) == 0
+    if kind == "int8":  # the fused path's state and output against the oracle too
+        n_after = [n + 40 for n in lens]
+        for b in range(min(B, 2)):
+            hist_k = f64(k[b, :, :n_after[b]])
+            hist_v = f64(v[b, :, :n_after[b]])
+            q64 = f64(q.cpu())
+            check_int8_store(cf, b, 0, hist_k[0], hist_v[0], n_after[b])
+            check_int8_decode(fo[0][b, 0].cpu().numpy(), float(fo[1][b, 0]), None, b, 0, q64[b, 0], hist_k[0],
+                              hist_v[0], n_after[b], W, what="fused step")
+
+
+def test_fused_step_headline_shape_and_graph():
+    """B=16, H=32, W=32768 INT8 (one split per (b, h)): a captured fused
+    step replayed over 20 tokens, crossing a block commit, equals the eager
+    two-launch step on a twin cache each time."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, W, steps, prefill = 16, 32, 32768, 20, 32768 - 7
+    g = torch.Generator(device="cuda").manual_seed(5)
+    k = torch.randn((B, H, prefill + steps, 128), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, prefill + steps, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qs = torch.randn((steps, B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache("int8", B, H, 128, W)
+        c.k_stage.zero_(); c.v_stage.zero_()
+        for c0 in range(0, prefill, 8192):
+            c1 = min(prefill, c0 + 8192)
+            swa.kv_append(c, k[:, :, c0:c1].contiguous(), v[:, :, c0:c1].contiguous())
+        caches.append(c)
+    cg, ce = caches
+    sk = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    sv = torch.empty_like(sk)
+    sq = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    cmax = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = cg.workspace()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        swa.decode_step_int8(cg, sk, sv, sq, out=out, cmax=cmax, ws=ws)
+    torch.cuda.synchronize()
+    assert int(cg.next_position[0]) == prefill  # capture does not run the step
+    for i in range(steps):
+        p = prefill + i
+        sk.copy_(k[:, :, p:p + 1]); sv.copy_(v[:, :, p:p + 1]); sq.copy_(qs[i])
+        graph.replay()
+        swa.kv_append(ce, k[:, :, p:p + 1].contiguous(), v[:, :, p:p + 1].contiguous())
+        oe, ce_max, _ = swa.decode_attn_int8_witness(ce, qs[i])
+        torch.cuda.synchronize()
+        assert torch.equal(out, oe) and torch.equal(cmax, ce_max), f"replay {i}"
+        assert torch.equal(cg.next_position, ce.next_position)
+        if i % 8 == 7 or p % 16 == 15:
+            for name in ("k_stage", "v_stage", "pos", "k_scale"):
+                assert torch.equal(getattr(cg, name), getattr(ce, name)), (i, name)
+    assert int(cg.next_position[0]) == prefill + steps
+    assert swa.validate(cg) == 0
