@@ -176,3 +176,31 @@ def test_int8_empty_and_short_sequences(W):
         for h in range(H):
             check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, q64[b, h], k64[b, h], v64[b, h], lens[b], W,
                               what=f"W={W}")
+
+
+def test_int8_forced_corruption_is_detected():
+    """Failure detection forced from the host: zeroed witnesses make the
+    kernel report cmax = 0, and the per-token soundness check rejects it;
+    a block's key scale forced up moves the output away from the oracle and
+    the parity check rejects that."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, D, W, n = 1, 2, 128, 64, 90
+    g = torch.Generator().manual_seed(23)
+    k = torch.randn((B, H, n, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, n, D), generator=g).to(torch.bfloat16)
+    q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+    k64, v64, q64 = f64(k), f64(v), f64(q)
+    cache = swa.KVCache("int8", B, H, D, W)
+    swa.kv_append(cache, k.cuda(), v.cuda())
+    out, cmax, _ = swa.decode_attn_int8_witness(cache, q.cuda())
+    check_int8_decode(out[0, 0].cpu().numpy(), float(cmax[0, 0]), None, 0, 0, q64[0, 0], k64[0, 0], v64[0, 0], n, W)
+    cache.witness.zero_()
+    out, cmax, _ = swa.decode_attn_int8_witness(cache, q.cuda())
+    assert float(cmax.abs().max()) == 0.0
+    with pytest.raises(AssertionError):
+        check_int8_decode(out[0, 0].cpu().numpy(), float(cmax[0, 0]), None, 0, 0, q64[0, 0], k64[0, 0],
+                          v64[0, 0], n, W)
+    cache.k_scale[0, 0, 2] *= 4  # block of positions 32..47: visible
+    out, cmax, _ = swa.decode_attn_int8_witness(cache, q.cuda())
+    with pytest.raises(AssertionError):
+        check_int8_decode(out[0, 0].cpu().numpy(), 1e30, None, 0, 0, q64[0, 0], k64[0, 0], v64[0, 0], n, W)
