@@ -173,7 +173,7 @@ def main():
     ap.add_argument("--workload", default=INT8_32K.name, choices=sorted(ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fuse", action="store_true",
-                    help="INT8 kinds: time kv_append + the decode call instead of the one decode_step_int8 call")
+                    help="time kv_append + the decode call instead of the one decode_step / decode_step_int8 call")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="write a 512 MiB scratch buffer before each timed step so no K/V bytes are served from "
                          "the 256 MB MALL or L2; auto = on when a step reads under 2 GiB")
@@ -242,14 +242,17 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # INT8 kinds: one call per step (kv_append of the token and the decode,
-    # fused into one launch when the plan has one split per (b, h)).
-    fuse = wl.kind in ("int8", "int8_dither") and not args.no_fuse
+    # One call per step: kv_append of the token and the decode, fused into
+    # one launch when the plan has one split per (b, h).
+    fuse = not args.no_fuse
     dither = wl.kind == "int8_dither"
 
     def fused(i):
-        swa.decode_step_int8(cache, ks[i], vs[i], qs[i], tau=0.2, delta=DITHER_DELTA, out=out, cmax=cmax,
-                             tv=tv if dither else None, gate=gate if dither else None, ws=ws)
+        if wl.kind in ("int8", "int8_dither"):
+            swa.decode_step_int8(cache, ks[i], vs[i], qs[i], tau=0.2, delta=DITHER_DELTA, out=out, cmax=cmax,
+                                 tv=tv if dither else None, gate=gate if dither else None, ws=ws)
+        else:
+            swa.decode_step(cache, ks[i], vs[i], qs[i], out=out, ws=ws)
 
     def step(i):
         if fuse:
@@ -319,7 +322,8 @@ def main():
                    "context": min(wl.W, prefill) if lens is None else [int(n) for n in lens],
                    "kv_dtype": wl.kind, "layout": wl.layout, "cache_flush": flush,
                    "positions": [prefill + args.warmup, prefill + n_steps - 1],
-                   "step": ("decode_step_int8 (kv_append of one token + the decode, one call; "
+                   "step": ("decode_step (kv_append of one token + decode_attn, one call)" if wl.kind in ("bf16", "fp32")
+                            else "decode_step_int8 (kv_append of one token + the decode, one call; "
                             + ("cert, tv, gate, delta=%g)" % DITHER_DELTA if dither else "witness bound)")) if fuse
                    else "kv_append(T=1) + " + {"int8": "decode_attn_int8_witness",
                                                "int8_dither": "decode_attn_int8_dither (cert, tv, gate; "
@@ -334,7 +338,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": read_traffic(wl.name, wl.kind),
-            "kernel": ("decode_step_int8 call" if fuse else
+            "kernel": ("decode step call" if fuse else
                        "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel"),
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_median": round(kern_median, 4),

@@ -210,6 +210,23 @@ int decode_attn_int8_witness_tv(const swa_cache *c, const void *q, float *out, f
 int decode_attn_int8_dither(const swa_cache *c, const void *q, float *out, float *cert, float *tv,
                             int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes, void *stream);
 
+/* One decode step in one call for the BF16 and FP32 kinds: kv_append of
+ * one token per sequence, then decode_attn (airsota.com §三: write at the
+ * current position, then attend).  The result is bit for bit that of
+ * kv_append(c, k_new, v_new, 1) followed by decode_attn.  When the decode
+ * plan has one split per (b, h) this is one kernel launch: each (b, h)
+ * work-group writes its token's rows into slot next_position mod W, then
+ * decodes; the last of the H work-groups of a sequence advances
+ * next_position.  Otherwise it is the two ordinary launches.
+ *  k_new, v_new  [B][H][1][D] in the cache's input dtype
+ *  q, out        as for decode_attn
+ *  ws            as for decode_step_int8 (its counters zero before the
+ *                first call; swa_workspace_init does that)
+ * Errors: descriptor errors, SWA_EUNSUPPORTED for an INT8 kind, SWA_ENULL,
+ * SWA_EALIGN, SWA_EWORKSPACE, SWA_EHIP. */
+int decode_step(const swa_cache *c, const void *k_new, const void *v_new, const void *q, float *out, void *ws,
+                size_t ws_bytes, void *stream);
+
 /* One decode step in one call: kv_append of one token per sequence, then
  * the INT8 decode of that sequence's query (airsota.com §三: write at the
  * current position, then attend; WitCert, section SGLang 生产级落地: one

@@ -273,6 +273,23 @@ def decode_attn_int8_dither(cache, q: torch.Tensor, delta: float, tau: float = 0
     return out, cert, tv, gate
 
 
+def decode_step(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``decode_step``: append one token per sequence ([B, H, 1, D]) and decode ``q`` in one
+    call (bf16 / fp32 kinds).  Returns out [B, H, D] fp32."""
+    shape = (cache.B, cache.H, 1, cache.D)
+    _need(k_new, shape, cache.input_dtype, "k_new")
+    _need(v_new, shape, cache.input_dtype, "v_new")
+    _need(q, (cache.B, cache.H, cache.D), cache.input_dtype, "q")
+    if out is None:
+        out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=q.device)
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    ws = cache.workspace() if ws is None else ws
+    check(lib().decode_step(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)), "decode_step")
+    return out
+
+
 def decode_step_int8(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, tau: float = 0.2,
                      delta: float = 1e-6, want_tv: bool = False, out: Optional[torch.Tensor] = None,
                      cmax: Optional[torch.Tensor] = None, tv: Optional[torch.Tensor] = None,

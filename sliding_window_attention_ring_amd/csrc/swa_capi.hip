@@ -295,6 +295,20 @@ int decode_attn_int8_witness(const swa_cache* c, const void* q, float* out, floa
   return decode_attn_int8_witness_tv(c, q, out, cmax, nullptr, nullptr, 0.f, c_all, ws, ws_bytes, stream);
 }
 
+int decode_step(const swa_cache* c, const void* k_new, const void* v_new, const void* q, float* out, void* ws,
+                size_t ws_bytes, void* stream) {
+  int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (is_int8(c->kind)) return SWA_EUNSUPPORTED;
+  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || ws == nullptr) return SWA_ENULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) || !aligned16(ws))
+    return SWA_EALIGN;
+  if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
+  const SplitPlan p = plan_decode(*c);
+  return launch_decode_step_rows(*c, k_new, v_new, q, out, ws, p, (hipStream_t)stream) == hipSuccess ? SWA_OK
+                                                                                                      : SWA_EHIP;
+}
+
 int decode_step_int8(const swa_cache* c, const void* k_new, const void* v_new, const void* q, float* out,
                      float* cmax, float* tv, int32_t* gate, float tau, float delta, void* ws, size_t ws_bytes,
                      void* stream) {

@@ -88,13 +88,15 @@ constexpr float kNegBig = -1e30f;  // finite start value of the running max
 #define SWA_ROW_U 4
 #endif
 
+// The decode of one (split, h, b) work-group, called by decode_kernel and
+// by the fused step kernel; n is next_position[b] as this decode sees it.
 // FINAL: the host plan has one split per (b, h), so the work-group writes
 // the output itself (zeros for an empty sequence) and no merge kernel runs.
+// No restrict qualifiers: the fused step writes a row of K and V first.
 template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(
-    const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
-    const int32_t* __restrict__ table, int64_t num_pages, const uint4* __restrict__ q, float* __restrict__ out,
-    float* __restrict__ part, int H, int W, int chunk, int nsplit_max) {
+__device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint4* V, const int32_t* table,
+                                               int64_t num_pages, const uint4* q, float* out, float* part, int H,
+                                               int W, int chunk, int nsplit_max) {
   using F = RowFmt<T>;
   constexpr int EPV = F::kEpv;
   constexpr int VPR = D / EPV;          // 16-byte vectors per row
@@ -112,7 +114,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * H + h;
-  const int n = np[b];
   const int len = n < W ? n : W;
   if (len <= 0) {  // empty cache: zeros, written here or by the merge kernel
     if constexpr (FINAL) {
@@ -266,6 +267,52 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   if (t == 0) { my[0] = M; my[1] = L; }
 }
 
+template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(
+    const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
+    const int32_t* __restrict__ table, int64_t num_pages, const uint4* __restrict__ q, float* __restrict__ out,
+    float* __restrict__ part, int H, int W, int chunk, int nsplit_max) {
+  decode_rows_wg<T, D, NW, U, PAGED, FINAL>(np[blockIdx.z], K, V, table, num_pages, q, out, part, H, W, chunk,
+                                            nsplit_max);
+}
+
+// Fused decode step (one token per sequence) for row caches, one
+// work-group per (b, h); plans with a single split per (b, h) only.  The
+// work-group writes its token's key and value rows into slot
+// next_position mod W (and, for h == 0, the slot's position), then decodes
+// with next_position + 1 after a barrier; the rows are private to its
+// (b, h).  next_position[b] is advanced by the last of the H work-groups of
+// sequence b to finish, elected by a per-sequence counter in the workspace,
+// as in the INT8 step kernel.  A negative next_position (a violated
+// precondition) appends nothing and advances nothing.
+template <typename T, int D, int NW, int U, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
+    uint4* K, uint4* V, int32_t* np, int32_t* pos, int32_t* cnt, RowMap map, const uint4* k_new,
+    const uint4* v_new, int64_t num_pages, const uint4* q, float* out, int H, int W, int chunk) {
+  constexpr int VPR = D / RowFmt<T>::kEpv;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * H + h;
+  const int n0 = np[b];
+  if (n0 >= 0) {
+    const int64_t slot = n0 % W;
+    const int64_t row = map.row(b, h, slot);
+    for (int i = threadIdx.x; i < 2 * VPR; i += NW * 64) {
+      if (i < VPR) K[row * VPR + i] = k_new[bh * VPR + i];
+      else V[row * VPR + (i - VPR)] = v_new[bh * VPR + (i - VPR)];
+    }
+    if (h == 0 && threadIdx.x == 0) pos[(int64_t)b * W + slot] = n0;
+  }
+  __syncthreads();
+  decode_rows_wg<T, D, NW, U, PAGED, true>(n0 >= 0 ? n0 + 1 : n0, K, V, map.table, num_pages, q, out, nullptr, H,
+                                           W, chunk, 1);
+  if (threadIdx.x == 0 && n0 >= 0) {
+    if (atomicAdd(cnt + b, 1) == H - 1) {
+      atomicExch(cnt + b, 0);
+      np[b] = n0 + 1;
+    }
+  }
+}
+
 // Log-sum-exp merge of the split partials of one (b, h); thread t owns dim t.
 // A (b, h) served by a single split already has its output; an empty cache
 // gets zeros.
@@ -317,7 +364,51 @@ hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, c
   return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_step_one(const swa_cache& c, const void* k_new, const void* v_new, const void* q, float* out,
+                           void* ws, const SplitPlan& plan, hipStream_t s) {
+  constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
+  const bool paged = c.layout == SWA_LAYOUT_PAGED;
+  const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
+  const dim3 grid(1, c.H, c.B), block(NW * 64);
+  int32_t* cnt = step_counters(c, plan, ws);
+#define SWA_ROW_STEP(P)                                                                                           \
+  hipLaunchKernelGGL((decode_step_rows_kernel<T, D, NW, U, P>), grid, block, lds, s, reinterpret_cast<uint4*>(c.k), \
+                     reinterpret_cast<uint4*>(c.v), c.next_position, c.pos, cnt, row_map(c),                       \
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),                \
+                     paged ? c.num_pages : 0, reinterpret_cast<const uint4*>(q), out, c.H, c.W, plan.unit_per_split)
+  if (paged) SWA_ROW_STEP(true); else SWA_ROW_STEP(false);
+#undef SWA_ROW_STEP
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_step_rows(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
+                                   float* out, void* ws, const SplitPlan& plan, hipStream_t s) {
+  if (plan.nsplit_max != 1) {  // several splits per (b, h): the two ordinary launches
+    bool advanced = false;
+    hipError_t e = launch_append_rows(c, k_new, v_new, 1, s, &advanced);
+    if (e == hipSuccess && !advanced) e = launch_advance(c, 1, s);
+    if (e != hipSuccess) return e;
+    return launch_decode(c, q, out, ws, plan, s);
+  }
+  if (c.kind == SWA_KV_BF16) {
+    switch (c.D) {
+      case 64: return launch_step_one<uint16_t, 64>(c, k_new, v_new, q, out, ws, plan, s);
+      case 128: return launch_step_one<uint16_t, 128>(c, k_new, v_new, q, out, ws, plan, s);
+      case 256: return launch_step_one<uint16_t, 256>(c, k_new, v_new, q, out, ws, plan, s);
+    }
+  } else if (c.kind == SWA_KV_FP32) {
+    switch (c.D) {
+      case 16: return launch_step_one<float, 16>(c, k_new, v_new, q, out, ws, plan, s);
+      case 32: return launch_step_one<float, 32>(c, k_new, v_new, q, out, ws, plan, s);
+      case 64: return launch_step_one<float, 64>(c, k_new, v_new, q, out, ws, plan, s);
+      case 128: return launch_step_one<float, 128>(c, k_new, v_new, q, out, ws, plan, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
 
 // Rows of one work-group iteration round (all NW waves): the split size is a
 // multiple of it so that every wave does the same number of iterations.

@@ -49,6 +49,10 @@ hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const 
                                    float* out, float* cmax, float* tv, int32_t* gate, float tau, float delta,
                                    void* ws, const SplitPlan& plan, hipStream_t s);
 
+// The same for the bf16 / fp32 row kinds (kv_append of one token + decode_attn).
+hipError_t launch_decode_step_rows(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
+                                   float* out, void* ws, const SplitPlan& plan, hipStream_t s);
+
 // Workspace layout: split partials (B*H*nsplit_max*(D+4) floats), padded to
 // 256 bytes, then B int32 counters of the fused step (zero between calls).
 inline size_t partials_bytes(const swa_cache& c, const SplitPlan& p) {

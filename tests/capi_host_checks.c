@@ -70,6 +70,7 @@ int main(void) {
              kinds[i] == SWA_KV_INT8_DITHER ? SWA_EINVAL : SWA_EUNSUPPORTED);
       EXPECT(decode_step_int8(&c, A, A, A, F, F, NULL, NULL, 0.2f, 0.1f, ws, need - 1, NULL),
              i >= 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
+      EXPECT(decode_step(&c, A, A, A, F, ws, need - 1, NULL), i < 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
       EXPECT(kv_truncate(&c, NULL, NULL, NULL), SWA_ENULL);
       EXPECT(kv_truncate(&c, (const int32_t *)0xA0002, NULL, NULL), SWA_EALIGN);
       EXPECT(swa_validate(&c, NULL, NULL), SWA_ENULL);

@@ -105,6 +105,10 @@ def test_argument_checks_return_codes():
     assert dd(p(i8), A16, A16, A16, None, None, 0.2, 0.1, ws, nz, None) == -4      # Tier A cache
     assert L.decode_attn_int8_witness(p(dz), A16, A16, A16, None, ws, nz, None) == -4
     assert L.decode_attn(p(dz), A16, A16, ws, nz, None) == -4
+    assert L.decode_step(p(i8), A16, A16, A16, A16, ws, 1 << 30, None) == -4                  # INT8 cache
+    assert L.decode_step(p(d), None, A16, A16, A16, ws, need, None) == -2
+    assert L.decode_step(p(d), A16, ODD, A16, A16, ws, need, None) == -3
+    assert L.decode_step(p(d), A16, A16, A16, A16, ws, need - 1, None) == -5
     st = L.decode_step_int8
     assert st(p(d), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, need, None) == -4     # bf16 cache
     assert st(p(i8), None, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, 1 << 30, None) == -2

@@ -147,3 +147,42 @@ def test_fused_step_headline_shape_and_graph():
                 assert torch.equal(getattr(cg, name), getattr(ce, name)), (i, name)
     assert int(cg.next_position[0]) == prefill + steps
     assert swa.validate(cg) == 0
+
+
+@pytest.mark.parametrize("kind,B,H,D,W,layout", [("bf16", 16, 32, 128, 64, "ring"), ("bf16", 16, 32, 128, 64, "paged"),
+                                                 ("fp32", 1, 2, 16, 4, "ring"), ("bf16", 1, 2, 64, 4096, "ring")])
+def test_fused_row_step_equals_append_then_decode(kind, B, H, D, W, layout):
+    """decode_step (bf16 / fp32 kinds) against kv_append + decode_attn on twin
+    caches, bit for bit in the output and the ring state, over 3W ragged
+    steps; the last shape has several splits per (b, h) (two launches)."""
+    import sliding_window_attention_ring_amd as swa
+    say("fused row step", kind, B, H, D, W, layout)
+    dt = torch.float32 if kind == "fp32" else torch.bfloat16
+    rng = np.random.default_rng(B * H + W)
+    lens = [int(x) for x in rng.integers(0, 2 * W, size=B)]
+    steps = min(3 * W, 40) if W > 64 else 3 * W
+    g = torch.Generator().manual_seed(W + D)
+    N = max(lens) + steps
+    k = torch.randn((B, H, N, D), generator=g).to(dt)
+    v = torch.randn((B, H, N, D), generator=g).to(dt)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache(kind, B, H, D, W, layout=layout)
+        c.k.zero_(); c.v.zero_()
+        for b, n in enumerate(lens):
+            if n:
+                swa.kv_append(c.seq_view(b), k[b:b + 1, :, :n].contiguous().cuda(), v[b:b + 1, :, :n].contiguous().cuda())
+        caches.append(c)
+    cf, cs = caches
+    for i in range(steps):
+        pos = [n + i for n in lens]
+        kn = torch.stack([k[b, :, p:p + 1] for b, p in enumerate(pos)]).contiguous().cuda()
+        vn = torch.stack([v[b, :, p:p + 1] for b, p in enumerate(pos)]).contiguous().cuda()
+        q = torch.randn((B, H, D), generator=g).to(dt).cuda()
+        of = swa.decode_step(cf, kn, vn, q)
+        swa.kv_append(cs, kn, vn)
+        os_ = swa.decode_attn(cs, q)
+        assert torch.equal(of, os_), f"step {i}: out differs"
+        for name in ("k", "v", "pos", "next_position"):
+            assert torch.equal(getattr(cf, name), getattr(cs, name)), f"step {i}: {name} differs"
+    assert swa.validate(cf) == 0
