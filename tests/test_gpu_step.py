@@ -186,3 +186,66 @@ def test_fused_row_step_equals_append_then_decode(kind, B, H, D, W, layout):
         for name in ("k", "v", "pos", "next_position"):
             assert torch.equal(getattr(cf, name), getattr(cs, name)), f"step {i}: {name} differs"
     assert swa.validate(cf) == 0
+
+
+@pytest.mark.parametrize("kind", ["int8", "int8_dither", "bf16"])
+def test_fused_step_mixed_with_other_operations(kind):
+    """Fused steps interleaved with truncations, multi-token appends and
+    separate decodes on one cache (sharing its workspace); a twin takes the
+    same operations with kv_append + the separate decode only.  Every output
+    and the whole state must agree bit for bit after every operation."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, W = (32, 64, 64) if kind == "int8_dither" else (4, 64, 64)
+    rng = np.random.default_rng(99)
+    g = torch.Generator().manual_seed(99)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache(kind, B, H, 128, W)
+        for name in ("k", "v", "k_scale", "v_scale", "witness", "k_stage", "v_stage"):
+            if getattr(c, name, None) is not None:
+                getattr(c, name).zero_()
+        caches.append(c)
+    cf, cs = caches
+    names = ["k", "v", "pos", "next_position"] + (["k_scale", "v_scale", "k_stage", "v_stage"] if kind != "bf16" else []) \
+        + (["witness"] if kind == "int8" else [])
+
+    def rows(T):
+        k = torch.randn((B, H, T, 128), generator=g).to(torch.bfloat16).cuda()
+        v = torch.randn((B, H, T, 128), generator=g).to(torch.bfloat16).cuda()
+        return k, v
+
+    def dec(c, q):
+        if kind == "bf16":
+            return (swa.decode_attn(c, q),)
+        if kind == "int8":
+            return swa.decode_attn_int8_witness_tv(c, q)[:4]
+        return swa.decode_attn_int8_dither(c, q, delta=1e-3)
+
+    for op in range(60):
+        r = rng.random()
+        q = torch.randn((B, H, 128), generator=g).to(torch.bfloat16).cuda()
+        if r < 0.55:  # fused step on one cache, append + decode on the twin
+            k, v = rows(1)
+            if kind == "bf16":
+                of = (swa.decode_step(cf, k, v, q),)
+            else:
+                of = swa.decode_step_int8(cf, k, v, q, delta=1e-3, want_tv=True)
+            swa.kv_append(cs, k, v)
+            os_ = dec(cs, q)
+            for a, b_ in zip(of, os_):
+                assert torch.equal(a, b_), f"op {op}"
+        elif r < 0.7:  # multi-token append on both
+            k, v = rows(int(rng.integers(2, 40)))
+            for c in caches:
+                swa.kv_append(c, k, v)
+        elif r < 0.8:  # truncation on both
+            n = cf.next_position.cpu().numpy()
+            cut = torch.tensor([int(rng.integers(0, m + 1)) for m in n], dtype=torch.int32, device="cuda")
+            oka, okb = swa.kv_truncate(cf, cut), swa.kv_truncate(cs, cut)
+            assert torch.equal(oka, okb)
+        else:  # separate decode on both (uses the same workspace as the fused steps)
+            for a, b_ in zip(dec(cf, q), dec(cs, q)):
+                assert torch.equal(a, b_), f"op {op}"
+        for name in names:
+            assert torch.equal(getattr(cf, name), getattr(cs, name)), f"op {op}: {name}"
+    assert swa.validate(cf) == 0
