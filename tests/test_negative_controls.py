@@ -1,10 +1,10 @@
-"""Negative controls for the GPU tests' own checkers (CPU only).
+"""Negative controls for the comparisons in the GPU parity tests (CPU only).
 
 The GPU parity tests are only as strong as their comparisons.  Here the
 correct state and outputs come from the oracle, a planted mistake of each
 class the sliding-window pages warn about (page "用Lean4形式化验证滑动窗口KV
 Cache的正确性", §1.2 and §5.1; page "LLM 機制實驗（五）": a stale
-next_position) is applied to them on the CPU, and the checkers must reject
+next_position) is applied to them on the CPU, and those comparisons must reject
 every one: slot off by one, wrong base while the ring fills, stale
 next_position, head advanced before the write; for the outputs, a decode
 with a stale next_position; for the bounds, a zeroed witness and a halved

@@ -5,9 +5,9 @@ What pins it (not a retyping of the oracle's own formulas):
 * brute force over every small window and history against the one-step
   commutation equation and the three proof goals of [Lean-SWA] §2.4;
 * the printed §4.1 identity is shown false on its counterexample, so the
-  checker is able to see an off-by-one;
+  window comparison is able to see an off-by-one;
 * planted bugs (the bug classes listed in [Lean-SWA] §1.2 and the stale
-  ``next_position`` of [Prefix-Reuse]) are caught by the checker that the GPU
+  ``next_position`` of [Prefix-Reuse]) are caught by the window comparison that the GPU
   parity tests use.
 """
 
@@ -96,9 +96,9 @@ def test_printed_ring_to_list_reads_garbage_when_unfilled():
     assert None not in lm.ring_to_list(w, ring, n)
 
 
-# ---- planted bugs: the checker used by the parity tests must reject each ----
+# ---- planted bugs: the window comparison used by the parity tests must reject each ----
 
-def checker(w, ring, n, hist):
+def window_matches(w, ring, n, hist):
     return lm.ring_to_list(w, ring, n) == lm.last_window(w, hist)
 
 
@@ -111,7 +111,7 @@ def buggy_ring(w, hist, slot_fn):
 
 @pytest.mark.parametrize("bug", ["slot_off_by_one", "advance_before_write", "unfilled_base",
                                  "stale_next_position"])
-def test_checker_rejects_planted_bugs(bug):
+def test_window_comparison_rejects_planted_bugs(bug):
     """[Lean-SWA] §1.2 lists the real bug classes (window offset by one, wrong
     base while unfilled, wrong absolute position, head/tail update order);
     [Prefix-Reuse] plants a stale next_position.  Each must fail the check at
@@ -122,7 +122,7 @@ def test_checker_rejects_planted_bugs(bug):
         hist = cells(n)
         if bug == "slot_off_by_one":
             ring = buggy_ring(w, hist, lambda p: (p + 1) % w)
-            ok = checker(w, ring, n, hist)
+            ok = window_matches(w, ring, n, hist)
         elif bug == "advance_before_write":
             # once the ring is full, the head (oldest slot) is advanced before the
             # overwrite, so the read-back starts one slot late
@@ -139,7 +139,7 @@ def test_checker_rejects_planted_bugs(bug):
         else:  # stale next_position: positions restart 2 too late
             shifted = [(p + 2, t) for p, t in hist]
             ring = lm.ring_state(w, shifted, pos_of, None)
-            ok = checker(w, ring, n, hist)
+            ok = window_matches(w, ring, n, hist)
         if not ok:
             caught = True
     assert caught, bug
