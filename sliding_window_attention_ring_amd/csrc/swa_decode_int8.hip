@@ -14,13 +14,15 @@
 // committed blocks of the ring: blocks k0..nb-1 with k0 = (n-len)/16, block k
 // in slots [16k mod W, +16); in block k0 the positions below n-len are masked.
 // The newest n mod 16 tokens are exact bf16 rows in the staging area and
-// carry c_t = 0; the merge kernel folds them in.
+// carry c_t = 0; the last stage (finish_int8) folds them in.
 //
 // Layout of the work: grid (split, h, b), NW waves; a split owns `cb`
-// consecutive blocks; a wave takes UB blocks per iteration.  Every split
-// writes a partial (m, l, cmax, acc[D]); a second kernel merges the splits
-// of each (b, h) -- the kernel boundary makes the partials visible across
-// the XCDs' L2 caches without any device-wide fence.  Per block a
+// consecutive blocks; a wave takes UB blocks per iteration.  When the plan
+// has one split per (b, h) (FINAL), the work-group runs the last stage
+// itself.  Otherwise every split writes a partial (m, l, cmax, acc[D]) and
+// a second kernel merges the splits of each (b, h) -- the kernel boundary
+// makes the partials visible across the XCDs' L2 caches without any
+// device-wide fence.  Per block a
 // lane loads 2x16 B of key codes and 2x16 B of value codes (8 lanes per
 // 128-byte row, rows g and g+8) and 8 B of witness (4 lanes per token).
 //
@@ -60,10 +62,6 @@ namespace {
 #ifndef SWA_INT8_UB
 #define SWA_INT8_UB 2
 #endif
-// 1: key dots on packed fp16 (codes as 1024+u, query in fp16) with v_dot2_f32_f16.
-#ifndef SWA_INT8_KDOT_F16
-#define SWA_INT8_KDOT_F16 0
-#endif
 
 constexpr int D = 128;
 constexpr int PF = D + 4;          // m, l, cmax, pad, acc[D]
@@ -81,52 +79,8 @@ struct Blk {
 };
 
 // Dot product of this lane's 16 query dims with 16 int8 key codes, in
-// base-2 logit units before the block scale.
-#if SWA_INT8_KDOT_F16
-// Codes c are shifted to u = c + 128 (xor 0x80) and packed two per register
-// as the fp16 values 1024 + u (bits 0x64uu, built with one byte permute);
-// the query is held in fp16 (exact for bf16 values of magnitude 2^-14..65504).
-// sum q(1024 + u) = sum q c + 1152 sum q, so the per-lane constant
-// 1152*sum(q) is removed before the cross-lane sum.
-struct KeyDot {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  h2 q2[8];
-  float corr, scale;
-  __device__ __forceinline__ void init(const uint4* qv, float qscale) {
-    float f[16];
-    float t8[8];
-    unpack8(qv[0], t8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = t8[e];
-    unpack8(qv[1], t8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[8 + e] = t8[e];
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      q2[i] = h2{(_Float16)f[2 * i], (_Float16)f[2 * i + 1]};
-      sum += (float)q2[i].x + (float)q2[i].y;
-    }
-    corr = 1152.0f * sum;
-    scale = qscale;
-  }
-  __device__ __forceinline__ float dot(const uint4 c) const {
-    const uint32_t w[4] = {c.x ^ 0x80808080u, c.y ^ 0x80808080u, c.z ^ 0x80808080u, c.w ^ 0x80808080u};
-    float d = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, w[i], 0x04010400u);
-      const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, w[i], 0x04030402u);
-      d = __builtin_amdgcn_fdot2(q2[2 * i], __builtin_bit_cast(h2, lo), d, false);
-      d = __builtin_amdgcn_fdot2(q2[2 * i + 1], __builtin_bit_cast(h2, hi), d, false);
-    }
-    return d - corr;
-  }
-  __device__ __forceinline__ float finish(float d) const { return d * scale; }
-};
-#else
-// Each code converts with one sign-extending byte convert; the query is
-// pre-scaled by log2(e)/sqrt(D).
+// base-2 logit units before the block scale.  Each code converts with one
+// sign-extending byte convert; the query is pre-scaled by log2(e)/sqrt(D).
 struct KeyDot {
   float qf[16];
   __device__ __forceinline__ void init(const uint4* qv, float qscale) {
@@ -147,9 +101,7 @@ struct KeyDot {
       for (int j = 0; j < 4; ++j) d = fmaf(qf[4 * i + j], s8(cw[i], j), d);
     return d;
   }
-  __device__ __forceinline__ float finish(float d) const { return d; }
 };
-#endif
 
 // Tier B element values t = 256 code + 255 - m for the 4 codes of word cw,
 // given nm = ~m: bytes (~m0, c0, ~m1, c1) and (~m2, c2, ~m3, c3) as two
@@ -300,7 +252,6 @@ __device__ __forceinline__ void decode_int8_wg(
     float* out, float* cmax_out, float* tv, int32_t* gate, float tau, const uint64_t* req, uint32_t layer,
     float delta) {
   static_assert(NW * 64 >= 256, "the staging fold needs 256 threads");
-  static_assert(!DITHER || !SWA_INT8_KDOT_F16, "Tier B uses the byte-convert key dot");
   static_assert(!APPEND || FINAL, "the fused step needs one split per (b, h)");
   __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
   __shared__ float sm_acc[NW][D];
@@ -451,7 +402,7 @@ __device__ __forceinline__ void decode_int8_wg(
           d = group_sum<8>(d) * sk;
         } else {
           d = kd.dot(half ? cur[ub].k1 : cur[ub].k0);
-          d = kd.finish(group_sum<8>(d)) * sk;  // key scale folded into the finished dot
+          d = group_sum<8>(d) * sk;  // key scale folded into the finished dot
         }
         s[2 * ub + half] = (live && pos >= p0) ? d : -INFINITY;
       }
