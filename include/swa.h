@@ -213,11 +213,12 @@ int decode_attn_int8_dither(const swa_cache *c, const void *q, float *out, float
 /* One decode step in one call for the BF16 and FP32 kinds: kv_append of
  * one token per sequence, then decode_attn (airsota.com §三: write at the
  * current position, then attend).  The result is bit for bit that of
- * kv_append(c, k_new, v_new, 1) followed by decode_attn.  When the decode
- * plan has one split per (b, h) this is one kernel launch: each (b, h)
- * work-group writes its token's rows into slot next_position mod W, then
- * decodes; the last of the H work-groups of a sequence advances
- * next_position.  Otherwise it is the two ordinary launches.
+ * kv_append(c, k_new, v_new, 1) followed by decode_attn.  The append and
+ * the decode are one kernel launch: the work-group whose split holds slot
+ * next_position mod W of a (b, h) writes the token's rows there, then every
+ * work-group decodes its split; the last work-group of a sequence to finish
+ * advances next_position.  A plan with several splits per (b, h) adds the
+ * merge launch, as decode_attn does.
  *  k_new, v_new  [B][H][1][D] in the cache's input dtype
  *  q, out        as for decode_attn
  *  ws            as for decode_step_int8 (its counters zero before the
@@ -233,10 +234,12 @@ int decode_step(const swa_cache *c, const void *k_new, const void *v_new, const 
  * fused pass per step).  INT8 kinds only.  The result is bit for bit that
  * of kv_append(c, k_new, v_new, 1) followed by decode_attn_int8_witness_tv
  * (INT8) or decode_attn_int8_dither (INT8_DITHER) with the same arguments.
- * When the decode plan has one split per (b, h) this is one kernel launch:
- * each (b, h) work-group appends its own token, quantizing the block it
- * completes, then decodes; the last of the H work-groups of a sequence
- * advances next_position.  Otherwise it is the two ordinary launches.
+ * The append and the decode are one kernel launch: for each (b, h) one
+ * work-group appends the token (quantizing the block it completes, in the
+ * work-group whose split decodes that block), then every work-group decodes
+ * its split; the last work-group of a sequence to finish advances
+ * next_position.  A plan with several splits per (b, h) adds the merge
+ * launch, as the decode entry points do.
  *  k_new, v_new  [B][H][1][D] bf16
  *  q, out, cmax, tv, gate, tau  as for decode_attn_int8_witness_tv; cmax is
  *                the certificate for INT8_DITHER
@@ -255,12 +258,13 @@ int decode_step_int8(const swa_cache *c, const void *k_new, const void *v_new, c
 
 /* Workspace bytes the decode entry points need for this cache shape: the
  * split partials (B*H*nsplit*(D+4) floats) padded to 256 bytes, then B
- * int32 counters for decode_step_int8, padded to 256 bytes.  0 for an
- * invalid descriptor. */
+ * int32 counters for decode_step and decode_step_int8, padded to 256
+ * bytes.  0 for an invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);
 
 /* Zero-fill a workspace.  The decode entry points overwrite the partials
- * they read; decode_step_int8 needs its counters zero before its first call.
+ * they read; decode_step and decode_step_int8 need the counters zero
+ * before their first call.
  * Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
 int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
 

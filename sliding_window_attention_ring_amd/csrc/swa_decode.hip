@@ -276,37 +276,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
                                             nsplit_max);
 }
 
-// Fused decode step (one token per sequence) for row caches, one
-// work-group per (b, h); plans with a single split per (b, h) only.  The
-// work-group writes its token's key and value rows into slot
-// next_position mod W (and, for h == 0, the slot's position), then decodes
-// with next_position + 1 after a barrier; the rows are private to its
-// (b, h).  next_position[b] is advanced by the last of the H work-groups of
-// sequence b to finish, elected by a per-sequence counter in the workspace,
-// as in the INT8 step kernel.  A negative next_position (a violated
-// precondition) appends nothing and advances nothing.
-template <typename T, int D, int NW, int U, bool PAGED>
+// Fused decode step (one token per sequence) for row caches: grid (split,
+// h, b) as the decode's.  The work-group of the split whose slots hold slot
+// next_position mod W writes its token's key and value rows there (and, for
+// h == 0, the slot's position); after a barrier every work-group decodes its
+// split with next_position + 1.  The rows are read only by the work-group
+// that wrote them.  next_position[b] is advanced by the last of the work-groups
+// of sequence b to finish, elected by a per-sequence counter in the
+// workspace, as in the INT8 step kernel.  A negative next_position (a
+// violated precondition) appends nothing and advances nothing.
+template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
     uint4* K, uint4* V, int32_t* np, int32_t* pos, int32_t* cnt, RowMap map, const uint4* k_new,
-    const uint4* v_new, int64_t num_pages, const uint4* q, float* out, int H, int W, int chunk) {
+    const uint4* v_new, int64_t num_pages, const uint4* q, float* out, float* part, int H, int W, int chunk,
+    int nsplit_max) {
   constexpr int VPR = D / RowFmt<T>::kEpv;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
   const int n0 = np[b];
   if (n0 >= 0) {
     const int64_t slot = n0 % W;
-    const int64_t row = map.row(b, h, slot);
-    for (int i = threadIdx.x; i < 2 * VPR; i += NW * 64) {
-      if (i < VPR) K[row * VPR + i] = k_new[bh * VPR + i];
-      else V[row * VPR + (i - VPR)] = v_new[bh * VPR + (i - VPR)];
+    if (slot / chunk == split) {
+      const int64_t row = map.row(b, h, slot);
+      for (int i = threadIdx.x; i < 2 * VPR; i += NW * 64) {
+        if (i < VPR) K[row * VPR + i] = k_new[bh * VPR + i];
+        else V[row * VPR + (i - VPR)] = v_new[bh * VPR + (i - VPR)];
+      }
+      if (h == 0 && threadIdx.x == 0) pos[(int64_t)b * W + slot] = n0;
     }
-    if (h == 0 && threadIdx.x == 0) pos[(int64_t)b * W + slot] = n0;
   }
   __syncthreads();
-  decode_rows_wg<T, D, NW, U, PAGED, true>(n0 >= 0 ? n0 + 1 : n0, K, V, map.table, num_pages, q, out, nullptr, H,
-                                           W, chunk, 1);
+  decode_rows_wg<T, D, NW, U, PAGED, FINAL>(n0 >= 0 ? n0 + 1 : n0, K, V, map.table, num_pages, q, out, part, H, W,
+                                            chunk, nsplit_max);
   if (threadIdx.x == 0 && n0 >= 0) {
-    if (atomicAdd(cnt + b, 1) == H - 1) {
+    if (atomicAdd(cnt + b, 1) == H * (int)gridDim.x - 1) {
       atomicExch(cnt + b, 0);
       np[b] = n0 + 1;
     }
@@ -331,6 +334,14 @@ __global__ __launch_bounds__(D) void merge_kernel(const int32_t* __restrict__ np
   float M, L, A;
   merge_partials<PF>(part + bh * nsplit_max * PF, nsplit, t, M, L, A);
   out[bh * D + t] = A / L;
+}
+
+// The second launch of a plan with several splits per (b, h).
+template <int D>
+hipError_t launch_merge(const swa_cache& c, float* out, const float* part, const SplitPlan& plan, hipStream_t s) {
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(c.H, c.B), dim3(D), 0, s, c.next_position, part, out, c.H, c.W,
+                     plan.unit_per_split, plan.nsplit_max);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -359,9 +370,7 @@ hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, c
 #undef SWA_ROW_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || final_pass) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(c.H, c.B), dim3(D), 0, s, c.next_position, part, out, c.H, c.W,
-                     plan.unit_per_split, plan.nsplit_max);
-  return hipGetLastError();
+  return launch_merge<D>(c, out, part, plan, s);
 }
 
 template <typename T, int D>
@@ -369,30 +378,32 @@ hipError_t launch_step_one(const swa_cache& c, const void* k_new, const void* v_
                            void* ws, const SplitPlan& plan, hipStream_t s) {
   constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
   const bool paged = c.layout == SWA_LAYOUT_PAGED;
+  const bool final_pass = plan.nsplit_max == 1;
   const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
-  const dim3 grid(1, c.H, c.B), block(NW * 64);
+  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  float* part = reinterpret_cast<float*>(ws);
   int32_t* cnt = step_counters(c, plan, ws);
-#define SWA_ROW_STEP(P)                                                                                           \
-  hipLaunchKernelGGL((decode_step_rows_kernel<T, D, NW, U, P>), grid, block, lds, s, reinterpret_cast<uint4*>(c.k), \
-                     reinterpret_cast<uint4*>(c.v), c.next_position, c.pos, cnt, row_map(c),                       \
-                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),                \
-                     paged ? c.num_pages : 0, reinterpret_cast<const uint4*>(q), out, c.H, c.W, plan.unit_per_split)
-  if (paged) SWA_ROW_STEP(true); else SWA_ROW_STEP(false);
+#define SWA_ROW_STEP(P, F)                                                                                        \
+  hipLaunchKernelGGL((decode_step_rows_kernel<T, D, NW, U, P, F>), grid, block, lds, s,                           \
+                     reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.next_position, c.pos, cnt,    \
+                     row_map(c), reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),    \
+                     paged ? c.num_pages : 0, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,               \
+                     plan.unit_per_split, plan.nsplit_max)
+  if (paged) {
+    if (final_pass) SWA_ROW_STEP(true, true); else SWA_ROW_STEP(true, false);
+  } else {
+    if (final_pass) SWA_ROW_STEP(false, true); else SWA_ROW_STEP(false, false);
+  }
 #undef SWA_ROW_STEP
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || final_pass) return e;
+  return launch_merge<D>(c, out, part, plan, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_step_rows(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
                                    float* out, void* ws, const SplitPlan& plan, hipStream_t s) {
-  if (plan.nsplit_max != 1) {  // several splits per (b, h): the two ordinary launches
-    bool advanced = false;
-    hipError_t e = launch_append_rows(c, k_new, v_new, 1, s, &advanced);
-    if (e == hipSuccess && !advanced) e = launch_advance(c, 1, s);
-    if (e != hipSuccess) return e;
-    return launch_decode(c, q, out, ws, plan, s);
-  }
   if (c.kind == SWA_KV_BF16) {
     switch (c.D) {
       case 64: return launch_step_one<uint16_t, 64>(c, k_new, v_new, q, out, ws, plan, s);

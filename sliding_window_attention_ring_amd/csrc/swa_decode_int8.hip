@@ -239,11 +239,12 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
 
 // The decode of one (split, h, b) work-group, called by decode_int8_kernel
 // and by the fused step kernel; n is next_position[b] as this decode sees
-// it.  APPEND (fused step): block kb_new was committed by this work-group
-// in this launch, and its two scales are taken from sk_new / sv_new, not
-// from memory -- a scalar-cache line holding them may have been filled
-// before the commit (lines are shared across heads).  The pointers carry no
-// restrict qualifier because the fused step writes the same buffers first.
+// it.  APPEND (fused step): block kb_new, unless -1, was committed by this
+// work-group in this launch, and its two scales are taken from sk_new /
+// sv_new, not from memory -- a scalar-cache line holding them may have been
+// filled before the commit (lines are shared across heads).  The pointers
+// carry no restrict qualifier because the fused step writes the same
+// buffers first.
 template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER, bool APPEND>
 __device__ __forceinline__ void decode_int8_wg(
     int n, int kb_new, float sk_new, float sv_new, const int8_t* Kc, const int8_t* Vc, const float* ksc,
@@ -252,7 +253,6 @@ __device__ __forceinline__ void decode_int8_wg(
     float* out, float* cmax_out, float* tv, int32_t* gate, float tau, const uint64_t* req, uint32_t layer,
     float delta) {
   static_assert(NW * 64 >= 256, "the staging fold needs 256 threads");
-  static_assert(!APPEND || FINAL, "the fused step needs one split per (b, h)");
   __shared__ float sm_m[NW], sm_l[NW], sm_c[NW];
   __shared__ float sm_acc[NW][D];
   __shared__ float sm_s[16];
@@ -549,58 +549,66 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
                                                       out, cmax_out, tv, gate, tau, req, layer, delta);
 }
 
-// Fused decode step (one token per sequence), one work-group per (b, h);
-// plans with a single split per (b, h) only.  The work-group first appends
-// its own token: into the staging rows, or -- when the token completes a
-// 16-token block -- by quantizing that block (waves 0 and 1, exactly as
-// kv_append does).  After a barrier it decodes with next_position + 1; the
-// rows it wrote are private to its (b, h), and the new block's scales come
-// through LDS (see decode_int8_wg).  next_position[b] is shared by the H
-// work-groups of sequence b: each reads it first, and a per-sequence
-// counter in the workspace elects the last of them to finish, which writes
+// Fused decode step (one token per sequence): grid (split, h, b) as the
+// decode's.  First the token is appended: into the staging rows (by split
+// 0), or -- when the token completes a 16-token block -- by quantizing that
+// block (waves 0 and 1 of the split that owns the block, exactly as
+// kv_append does).  After a barrier every work-group decodes its split with
+// next_position + 1; the rows written are private to their (b, h) and read
+// only by the work-group that wrote them (the staging rows only by the last
+// stage, FINAL or the merge kernel), and the new block's scales come through
+// LDS (see decode_int8_wg).  next_position[b] is shared by the work-groups
+// of sequence b: each reads it first, and a per-sequence counter in the
+// workspace elects the last of them to finish, which writes
 // next_position + 1 and clears the counter.  Every work-group of b has read
-// next_position before it counts, so none reads the new value; the next
-// launch does.  A negative next_position (a violated precondition) appends
-// nothing and advances nothing, as kv_append.
-template <int NW, int UB, bool PAGED, bool DITHER>
+// next_position before it counts, so none reads the new value; the merge
+// kernel and the next launch do.  A negative next_position (a violated
+// precondition) appends nothing and advances nothing, as kv_append.
+template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER>
 __global__ __launch_bounds__(NW * 64) void decode_step_int8_kernel(
     int8_t* Kc, int8_t* Vc, float* ksc, float* vsc, uint16_t* wit, int32_t* np, int32_t* pos, int32_t* cnt,
     RowMap map, const uint16_t* k_new, const uint16_t* v_new, Dither dz, const int32_t* table, int64_t num_pages,
-    const uint16_t* q, int H, int W, int cb, uint16_t* kst, uint16_t* vst, float* out, float* cmax_out, float* tv,
-    int32_t* gate, float tau, float delta) {
+    const uint16_t* q, float* part, int H, int W, int cb, int nsplit_max, uint16_t* kst, uint16_t* vst, float* out,
+    float* cmax_out, float* tv, int32_t* gate, float tau, float delta) {
   __shared__ float sm_scale[2];
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * H + h;
   const int n0 = np[b];
   int n = n0, kb_new = -1;
   if (n0 >= 0) {
+    n = n0 + 1;
     if ((n0 & 15) == 15) {  // this token completes block n0 / 16
-      kb_new = n0 >> 4;
-      if (wave < 2) {
-        const bool key = wave == 0;
-        const float s = commit_block_wave(lane, key, key ? k_new : v_new, key ? kst : vst, n0, 1, kb_new, b, h, map,
-                                          key ? Kc : Vc, key ? ksc : vsc, wit,
-                                          (key && h == 0) ? pos + (int64_t)b * W : nullptr, dz);
-        if (lane == 0) sm_scale[wave] = s;
+      // The split that decodes block n0 / 16 (blocks k0.. of the new window,
+      // cb per split) commits it.
+      const int len = n < W ? n : W;
+      const int owner = ((n0 >> 4) - (n - len) / 16) / cb;
+      if (split == owner) {
+        kb_new = n0 >> 4;
+        if (wave < 2) {
+          const bool key = wave == 0;
+          const float s = commit_block_wave(lane, key, key ? k_new : v_new, key ? kst : vst, n0, 1, kb_new, b, h,
+                                            map, key ? Kc : Vc, key ? ksc : vsc, wit,
+                                            (key && h == 0) ? pos + (int64_t)b * W : nullptr, dz);
+          if (lane == 0) sm_scale[wave] = s;
+        }
       }
-    } else if (threadIdx.x < 32) {  // staging row n0 mod 16: 16 vectors of 16 B per tensor
+    } else if (split == 0 && threadIdx.x < 32) {  // staging row n0 mod 16: 16 vectors of 16 B per tensor
       const int v16 = threadIdx.x & 15;
       const bool key = threadIdx.x < 16;
       const uint4* src = reinterpret_cast<const uint4*>(key ? k_new : v_new) + bh * 16 + v16;
       uint4* dst = reinterpret_cast<uint4*>(key ? kst : vst) + (bh * 16 + (n0 & 15)) * 16 + v16;
       *dst = *src;
     }
-    n = n0 + 1;
   }
   __syncthreads();
   const float sk_new = kb_new >= 0 ? sm_scale[0] : 0.f;
   const float sv_new = kb_new >= 0 ? sm_scale[1] : 0.f;
-  decode_int8_wg<NW, UB, PAGED, true, DITHER, true>(n, kb_new, sk_new, sv_new, Kc, Vc, ksc, vsc, wit, table,
-                                                    num_pages, q, nullptr, nullptr, H, W, cb, 1, kst, vst, out,
-                                                    cmax_out, tv, gate, tau, dz.req, dz.layer, delta);
+  decode_int8_wg<NW, UB, PAGED, FINAL, DITHER, true>(n, kb_new, sk_new, sv_new, Kc, Vc, ksc, vsc, wit, table,
+                                                     num_pages, q, nullptr, part, H, W, cb, nsplit_max, kst, vst,
+                                                     out, cmax_out, tv, gate, tau, dz.req, dz.layer, delta);
   if (threadIdx.x == 0 && n0 >= 0) {
-    if (atomicAdd(cnt + b, 1) == H - 1) {
+    if (atomicAdd(cnt + b, 1) == H * (int)gridDim.x - 1) {
       atomicExch(cnt + b, 0);
       np[b] = n0 + 1;
     }
@@ -640,6 +648,21 @@ __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
     p[i] = 0.f;
 }
 
+// The second launch of a plan with several splits per (b, h).
+hipError_t launch_merge_int8(const swa_cache& c, const void* q, float* out, float* cmax, float* tv, int32_t* gate,
+                             float tau, float delta, const float* part, const SplitPlan& plan, hipStream_t s) {
+  const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+  const uint16_t* kst = reinterpret_cast<const uint16_t*>(c.k_stage);
+  const uint16_t* vst = reinterpret_cast<const uint16_t*>(c.v_stage);
+  if (c.kind == SWA_KV_INT8_DITHER)
+    hipLaunchKernelGGL(merge_int8_kernel<true>, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst,
+                       q16, out, cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max, delta);
+  else
+    hipLaunchKernelGGL(merge_int8_kernel<false>, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst,
+                       q16, out, cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max, delta);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int decode_int8_round_blocks() { return SWA_INT8_NW * SWA_INT8_UB; }
@@ -647,37 +670,37 @@ int decode_int8_round_blocks() { return SWA_INT8_NW * SWA_INT8_UB; }
 hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
                                    float* out, float* cmax, float* tv, int32_t* gate, float tau, float delta,
                                    void* ws, const SplitPlan& plan, hipStream_t s) {
-  if (plan.nsplit_max != 1) {  // several splits per (b, h): the two ordinary launches
-    bool advanced = false;
-    hipError_t e = launch_append_int8(c, k_new, v_new, 1, s, &advanced);
-    if (e == hipSuccess && !advanced) e = launch_advance(c, 1, s);
-    if (e != hipSuccess) return e;
-    return launch_decode_int8(c, q, out, cmax, nullptr, tv, gate, tau, delta, ws, plan, s);
-  }
   constexpr int NW = SWA_INT8_NW, UB = SWA_INT8_UB;
   const bool paged = c.layout == SWA_LAYOUT_PAGED;
   const bool dither = c.kind == SWA_KV_INT8_DITHER;
+  const bool final_pass = plan.nsplit_max == 1;
   const Dither dz{dither ? c.request_id : nullptr, c.layer};
+  float* part = reinterpret_cast<float*>(ws);
   int32_t* cnt = step_counters(c, plan, ws);
-  const dim3 grid(1, c.H, c.B), block(NW * 64);
+  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
   const size_t lds = paged ? ((size_t)plan.unit_per_split + 1) * sizeof(int32_t) : 0;
   const int32_t* table = paged ? c.block_table : nullptr;
   const int64_t npages = paged ? c.num_pages : 0;
-#define SWA_STEP_LAUNCH(P, DI)                                                                                   \
-  hipLaunchKernelGGL((decode_step_int8_kernel<NW, UB, P, DI>), grid, block, lds, s,                             \
+#define SWA_STEP_LAUNCH(P, F, DI)                                                                                \
+  hipLaunchKernelGGL((decode_step_int8_kernel<NW, UB, P, F, DI>), grid, block, lds, s,                          \
                      reinterpret_cast<int8_t*>(c.k), reinterpret_cast<int8_t*>(c.v), c.k_scale, c.v_scale,      \
                      c.witness, c.next_position, c.pos, cnt, row_map(c),                                         \
                      reinterpret_cast<const uint16_t*>(k_new), reinterpret_cast<const uint16_t*>(v_new), dz,    \
-                     table, npages, reinterpret_cast<const uint16_t*>(q), c.H, c.W, plan.unit_per_split,        \
-                     reinterpret_cast<uint16_t*>(c.k_stage), reinterpret_cast<uint16_t*>(c.v_stage), out, cmax, \
-                     tv, gate, tau, delta)
+                     table, npages, reinterpret_cast<const uint16_t*>(q), part, c.H, c.W, plan.unit_per_split,  \
+                     plan.nsplit_max, reinterpret_cast<uint16_t*>(c.k_stage),                                    \
+                     reinterpret_cast<uint16_t*>(c.v_stage), out, cmax, tv, gate, tau, delta)
+#define SWA_STEP_LAUNCH_F(P, DI)                                                  \
+  if (final_pass) SWA_STEP_LAUNCH(P, true, DI); else SWA_STEP_LAUNCH(P, false, DI);
   if (paged) {
-    if (dither) SWA_STEP_LAUNCH(true, true); else SWA_STEP_LAUNCH(true, false);
+    if (dither) { SWA_STEP_LAUNCH_F(true, true) } else { SWA_STEP_LAUNCH_F(true, false) }
   } else {
-    if (dither) SWA_STEP_LAUNCH(false, true); else SWA_STEP_LAUNCH(false, false);
+    if (dither) { SWA_STEP_LAUNCH_F(false, true) } else { SWA_STEP_LAUNCH_F(false, false) }
   }
+#undef SWA_STEP_LAUNCH_F
 #undef SWA_STEP_LAUNCH
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || final_pass) return e;
+  return launch_merge_int8(c, q, out, cmax, tv, gate, tau, delta, part, plan, s);
 }
 
 hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, float* cmax, float* c_all,
@@ -726,13 +749,7 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
 #undef SWA_INT8_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || final_pass) return e;
-  if (dither)
-    hipLaunchKernelGGL(merge_int8_kernel<true>, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst,
-                       q16, out, cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max, delta);
-  else
-    hipLaunchKernelGGL(merge_int8_kernel<false>, dim3(c.H, c.B), dim3(256), 0, s, c.next_position, part, kst, vst,
-                       q16, out, cmax, tv, gate, tau, c.H, c.W, plan.unit_per_split, plan.nsplit_max, delta);
-  return hipGetLastError();
+  return launch_merge_int8(c, q, out, cmax, tv, gate, tau, delta, part, plan, s);
 }
 
 }  // namespace swa

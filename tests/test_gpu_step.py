@@ -1,6 +1,6 @@
-"""The fused decode step (decode_step_int8): one token appended per
-sequence and the INT8 decode, in one launch when the plan has one split per
-(b, h).
+"""The fused decode steps (decode_step_int8, decode_step): one token
+appended per sequence and the decode in one launch, plus the merge launch
+when the plan has several splits per (b, h).
 
 Its result must be bit for bit that of kv_append(T=1) followed by the
 separate decode (decode_attn_int8_witness_tv, or decode_attn_int8_dither):
@@ -8,10 +8,11 @@ every output, bound, TV value and gate, and the whole cache state (codes,
 scales, witness, staging rows, slot positions, next_position), after every
 step, on twin caches.  Ragged prefills make different sequences complete
 their blocks at different steps; the steps wrap the ring.  Shapes with
-B*H at or above the split target take the fused launch (one work-group per
-CU for INT8, eight for the dithered kind); a long-window shape takes the
-two-launch fallback.  A few decodes are also checked against the oracle,
-and a graph-captured step is replayed.
+B*H at or above the split target (one work-group per CU for INT8, eight
+for the dithered kind) have one split per (b, h); long-window shapes have
+several, so the block a token completes is committed by the split that
+decodes it and the staging row by split 0.  A few decodes are also checked
+against the oracle, and a graph-captured step is replayed.
 """
 
 import numpy as np
@@ -68,7 +69,9 @@ def separate(swa, c, kn, vn, q, tau, delta):
 @pytest.mark.parametrize("kind,B,H,W,layout", [("int8", 4, 64, 64, "ring"), ("int8", 4, 64, 64, "paged"),
                                                ("int8_dither", 32, 64, 64, "ring"),
                                                ("int8_dither", 32, 64, 64, "paged"),
-                                               ("int8", 1, 2, 2048, "ring")])
+                                               ("int8", 1, 2, 2048, "ring"), ("int8", 1, 2, 2048, "paged"),
+                                               ("int8_dither", 1, 2, 2048, "ring"),
+                                               ("int8_dither", 2, 3, 1024, "paged")])
 def test_fused_step_equals_append_then_decode(kind, B, H, W, layout):
     import sliding_window_attention_ring_amd as swa
     say("fused step", kind, B, H, W, layout)
@@ -150,11 +153,14 @@ def test_fused_step_headline_shape_and_graph():
 
 
 @pytest.mark.parametrize("kind,B,H,D,W,layout", [("bf16", 16, 32, 128, 64, "ring"), ("bf16", 16, 32, 128, 64, "paged"),
-                                                 ("fp32", 1, 2, 16, 4, "ring"), ("bf16", 1, 2, 64, 4096, "ring")])
+                                                 ("fp32", 1, 2, 16, 4, "ring"), ("bf16", 1, 2, 64, 4096, "ring"),
+                                                 ("bf16", 1, 2, 64, 4096, "paged"), ("fp32", 2, 3, 32, 1024, "ring")])
 def test_fused_row_step_equals_append_then_decode(kind, B, H, D, W, layout):
     """decode_step (bf16 / fp32 kinds) against kv_append + decode_attn on twin
     caches, bit for bit in the output and the ring state, over 3W ragged
-    steps; the last shape has several splits per (b, h) (two launches)."""
+    steps (at most 40 for long windows); the last three shapes have several
+    splits per (b, h), so the row is written by the split whose slots hold
+    it and a merge launch follows."""
     import sliding_window_attention_ring_amd as swa
     say("fused row step", kind, B, H, D, W, layout)
     dt = torch.float32 if kind == "fp32" else torch.bfloat16
@@ -188,14 +194,16 @@ def test_fused_row_step_equals_append_then_decode(kind, B, H, D, W, layout):
     assert swa.validate(cf) == 0
 
 
-@pytest.mark.parametrize("kind", ["int8", "int8_dither", "bf16"])
-def test_fused_step_mixed_with_other_operations(kind):
+@pytest.mark.parametrize("kind,B,H,W", [("int8", 4, 64, 64), ("int8_dither", 32, 64, 64), ("bf16", 4, 64, 64),
+                                         ("int8", 2, 2, 1024), ("int8_dither", 2, 2, 1024), ("bf16", 2, 2, 1024)])
+def test_fused_step_mixed_with_other_operations(kind, B, H, W):
     """Fused steps interleaved with truncations, multi-token appends and
     separate decodes on one cache (sharing its workspace); a twin takes the
     same operations with kv_append + the separate decode only.  Every output
-    and the whole state must agree bit for bit after every operation."""
+    and the whole state must agree bit for bit after every operation.  The
+    W=1024 shapes have several splits per (b, h)."""
     import sliding_window_attention_ring_amd as swa
-    B, H, W = (32, 64, 64) if kind == "int8_dither" else (4, 64, 64)
+    say("mixed operations", kind, B, H, W)
     rng = np.random.default_rng(99)
     g = torch.Generator().manual_seed(99)
     caches = []

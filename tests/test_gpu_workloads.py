@@ -229,3 +229,68 @@ def test_int8_dither_ctx32768():
         check_dither_decode(out[b, h].cpu().numpy(), float(cert[b, h]), b, h, f64(q[b, h]), k64, v64, n, wl.W, reqs[b],
                             cache.layer, delta, float(tv[b, h]), int(gate[b, h]), what=f"32k step n={n}")
     say("dither 32k steps ok, last n", n)
+
+
+def test_long_context_shard_16384_spiked():
+    """One GPU's share of the 131072 context split 8 ways: B=4, H=8,
+    W=16384 with 1% of keys x8, all 32 pairs, through decode_step (the
+    benchmark's call; several splits per pair, so append + decode + merge)."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.LONG_CTX_SHARD
+    dev = torch.device("cuda")
+    n = wl.prefill + 1
+    k_all = gen.tokens(wl, "k", n, device=dev)
+    v_all = gen.tokens(wl, "v", n, device=dev)
+    cache = swa.KVCache("bf16", wl.B, wl.H, wl.D, wl.W)
+    prefill(swa, cache, k_all, v_all, wl.prefill, 8192)
+    q = gen.query(wl, n - 1, device=dev)
+    out = swa.decode_step(cache, k_all[:, :, n - 1:n].contiguous(), v_all[:, :, n - 1:n].contiguous(), q)
+    out = out.cpu().numpy()
+    assert swa.validate(cache) == 0
+    assert host_bits(cache.next_position).tolist() == [n] * wl.B
+    q64 = f64(q)
+    worst = 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            k64, v64 = f64(k_all[b, h]), f64(v_all[b, h])
+            ref = attention.masked_attention(q64[b, h], np.arange(n), k64, v64, n - 1, wl.W)
+            worst = max(worst, assert_close(out[b, h], ref, f"ctx shard b={b} h={h}"))
+    say(f"context-shard max abs err {worst:.2e}")
+
+
+def test_int8_head_shard_ctx32768():
+    """One GPU's 4 of the 32 heads of the INT8 32k workload: B=16, H=4,
+    W=32768.  After prefill, 3 sampled pairs get the store and per-token bound
+    checks; then 20 decode_step_int8 calls (the benchmark's call; several
+    splits per pair, so the separate launches) at positions 32768..32787 check
+    one pair each, with the cache state validated every step."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.INT8_HEAD_SHARD
+    dev = torch.device("cuda")
+    total = wl.prefill + wl.steps
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("int8", wl.B, wl.H, wl.D, wl.W)
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(9)
+    n = wl.prefill
+    q = gen.query(wl, n - 1, device=dev)
+    out, cmax, c_all = swa.decode_attn_int8_witness(cache, q, want_c_all=True)
+    out, cmax, c_all, qh = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy(), f64(q)
+    for _ in range(3):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        say("int8 head shard store check", b, h)
+        check_int8_store(cache, b, h, k64, v64, n)
+        check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, qh[b, h], k64, v64, n, wl.W, "head shard")
+    for i in range(wl.steps):
+        q = gen.query(wl, n, device=dev)
+        out, cmax, _, _ = swa.decode_step_int8(cache, k_all[:, :, n:n + 1].contiguous(),
+                                               v_all[:, :, n:n + 1].contiguous(), q)
+        n += 1
+        assert swa.validate(cache) == 0
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]), None, b, h, f64(q[b, h]), k64, v64, n,
+                          wl.W, f"head shard step n={n}")
+    say("int8 head shard steps ok, last n", n)

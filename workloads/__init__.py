@@ -63,5 +63,14 @@ INT8_DITHER_32K = Workload(5, "int8-dither-ctx32768", "int8_dither", B=16, H=32,
                            prefill=32768, steps=20, rope_base=10000.0, prefill_chunk=8192,
                            note="the INT8 32k workload with Philox subtractive dither (Tier B)")
 
+# One GPU's share when a workload is spread over 8 GPUs (the kernels at a
+# shard's real shape; the cross-GPU exchange itself is not built).
+LONG_CTX_SHARD = Workload(7, "long-ctx-131072-bf16-ctx-shard-1of8", "bf16", B=4, H=8, D=128, W=16384,
+                          prefill=16384, spike_frac=0.01, spike_mul=8.0,
+                          note="one GPU's 16384 slots of the 131072 context split 8 ways")
+INT8_HEAD_SHARD = Workload(8, "int8-witness-ctx32768-head-shard-1of8", "int8", B=16, H=4, D=128, W=32768,
+                           prefill=32768, steps=20, rope_base=10000.0, prefill_chunk=8192,
+                           note="one GPU's 4 of the 32 heads of the INT8 32k workload split 8 ways")
+
 ALL = {w.name: w for w in (TINY, FULL_RAGGED, RING, LONG, INT8_32K, BF16_32K, INT8_32K_PAGED, BF16_32K_PAGED,
-                           INT8_DITHER_32K)}
+                           INT8_DITHER_32K, LONG_CTX_SHARD, INT8_HEAD_SHARD)}
