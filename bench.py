@@ -243,7 +243,7 @@ def main():
         del a, b
 
     # One call per step: kv_append of the token and the decode, fused into
-    # one launch when the plan has one split per (b, h).
+    # one launch (plus the merge launch when a (b, h) has several splits).
     fuse = not args.no_fuse
     dither = wl.kind == "int8_dither"
 
