@@ -257,3 +257,71 @@ def test_fused_step_mixed_with_other_operations(kind, B, H, W):
         for name in names:
             assert torch.equal(getattr(cf, name), getattr(cs, name)), f"op {op}: {name}"
     assert swa.validate(cf) == 0
+
+
+@pytest.mark.parametrize("kind", ["int8", "int8_dither", "bf16"])
+def test_fused_step_several_splits_graph(kind):
+    """B=2, H=3, W=1024 (several splits per (b, h)): the fused step and its
+    merge launch captured as one graph and replayed over 40 tokens, crossing
+    block commits and the ring wrap, equal the eager kv_append + decode on a
+    twin cache after every replay (outputs and the whole cache state)."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, W, steps = 2, 3, 1024, 40
+    say("several-split graph", kind)
+    lens = [1000, 1030]  # one sequence fills the ring during the replays, the other has wrapped
+    N = max(lens) + steps
+    g = torch.Generator(device="cuda").manual_seed(11)
+    k = torch.randn((B, H, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qs = torch.randn((steps, B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache(kind, B, H, 128, W)
+        for name in ("k", "v", "k_scale", "v_scale", "witness", "k_stage", "v_stage"):
+            if getattr(c, name, None) is not None:
+                getattr(c, name).zero_()
+        for b, n in enumerate(lens):
+            swa.kv_append(c.seq_view(b), k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous())
+        caches.append(c)
+    cg, ce = caches
+    names = ["k", "v", "pos", "next_position"] + (["k_scale", "v_scale", "k_stage", "v_stage"] if kind != "bf16" else []) \
+        + (["witness"] if kind == "int8" else [])
+    sk = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    sv = torch.empty_like(sk)
+    sq = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    cmax = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    tv = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    gate = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    ws = cg.workspace()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        if kind == "bf16":
+            swa.decode_step(cg, sk, sv, sq, out=out, ws=ws)
+        else:
+            swa.decode_step_int8(cg, sk, sv, sq, delta=1e-3, out=out, cmax=cmax, tv=tv, gate=gate, ws=ws)
+    torch.cuda.synchronize()
+    assert host_bits(cg.next_position).tolist() == lens  # capture does not run the step
+    for i in range(steps):
+        kn = torch.stack([k[b, :, n + i:n + i + 1] for b, n in enumerate(lens)]).contiguous()
+        vn = torch.stack([v[b, :, n + i:n + i + 1] for b, n in enumerate(lens)]).contiguous()
+        sk.copy_(kn); sv.copy_(vn); sq.copy_(qs[i])
+        graph.replay()
+        swa.kv_append(ce, kn, vn)
+        if kind == "bf16":
+            eo = (swa.decode_attn(ce, qs[i]),)
+            go = (out,)
+        elif kind == "int8":
+            eo = swa.decode_attn_int8_witness_tv(ce, qs[i])[:4]
+            go = (out, cmax, tv, gate)
+        else:
+            eo = swa.decode_attn_int8_dither(ce, qs[i], delta=1e-3)
+            go = (out, cmax, tv, gate)
+        torch.cuda.synchronize()
+        for a, b_ in zip(go, eo):
+            assert torch.equal(a, b_), f"replay {i}"
+        for name in names:
+            assert torch.equal(getattr(cg, name), getattr(ce, name)), f"replay {i}: {name}"
+    assert host_bits(cg.next_position).tolist() == [n + steps for n in lens]
+    assert swa.validate(cg) == 0
