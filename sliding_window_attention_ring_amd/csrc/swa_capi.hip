@@ -72,10 +72,10 @@ int check_cache(const swa_cache* c) {
 // short ones: each split pays a query load, its pipeline fill and a partial
 // write, and the merge reads every partial.  The dithered INT8 decode is the
 // exception: it carries about 1.5x the VALU work per byte of the witness
-// decode, and 8 work-groups per CU (more waves to interleave ALU and loads)
-// ran it 1.7% faster on MI355X.  SWA_TARGET_WGS overrides the target for
-// every kind; it is read once per process so workspace sizes stay
-// consistent.
+// decode, and 4 work-groups per CU (two splits per (b, h) at B*H = 512) ran
+// its fused step up to 0.6% faster than 1 per CU on MI355X; 8 per CU was
+// 5% slower on some parts.  SWA_TARGET_WGS overrides the target for every
+// kind; it is read once per process so workspace sizes stay consistent.
 int target_wgs(int kind) {
   static int env = [] {
     const char* s = getenv("SWA_TARGET_WGS");
@@ -90,7 +90,7 @@ int target_wgs(int kind) {
     return n;
   }();
   if (env > 0) return env;
-  return kind == SWA_KV_INT8_DITHER ? 8 * cus : cus;
+  return kind == SWA_KV_INT8_DITHER ? 4 * cus : cus;
 }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }

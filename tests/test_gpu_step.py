@@ -8,7 +8,7 @@ every output, bound, TV value and gate, and the whole cache state (codes,
 scales, witness, staging rows, slot positions, next_position), after every
 step, on twin caches.  Ragged prefills make different sequences complete
 their blocks at different steps; the steps wrap the ring.  Shapes with
-B*H at or above the split target (one work-group per CU for INT8, eight
+B*H at or above the split target (one work-group per CU for INT8, four
 for the dithered kind) have one split per (b, h); long-window shapes have
 several, so the block a token completes is committed by the split that
 decodes it and the staging row by split 0.  A few decodes are also checked
