@@ -258,8 +258,8 @@ int decode_step_int8(const swa_cache *c, const void *k_new, const void *v_new, c
 
 /* Workspace bytes the decode entry points need for this cache shape: the
  * split partials (B*H*nsplit*(D+4) floats) padded to 256 bytes, then B
- * int32 counters for decode_step and decode_step_int8, padded to 256
- * bytes.  0 for an invalid descriptor. */
+ * int32 counters for decode_step and decode_step_int8, one per 256-byte
+ * line.  0 for an invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);
 
 /* Zero-fill a workspace.  The decode entry points overwrite the partials

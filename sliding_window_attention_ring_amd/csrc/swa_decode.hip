@@ -309,8 +309,9 @@ __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
   decode_rows_wg<T, D, NW, U, PAGED, FINAL>(n0 >= 0 ? n0 + 1 : n0, K, V, map.table, num_pages, q, out, part, H, W,
                                             chunk, nsplit_max);
   if (threadIdx.x == 0 && n0 >= 0) {
-    if (atomicAdd(cnt + b, 1) == H * (int)gridDim.x - 1) {
-      atomicExch(cnt + b, 0);
+    int32_t* c = cnt + (int64_t)b * kCounterStride;
+    if (atomicAdd(c, 1) == H * (int)gridDim.x - 1) {
+      atomicExch(c, 0);
       np[b] = n0 + 1;
     }
   }

@@ -608,8 +608,9 @@ __global__ __launch_bounds__(NW * 64) void decode_step_int8_kernel(
                                                      num_pages, q, nullptr, part, H, W, cb, nsplit_max, kst, vst,
                                                      out, cmax_out, tv, gate, tau, dz.req, dz.layer, delta);
   if (threadIdx.x == 0 && n0 >= 0) {
-    if (atomicAdd(cnt + b, 1) == H * (int)gridDim.x - 1) {
-      atomicExch(cnt + b, 0);
+    int32_t* c = cnt + (int64_t)b * kCounterStride;
+    if (atomicAdd(c, 1) == H * (int)gridDim.x - 1) {
+      atomicExch(c, 0);
       np[b] = n0 + 1;
     }
   }

@@ -125,7 +125,7 @@ def test_argument_checks_return_codes():
 
 def test_workspace_size_follows_split_plan():
     """Workspace = B*H*nsplit*(D+4) floats of split partials, padded to 256
-    bytes, then B int32 step counters, padded to 256 bytes."""
+    bytes, then B int32 step counters, one per 256-byte line."""
     from sliding_window_attention_ring_amd._capi import lib
     L = lib()
     for kw in [dict(kind=0, B=16, H=32, D=128, W=32768), dict(kind=2, B=16, H=32, D=128, W=32768),
@@ -133,7 +133,7 @@ def test_workspace_size_follows_split_plan():
         d = desc(**kw)
         nb = L.swa_workspace_bytes(ctypes.byref(d))
         per = kw["B"] * kw["H"] * (kw["D"] + 4) * 4
-        counters = (kw["B"] * 4 + 255) // 256 * 256
+        counters = kw["B"] * 256
         assert nb % 256 == 0 and nb > counters
         partials = nb - counters
         assert any((ns * per + 255) // 256 * 256 == partials for ns in range(1, kw["W"] + 1))
