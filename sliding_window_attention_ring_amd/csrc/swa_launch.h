@@ -44,7 +44,7 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
                               const SplitPlan& plan, hipStream_t s);
 
 // One decode step (kv_append of one token, then the INT8 decode) in one
-// launch when the plan has a single split per (b, h), else the two launches.
+// launch, plus the merge launch when the plan has several splits per (b, h).
 hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
                                    float* out, float* cmax, float* tv, int32_t* gate, float tau, float delta,
                                    void* ws, const SplitPlan& plan, hipStream_t s);
