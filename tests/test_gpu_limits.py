@@ -71,13 +71,14 @@ def spike_bound(n_vis, vmax, out2, logit):
     return (n_vis - 2) * (vmax + float(np.max(np.abs(out2)))) / (2.0 * np.exp(logit))
 
 
-def test_bf16_region_at_4gib():
+@pytest.mark.parametrize("layout", ["ring", "paged"])
+def test_bf16_region_at_4gib(layout):
     import sliding_window_attention_ring_amd as swa
     W = (1 << 24) - 16                      # W * D * 2 bytes = 4 GiB - 4 KiB per (b, h)
     n = W + 5                               # wraps: the window is positions [5, W + 4]
     spikes = [W - 1, 5]                     # slot W - 1 (highest offset) and the oldest visible position
-    say("bf16 W", W, "n", n)
-    cache = swa.KVCache("bf16", 1, 1, D, W)
+    say("bf16 W", W, "n", n, layout)
+    cache = swa.KVCache("bf16", 1, 1, D, W, layout=layout)
     vmax, vrows, _ = fill(swa, cache, n - 1, spikes, seed=41)
     kn = torch.zeros((1, 1, 1, D), dtype=torch.bfloat16, device="cuda")
     vn = torch.randn((1, 1, 1, D), generator=torch.Generator(device="cuda").manual_seed(42),
@@ -89,6 +90,8 @@ def test_bf16_region_at_4gib():
     assert host_bits(cache.next_position).tolist() == [n]
     assert swa.validate(cache) == 0
     assert int(cache.pos[0, W - 1]) == W - 1 and int(cache.pos[0, 4]) == n - 1
+    if layout == "paged":  # the spike rows sit in shuffled pages anywhere in the 4 GiB pools
+        say("pages of the spike slots", [int(cache.block_table[0, p % W // 16]) for p in spikes])
     kk = np.full((2, D), SPIKE)
     out2 = attention.plain_attention(np.ones(D), kk, np.stack([vrows[p] for p in spikes]))
     logit = SPIKE * D / np.sqrt(D)
@@ -99,14 +102,14 @@ def test_bf16_region_at_4gib():
     del cache
 
 
-@pytest.mark.parametrize("kind", ["int8", "int8_dither"])
-def test_int8_region_at_4gib(kind):
+@pytest.mark.parametrize("kind,layout", [("int8", "ring"), ("int8_dither", "ring"), ("int8", "paged")])
+def test_int8_region_at_4gib(kind, layout):
     import sliding_window_attention_ring_amd as swa
     W = 33554416                            # W * D code bytes = 4 GiB - 2 KiB per (b, h)
     n = W + 21                              # wraps; window [21, W + 20]; 5 staged tokens after the step
     spikes = [W - 1, 40]                    # the last slot of the ring and a block near its start
-    say(kind, "W", W, "n", n)
-    cache = swa.KVCache(kind, 1, 1, D, W)
+    say(kind, "W", W, "n", n, layout)
+    cache = swa.KVCache(kind, 1, 1, D, W, layout=layout)
     vmax, _, vblocks = fill(swa, cache, n - 1, spikes, seed=43)
     kn = torch.zeros((1, 1, 1, D), dtype=torch.bfloat16, device="cuda")
     vn = torch.zeros((1, 1, 1, D), dtype=torch.bfloat16, device="cuda")
@@ -162,7 +165,7 @@ def test_int8_region_at_4gib(kind):
         # exact one: allow sum_b ||q_b|| 2^-24 / sqrt(D) on top of the relative pad.
         slack = 16 * np.sqrt(8.0) * 2.0 ** -24 / np.sqrt(D)
         assert cm <= max(c_or) * (1 + 2.0 ** -9) + slack, (cm, c_or)
-        ca = c_all.cpu().numpy()[0, 0]
+        ca = c_all.cpu().numpy()[0, 0]  # slot-indexed in both layouts
         for i, p in enumerate(spikes):
             assert ca[p % W] >= e_true[i]
         zero = np.ones(W, dtype=bool)
