@@ -173,3 +173,60 @@ def test_int8_region_at_4gib(kind, layout):
         assert not np.any(ca[zero]), "zero-key tokens have c_t = 0"
     say(f"{kind} W={W}: max abs err {err:.2e}, bound {cm:.3e} >= true {np.max(e_true):.3e}")
     del cache
+
+
+@pytest.mark.parametrize("B,H", [(65535, 1), (1, 65535)])
+def test_row_cache_at_the_grid_limits(B, H):
+    """B or H at 65535, the largest the descriptor accepts (grid dimension
+    limits): fp32, D=16, W=4, six fused steps from an empty cache (unfilled,
+    full, overwritten); 64 sampled (b, h) pairs per step against the oracle's
+    full-history masked attention, the ring state everywhere through
+    swa_validate."""
+    import sliding_window_attention_ring_amd as swa
+    W, steps, Dd = 4, 6, 16
+    say("row cache grid limits", B, H)
+    g = torch.Generator(device="cuda").manual_seed(B + 7 * H)
+    k = torch.randn((B, H, steps, Dd), generator=g, device="cuda")
+    v = torch.randn((B, H, steps, Dd), generator=g, device="cuda")
+    qs = torch.randn((steps, B, H, Dd), generator=g, device="cuda")
+    cache = swa.KVCache("fp32", B, H, Dd, W)
+    rng = np.random.default_rng(B + H)
+    for t in range(steps):
+        out = swa.decode_step(cache, k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous(), qs[t])
+        assert swa.validate(cache) == 0
+        idx = [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(64)]
+        o = out.cpu().numpy()
+        for b, h in idx:
+            ref = attention.masked_attention(f64(qs[t, b, h]), np.arange(t + 1), f64(k[b, h, :t + 1]),
+                                             f64(v[b, h, :t + 1]), t, W)
+            assert_close(o[b, h], ref, f"grid limits B={B} H={H} t={t} b={b} h={h}")
+    assert host_bits(cache.next_position).tolist() == [steps] * B
+
+
+def test_int8_cache_at_the_head_limit():
+    """H = 65535 INT8 heads (one sequence, W = 16, D = 128): 18 fused steps
+    from an empty cache commit one block for every head at step 16 (131070
+    quantize tasks in the step kernels); sampled heads against the oracle's
+    INT8 decode with their bound checked, stores checked bit-exactly."""
+    import sliding_window_attention_ring_amd as swa
+    from tests.gpu_util import check_int8_decode, check_int8_store
+    B, H, W, steps = 1, 65535, 16, 18
+    g = torch.Generator(device="cuda").manual_seed(99)
+    k = torch.randn((B, H, steps, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, steps, D), generator=g, device="cuda").to(torch.bfloat16)
+    qs = torch.randn((steps, B, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    cache = swa.KVCache("int8", B, H, D, W)
+    rng = np.random.default_rng(5)
+    for t in range(steps):
+        out, cmax, _, _ = swa.decode_step_int8(cache, k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous(),
+                                               qs[t])
+        assert swa.validate(cache) == 0
+        if t in (0, 14, 15, 16, 17):
+            o, cm = out.cpu().numpy(), cmax.cpu().numpy()
+            for h in [0, H - 1] + [int(x) for x in rng.integers(H, size=6)]:
+                k64, v64 = f64(k[0, h, :t + 1]), f64(v[0, h, :t + 1])
+                check_int8_decode(o[0, h], cm[0, h], None, 0, h, f64(qs[t, 0, h]), k64, v64, t + 1, W,
+                                  f"head limit t={t}")
+                if t == steps - 1:
+                    check_int8_store(cache, 0, h, k64, v64, t + 1)
+    assert host_bits(cache.next_position).tolist() == [steps]
