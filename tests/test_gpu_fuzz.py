@@ -1,8 +1,9 @@
 """Seeded fuzz of mixed operations against per-sequence oracle histories:
 appends of random sizes (whole batch or one sequence through a view),
-truncations (exact or fallback) and decodes, on bf16 and INT8 caches of
-both layouts.  After every operation the ring state is compared
-bit-exactly and every decode output with the oracle."""
+truncations (exact or fallback), fused decode steps and decodes, on bf16
+and INT8 caches of both layouts, with one or several splits per (b, h).
+After every operation the ring state is compared bit-exactly and every
+decode output with the oracle."""
 
 import numpy as np
 import pytest
@@ -22,7 +23,11 @@ def _gpu():
 
 @pytest.mark.parametrize("kind,layout,W,seed", [("bf16", "ring", 48, 1), ("bf16", "paged", 64, 2),
                                                 ("int8", "ring", 64, 3), ("int8", "paged", 48, 4),
-                                                ("int8_dither", "ring", 48, 5), ("int8_dither", "paged", 64, 6)])
+                                                ("int8_dither", "ring", 48, 5), ("int8_dither", "paged", 64, 6),
+                                                # several splits per (b, h) in the decode plans
+                                                ("bf16", "paged", 1024, 7), ("int8", "ring", 1024, 8),
+                                                ("int8_dither", "paged", 1024, 9), ("bf16", "ring", 2048, 10),
+                                                ("int8", "paged", 2048, 11), ("int8_dither", "ring", 1024, 12)])
 def test_mixed_operation_fuzz(kind, layout, W, seed):
     import sliding_window_attention_ring_amd as swa
     rng = np.random.default_rng(seed)
@@ -31,6 +36,37 @@ def test_mixed_operation_fuzz(kind, layout, W, seed):
     cache = swa.KVCache(kind, B, H, D, W, layout=layout)
     hist_k = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
     hist_v = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
+
+    def check_outputs(op, q, outs, ns, step):
+        """Every (b, h) output (and bound) of a decode or fused step against the oracle."""
+        q64 = f64(q)
+        what = f"op {op}{' (step)' if step else ''}"
+        if kind == "int8_dither":
+            out, cert, tv, gate = (x.cpu().numpy() for x in outs)
+            reqs = request_ids(cache)
+            for b in range(B):
+                for h in range(H):
+                    if ns[b] == 0:
+                        assert not out[b, h].any() and cert[b, h] == 0
+                        continue
+                    check_dither_decode(out[b, h], cert[b, h], b, h, q64[b, h], f64(hist_k[b][h]),
+                                        f64(hist_v[b][h]), ns[b], W, reqs[b], cache.layer, 1e-3, tv[b, h],
+                                        gate[b, h], what=what)
+        elif kind == "int8":
+            out, cmax = outs[0].cpu().numpy(), outs[1].cpu().numpy()
+            c_all = None if step else outs[2].cpu().numpy()
+            for b in range(B):
+                for h in range(H):
+                    check_int8_decode(out[b, h], cmax[b, h], None if c_all is None else c_all[b, h], b, h,
+                                      q64[b, h], f64(hist_k[b][h]), f64(hist_v[b][h]), ns[b], W, what=what)
+        else:
+            out = outs[0].cpu().numpy()
+            for b in range(B):
+                if ns[b] == 0:
+                    assert not out[b].any()
+                else:
+                    assert_close(out[b], oracle_out(f64(hist_k[b]), f64(hist_v[b]), q64[b], ns[b], W), what)
+
     for op in range(40):
         r = rng.random()
         if r < 0.45:  # whole-batch append
@@ -49,6 +85,20 @@ def test_mixed_operation_fuzz(kind, layout, W, seed):
             swa.kv_append(cache.seq_view(b), k.cuda(), v.cuda())
             hist_k[b] = torch.cat([hist_k[b], k[0]], dim=1)
             hist_v[b] = torch.cat([hist_v[b], v[0]], dim=1)
+        elif r < 0.8 and rng.random() < 0.5:  # fused decode step: one token per sequence, then the decode
+            k = torch.randn((B, H, 1, D), generator=g).to(torch.bfloat16)
+            v = torch.randn((B, H, 1, D), generator=g).to(torch.bfloat16)
+            q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+            if kind == "bf16":
+                outs = (swa.decode_step(cache, k.cuda(), v.cuda(), q.cuda()),)
+            elif kind == "int8":
+                outs = swa.decode_step_int8(cache, k.cuda(), v.cuda(), q.cuda(), want_tv=True)
+            else:
+                outs = swa.decode_step_int8(cache, k.cuda(), v.cuda(), q.cuda(), delta=1e-3, want_tv=True)
+            for b in range(B):
+                hist_k[b] = torch.cat([hist_k[b], k[b]], dim=1)
+                hist_v[b] = torch.cat([hist_v[b], v[b]], dim=1)
+            check_outputs(op, q, outs, [hk.shape[1] for hk in hist_k], step=True)
         elif r < 0.8:  # truncation
             ns = [h.shape[1] for h in hist_k]
             cuts = [int(rng.integers(0, n + 1)) for n in ns]
@@ -79,30 +129,10 @@ def test_mixed_operation_fuzz(kind, layout, W, seed):
             check_ring_rows(cache, kb, vb, np.array(ns))
         if rng.random() < 0.6:  # decode
             q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
-            q64 = f64(q)
             if kind == "int8_dither":
-                out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q.cuda(), delta=1e-3)
-                out, cert, tv, gate = out.cpu().numpy(), cert.cpu().numpy(), tv.cpu().numpy(), gate.cpu().numpy()
-                reqs = request_ids(cache)
-                for b in range(B):
-                    for h in range(H):
-                        if ns[b] == 0:
-                            assert not out[b, h].any() and cert[b, h] == 0
-                            continue
-                        check_dither_decode(out[b, h], cert[b, h], b, h, q64[b, h], f64(hist_k[b][h]),
-                                            f64(hist_v[b][h]), ns[b], W, reqs[b], cache.layer, 1e-3, tv[b, h],
-                                            gate[b, h], what=f"op {op}")
+                outs = swa.decode_attn_int8_dither(cache, q.cuda(), delta=1e-3)
             elif kind == "int8":
-                out, cmax, c_all = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
-                out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
-                for b in range(B):
-                    for h in range(H):
-                        check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, q64[b, h], f64(hist_k[b][h]),
-                                          f64(hist_v[b][h]), ns[b], W, what=f"op {op}")
+                outs = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
             else:
-                out = swa.decode_attn(cache, q.cuda()).cpu().numpy()
-                for b in range(B):
-                    if ns[b] == 0:
-                        assert not out[b].any()
-                    else:
-                        assert_close(out[b], oracle_out(f64(hist_k[b]), f64(hist_v[b]), q64[b], ns[b], W), f"op {op}")
+                outs = (swa.decode_attn(cache, q.cuda()),)
+            check_outputs(op, q, outs, ns, step=False)
