@@ -184,7 +184,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the decode step needs no exchange, see the design notes for how it would shard.",
+              "the decode step needs no exchange when heads or sequences are split over GPUs.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -7,7 +7,7 @@ attention of [Lean-SWA] §2.1.  From the same history it derives the state a
 fixed ring of ``W`` slots must be in ([Lean-SWA] §3.4) and, for the INT8
 cache, the codes, scales, witnesses and the exact staging tokens.
 
-Readings taken (also listed in the design notes):
+Readings taken:
 * Positions are 0-based and contiguous; token ``j`` of a sequence has
   position ``j`` and ``next_position`` is the number of tokens appended.
 * A decode step appends first and then attends, so the query of the step at
