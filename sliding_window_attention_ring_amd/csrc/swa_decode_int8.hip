@@ -168,13 +168,37 @@ constexpr float kDitherBeta = 0x1p-9f + 0x1p-16f;
 // DITHER: CM is the largest key scale S of the visible blocks, and the bound
 // written to cmax_out is the Tier B certificate built from S, the query
 // norms, n_q and delta (see the top of this file).
+// The staging-tail inputs of the last stage, loaded ahead by the merge
+// kernel so that their latency overlaps the loads of the split partials:
+// thread t (< 256)'s 8 dims of staged key row t/16 and of q, and for t < D
+// the staged values of dim t.  All 16 staging rows are allocated, so the
+// loads need no guard (rows at or past the staged count are read but not
+// used), which lets them all be in flight at once.
+struct StageRows {
+  uint4 k, q;
+  float v[15];
+};
+
+__device__ __forceinline__ void load_stage(StageRows& st, int t, int64_t bh, const uint16_t* kst,
+                                           const uint16_t* vst, const uint16_t* q) {
+  const int tok = t >> 4, v16 = t & 15;
+  if (t < 256) {
+    st.k = reinterpret_cast<const uint4*>(kst + (bh * 16 + tok) * D)[v16];
+    st.q = reinterpret_cast<const uint4*>(q + bh * D)[v16];
+  }
+  if (t < D) {
+#pragma unroll
+    for (int i = 0; i < 15; ++i) st.v[i] = bf16_to_f32(vst[(bh * 16 + i) * D + t]);
+  }
+}
+
 template <bool DITHER>
 __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, float L, float A, float CM,
                                             float* sm_s, const uint16_t* __restrict__ kst,
                                             const uint16_t* __restrict__ vst, const uint16_t* __restrict__ q,
                                             float* __restrict__ out, float* __restrict__ cmax_out,
                                             float* __restrict__ tv, int32_t* __restrict__ gate, float tau,
-                                            int W, float delta) {
+                                            int W, float delta, const StageRows* pre = nullptr) {
   const float qscale = kLog2e / sqrtf((float)D);
   const int ns = n - (n / 16) * 16;
   if (ns > 0) {
@@ -183,8 +207,8 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
     float d = 0.f;
     if (tok < ns) {
       float f[8], qv[8];
-      unpack8(reinterpret_cast<const uint4*>(kst + (bh * 16 + tok) * D)[v16], f);
-      unpack8(reinterpret_cast<const uint4*>(q + bh * D)[v16], qv);
+      unpack8(pre ? pre->k : reinterpret_cast<const uint4*>(kst + (bh * 16 + tok) * D)[v16], f);
+      unpack8(pre ? pre->q : reinterpret_cast<const uint4*>(q + bh * D)[v16], qv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(qv[e] * qscale, f[e], d);
     }
@@ -198,10 +222,21 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
       const float sc = exp2_fast(M - Mn);
       L *= sc;
       A *= sc;
-      for (int i = 0; i < ns; ++i) {
-        const float p = exp2_fast(sm_s[i] - Mn);
-        L += p;
-        A = fmaf(p, bf16_to_f32(vst[(bh * 16 + i) * D + t]), A);
+      if (pre) {
+#pragma unroll
+        for (int i = 0; i < 15; ++i) {
+          if (i < ns) {
+            const float p = exp2_fast(sm_s[i] - Mn);
+            L += p;
+            A = fmaf(p, pre->v[i], A);
+          }
+        }
+      } else {
+        for (int i = 0; i < ns; ++i) {
+          const float p = exp2_fast(sm_s[i] - Mn);
+          L += p;
+          A = fmaf(p, bf16_to_f32(vst[(bh * 16 + i) * D + t]), A);
+        }
       }
     }
   }
@@ -635,13 +670,15 @@ __global__ __launch_bounds__(256) void merge_int8_kernel(
   const int nbr = nb > k0 ? nb - k0 : 0;
   int nsplit = (nbr + cb - 1) / cb;
   if (nsplit < 1) nsplit = 1;
+  StageRows st;
+  load_stage(st, t, bh, kst, vst, q);  // issued before the partial loads
   float M = kNegBig, L = 0.f, A = 0.f, CM = 0.f;
   if (t < D) {
     const float* pp = part + bh * nsplit_max * PF;
     merge_partials<PF>(pp, nsplit, t, M, L, A);
     for (int sp = 0; sp < nsplit; ++sp) CM = fmaxf(CM, pp[sp * PF + 2]);
   }
-  finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta);
+  finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta, &st);
 }
 
 __global__ void fill_zero_f32(float* __restrict__ p, int64_t n) {
