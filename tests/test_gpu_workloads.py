@@ -32,7 +32,9 @@ def prefill(swa, cache, k_all, v_all, n, chunk):
 
 
 def test_full_cache_ragged_4096():
-    """B=8, H=32, D=128, capacity 4096, lengths U{1024..4096}: all 256 pairs."""
+    """B=8, H=32, D=128, capacity 4096, lengths U{1024..4096}: all 256 pairs,
+    after the per-sequence prefill and after one fused step (decode_step, the
+    benchmark's call; a sequence at length 4096 wraps)."""
     import sliding_window_attention_ring_amd as swa
     wl = workloads.FULL_RAGGED
     lens = gen.ragged_lengths(wl)
@@ -54,12 +56,29 @@ def test_full_cache_ragged_4096():
         for h in range(wl.H):
             ref = attention.masked_attention(q64[b, h], np.arange(n), k64[h], v64[h], n - 1, wl.W)
             worst = max(worst, assert_close(out[b, h], ref, f"ragged b={b} h={h}"))
+    # one fused step (the benchmark's call): every sequence appends a token at its own position
+    g = torch.Generator(device="cuda").manual_seed(21)
+    kn = torch.randn((wl.B, wl.H, 1, wl.D), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((wl.B, wl.H, 1, wl.D), generator=g, device=dev).to(torch.bfloat16)
+    q2 = gen.query(wl, 1, device=dev)
+    out2 = swa.decode_step(cache, kn, vn, q2).cpu().numpy()
+    assert host_bits(cache.next_position).tolist() == (lens + 1).tolist()
+    assert swa.validate(cache) == 0
+    q64 = f64(q2)
+    for b, n in enumerate(lens):
+        k64 = np.concatenate([f64(k_all[b, :, :n]), f64(kn[b])], axis=1)
+        v64 = np.concatenate([f64(v_all[b, :, :n]), f64(vn[b])], axis=1)
+        for h in range(wl.H):
+            ref = attention.masked_attention(q64[b, h], np.arange(n + 1), k64[h], v64[h], n, wl.W)
+            worst = max(worst, assert_close(out2[b, h], ref, f"ragged step b={b} h={h}"))
     say(f"ragged max abs err {worst:.2e}")
 
 
 def test_ring_w4096_positions_8192_to_8447():
     """B=16, H=32, W=4096: prefill 0..8191 in two chunks, then 256 append+attend
-    steps; every step checks 4 sampled pairs and the position invariant; ring
+    steps, alternately the fused decode_step (the benchmark's call) and
+    kv_append + decode_attn; every step checks 4 sampled pairs and the
+    position invariant; ring
     bits of sampled sequences are compared at the first, a middle and the
     last step.  The sampled pairs rotate over a fixed seeded set of 8."""
     import sliding_window_attention_ring_amd as swa
@@ -76,9 +95,13 @@ def test_ring_w4096_positions_8192_to_8447():
     worst = 0.0
     for i in range(wl.steps):
         p = wl.prefill + i
-        swa.kv_append(cache, k_all[:, :, p:p + 1].contiguous(), v_all[:, :, p:p + 1].contiguous())
         q = gen.query(wl, p, device=dev)
-        out = swa.decode_attn(cache, q)
+        kn, vn = k_all[:, :, p:p + 1].contiguous(), v_all[:, :, p:p + 1].contiguous()
+        if i % 2 == 0:  # the benchmark's call: the fused step
+            out = swa.decode_step(cache, kn, vn, q)
+        else:
+            swa.kv_append(cache, kn, vn)
+            out = swa.decode_attn(cache, q)
         assert swa.validate(cache) == 0, f"step {p}"
         outh = out.cpu().numpy()
         qh = f64(q)
@@ -97,7 +120,9 @@ def test_ring_w4096_positions_8192_to_8447():
 
 
 def test_long_context_131072_spiked():
-    """B=4, H=8, W=131072 with 1% of keys x8: all 32 pairs."""
+    """B=4, H=8, W=131072 with 1% of keys x8: all 32 pairs, after prefill and
+    after one fused step (decode_step, the benchmark's call) that wraps the
+    ring."""
     import sliding_window_attention_ring_amd as swa
     wl = workloads.LONG
     dev = torch.device("cuda")
@@ -115,12 +140,26 @@ def test_long_context_131072_spiked():
             k64, v64 = f64(k_all[b, h]), f64(v_all[b, h])
             ref = attention.masked_attention(q64[b, h], np.arange(wl.W), k64, v64, wl.W - 1, wl.W)
             worst = max(worst, assert_close(out[b, h], ref, f"long b={b} h={h}"))
+    # one fused step (the benchmark's call): position 131072 overwrites slot 0
+    g = torch.Generator(device="cuda").manual_seed(22)
+    kn = torch.randn((wl.B, wl.H, 1, wl.D), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((wl.B, wl.H, 1, wl.D), generator=g, device=dev).to(torch.bfloat16)
+    q2 = gen.query(wl, wl.W, device=dev)
+    out2 = swa.decode_step(cache, kn, vn, q2).cpu().numpy()
+    assert swa.validate(cache) == 0
+    q64 = f64(q2)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            k64 = np.concatenate([f64(k_all[b, h]), f64(kn[b, h])])
+            v64 = np.concatenate([f64(v_all[b, h]), f64(vn[b, h])])
+            ref = attention.masked_attention(q64[b, h], np.arange(wl.W + 1), k64, v64, wl.W, wl.W)
+            worst = max(worst, assert_close(out2[b, h], ref, f"long step b={b} h={h}"))
     say(f"long-context max abs err {worst:.2e}")
 
 
 def test_bf16_ctx32768_sampled():
     """B=16, H=32, W=32768 bf16 (rotary keys): 8 sampled pairs after prefill
-    and after 3 more steps."""
+    and 2 after each of 3 fused steps (decode_step, the benchmark's call)."""
     import sliding_window_attention_ring_amd as swa
     wl = workloads.BF16_32K
     dev = torch.device("cuda")
@@ -132,11 +171,14 @@ def test_bf16_ctx32768_sampled():
     rng = np.random.default_rng(5)
     n = wl.prefill
     for extra in range(4):
-        if extra:
-            swa.kv_append(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous())
+        if extra:  # the benchmark's call: the fused step
+            q = gen.query(wl, n, device=dev)
+            out = swa.decode_step(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous(),
+                                  q).cpu().numpy()
             n += 1
-        q = gen.query(wl, n - 1, device=dev)
-        out = swa.decode_attn(cache, q).cpu().numpy()
+        else:
+            q = gen.query(wl, n - 1, device=dev)
+            out = swa.decode_attn(cache, q).cpu().numpy()
         qh = f64(q)
         for _ in range(2 if extra else 8):
             b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
@@ -150,8 +192,9 @@ def test_int8_witness_ctx32768():
     """B=16, H=32, W=32768 INT8 with rotary keys: after the 32768-token
     prefill, 3 sampled pairs get the full store check (codes, scales bits,
     witness >= exact norms) and the per-token bound check; then 20 steps at
-    positions 32768..32787 (crossing the block boundary at 32784) check one
-    pair each."""
+    positions 32768..32787 (crossing the block boundary at 32784), alternately
+    the fused decode_step_int8 (the benchmark's call) and kv_append + the
+    decode, check one pair each."""
     import sliding_window_attention_ring_amd as swa
     wl = workloads.INT8_32K
     dev = torch.device("cuda")
@@ -173,15 +216,21 @@ def test_int8_witness_ctx32768():
         check_int8_store(cache, b, h, k64, v64, n)
         check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, qh[b, h], k64, v64, n, wl.W, "32k")
     for i in range(wl.steps):
-        swa.kv_append(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous())
+        kn, vn = k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous()
+        q = gen.query(wl, n, device=dev)
+        if i % 2 == 1:  # the benchmark's call: the fused step (no c_all)
+            out, cmax, _, _ = swa.decode_step_int8(cache, kn, vn, q)
+            c_all = None
+        else:
+            swa.kv_append(cache, kn, vn)
+            out, cmax, c_all = swa.decode_attn_int8_witness(cache, q, want_c_all=True)
         n += 1
-        q = gen.query(wl, n - 1, device=dev)
-        out, cmax, c_all = swa.decode_attn_int8_witness(cache, q, want_c_all=True)
         assert swa.validate(cache) == 0
         b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
         k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
-        check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]), c_all[b, h].cpu().numpy(), b, h,
-                          f64(q[b, h]), k64, v64, n, wl.W, f"32k step n={n}")
+        check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]),
+                          None if c_all is None else c_all[b, h].cpu().numpy(), b, h, f64(q[b, h]), k64, v64, n,
+                          wl.W, f"32k step n={n}")
     say("int8 32k steps ok, last n", n)
 
 
@@ -190,9 +239,10 @@ def test_int8_dither_ctx32768():
     layer 0), decoded with delta = 1e-6 as the benchmark does: after the
     prefill, 2 sampled pairs get the full store check (codes and scales bit
     for bit against the oracle's own Philox stream) and the decode check;
-    then 20 steps at positions 32768..32787, with the decode of one pair
-    checked at six of them, including both sides of the block commit at
-    32784."""
+    then 20 steps at positions 32768..32787, alternately the fused
+    decode_step_int8 (the benchmark's call) and kv_append + the decode, with
+    the decode of one pair checked at six of them, including both sides of
+    the block commit at 32784."""
     import sliding_window_attention_ring_amd as swa
     wl = workloads.INT8_DITHER_32K
     delta = 1e-6
@@ -217,10 +267,14 @@ def test_int8_dither_ctx32768():
         check_dither_decode(out[b, h], cert[b, h], b, h, qh[b, h], k64, v64, n, wl.W, reqs[b], cache.layer, delta,
                             tv[b, h], gate[b, h], what="32k")
     for i in range(wl.steps):
-        swa.kv_append(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous())
+        kn, vn = k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous()
+        q = gen.query(wl, n, device=dev)
+        if i % 2 == 1:  # the benchmark's call: the fused step
+            out, cert, tv, gate = swa.decode_step_int8(cache, kn, vn, q, delta=delta, want_tv=True)
+        else:
+            swa.kv_append(cache, kn, vn)
+            out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q, delta=delta)
         n += 1
-        q = gen.query(wl, n - 1, device=dev)
-        out, cert, tv, gate = swa.decode_attn_int8_dither(cache, q, delta=delta)
         assert swa.validate(cache) == 0
         if i not in (0, 7, 14, 15, 16, 19):
             continue
