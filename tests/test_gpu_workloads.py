@@ -348,3 +348,87 @@ def test_int8_head_shard_ctx32768():
         check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]), None, b, h, f64(q[b, h]), k64, v64, n,
                           wl.W, f"head shard step n={n}")
     say("int8 head shard steps ok, last n", n)
+
+
+def test_int8_witness_ctx32768_paged():
+    """The INT8 32k workload in 16-token pages (shuffled table over the pool):
+    after the prefill, 2 sampled pairs get the store check (read back through
+    the table) and the per-token bound check; then 18 steps up to and past
+    the block commit at 32784, alternately the fused decode_step_int8 (the
+    benchmark's call) and kv_append + the decode, check one pair each."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.INT8_32K_PAGED
+    dev = torch.device("cuda")
+    total = wl.prefill + 18
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("int8", wl.B, wl.H, wl.D, wl.W, layout="paged")
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(18)
+    n = wl.prefill
+    q = gen.query(wl, n - 1, device=dev)
+    out, cmax, c_all = swa.decode_attn_int8_witness(cache, q, want_c_all=True)
+    assert swa.validate(cache) == 0
+    out, cmax, c_all, qh = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy(), f64(q)
+    for _ in range(2):
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        say("int8 32k paged store check", b, h)
+        check_int8_store(cache, b, h, k64, v64, n)
+        check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, qh[b, h], k64, v64, n, wl.W, "32k paged")
+    for i in range(18):
+        kn, vn = k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous()
+        q = gen.query(wl, n, device=dev)
+        if i % 2 == 1:
+            out, cmax, _, _ = swa.decode_step_int8(cache, kn, vn, q)
+        else:
+            swa.kv_append(cache, kn, vn)
+            out, cmax, _ = swa.decode_attn_int8_witness(cache, q)
+        n += 1
+        assert swa.validate(cache) == 0
+        b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+        k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+        check_int8_decode(out[b, h].cpu().numpy(), float(cmax[b, h]), None, b, h, f64(q[b, h]), k64, v64, n, wl.W,
+                          f"32k paged step n={n}")
+    b = int(rng.integers(wl.B))
+    check_int8_store(cache, b, 0, f64(k_all[b, 0, :n]), f64(v_all[b, 0, :n]), n)
+    say("int8 32k paged steps ok, last n", n)
+
+
+def test_bf16_ctx32768_paged_sampled():
+    """The bf16 32k workload in 16-token pages: 6 sampled pairs after the
+    prefill, then 3 fused steps (decode_step, the benchmark's call) with 2
+    sampled pairs each; ring rows of one sequence read back through the
+    table bit for bit."""
+    import sliding_window_attention_ring_amd as swa
+    wl = workloads.BF16_32K_PAGED
+    dev = torch.device("cuda")
+    total = wl.prefill + 3
+    k_all = gen.tokens(wl, "k", total, device=dev)
+    v_all = gen.tokens(wl, "v", total, device=dev)
+    cache = swa.KVCache("bf16", wl.B, wl.H, wl.D, wl.W, layout="paged")
+    prefill(swa, cache, k_all, v_all, wl.prefill, wl.prefill_chunk)
+    rng = np.random.default_rng(19)
+    n = wl.prefill
+    for extra in range(4):
+        if extra:
+            q = gen.query(wl, n, device=dev)
+            out = swa.decode_step(cache, k_all[:, :, n:n + 1].contiguous(), v_all[:, :, n:n + 1].contiguous(),
+                                  q).cpu().numpy()
+            n += 1
+        else:
+            q = gen.query(wl, n - 1, device=dev)
+            out = swa.decode_attn(cache, q).cpu().numpy()
+        assert swa.validate(cache) == 0
+        qh = f64(q)
+        for _ in range(2 if extra else 6):
+            b, h = int(rng.integers(wl.B)), int(rng.integers(wl.H))
+            k64, v64 = f64(k_all[b, h, :n]), f64(v_all[b, h, :n])
+            ref = attention.masked_attention(qh[b, h], np.arange(n), k64, v64, n - 1, wl.W)
+            assert_close(out[b, h], ref, f"bf16-32k paged n={n} b={b} h={h}")
+    from tests.gpu_util import RingView
+    view = RingView(cache)
+    b = int(rng.integers(wl.B))
+    exp = decoder.expected_ring(np.arange(n), wl.W)
+    np.testing.assert_array_equal(host_bits(view.pos[b]), exp)
+    np.testing.assert_array_equal(host_bits(view.k[b]), host_bits(k_all[b][:, torch.as_tensor(exp, device=dev)]))
