@@ -66,6 +66,8 @@ class KVCache:
             raise ValueError(f"layout must be one of {sorted(LAYOUT)}")
         self.kind, self.B, self.H, self.D, self.W, self.layout = kind, B, H, D, W, layout
         dev = torch.device(device)
+        if dev.type != "cuda":  # the kernels take device pointers: never hand them host memory
+            raise ValueError(f"a KVCache lives in GPU memory: device must be a GPU device, got {dev}")
         paged = layout == "paged"
         if paged:
             if W % 16:

@@ -1,0 +1,64 @@
+"""The Python binding's own checks (CPU only): it refuses host memory and
+mis-shaped, mis-typed or non-contiguous tensors before anything reaches the
+C ABI, and it raises when the library is missing (there is no CPU fallback)."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+from tests.conftest import ROOT
+
+
+def test_cache_refuses_host_memory():
+    import sliding_window_attention_ring_amd as swa
+    with pytest.raises(ValueError, match="GPU"):
+        swa.KVCache("bf16", 1, 1, 64, 16, device="cpu")
+    with pytest.raises(ValueError, match="kind"):
+        swa.KVCache("int4", 1, 1, 64, 16)
+    with pytest.raises(ValueError, match="layout"):
+        swa.KVCache("bf16", 1, 1, 64, 16, layout="tree")
+
+
+def test_tensor_checks():
+    from sliding_window_attention_ring_amd.cache import _need
+    t = torch.zeros((2, 3), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _need(t, (2, 3), torch.float32, "x")
+    with pytest.raises(TypeError):
+        _need([1, 2], (2,), torch.float32, "x")
+
+
+class _FakeCuda:
+    """Stands in for a GPU tensor to reach the shape, dtype and layout checks."""
+    is_cuda = True
+
+    def __init__(self, shape, dtype, contiguous=True):
+        self.shape, self.dtype, self._c = shape, dtype, contiguous
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_shape_dtype_and_layout_checks(monkeypatch):
+    from sliding_window_attention_ring_amd import cache
+    monkeypatch.setattr(cache.torch, "Tensor", _FakeCuda)
+    cache._need(_FakeCuda((2, 3), torch.bfloat16), (2, 3), torch.bfloat16, "x")  # passes
+    with pytest.raises(ValueError, match="expected"):
+        cache._need(_FakeCuda((2, 4), torch.bfloat16), (2, 3), torch.bfloat16, "x")
+    with pytest.raises(ValueError, match="expected"):
+        cache._need(_FakeCuda((2, 3), torch.float32), (2, 3), torch.bfloat16, "x")
+    with pytest.raises(ValueError, match="contiguous"):
+        cache._need(_FakeCuda((2, 3), torch.bfloat16, contiguous=False), (2, 3), torch.bfloat16, "x")
+
+
+def test_missing_library_raises():
+    code = ("import sliding_window_attention_ring_amd._capi as c\n"
+            "try:\n    c.lib()\nexcept RuntimeError as e:\n    print('raised:', e)\n")
+    env = dict(os.environ, SWA_LIB=os.path.join(ROOT, "no_such_dir", "libswa.so"))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, env=env,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert "raised:" in res.stdout and "missing" in res.stdout
