@@ -181,7 +181,22 @@ def workspace_bytes(cache) -> int:
     return int(lib().swa_workspace_bytes(ctypes.byref(cache.desc)))
 
 
+def _check_ws(ws: torch.Tensor) -> None:
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("the workspace must be a contiguous GPU tensor")
+
+
+def _workspace(cache, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    """The cache's own workspace, or a caller's after checking it is GPU memory
+    (its size is checked by the C ABI)."""
+    if ws is None:
+        return cache.workspace()
+    _check_ws(ws)
+    return ws
+
+
 def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check_ws(ws)
     check(lib().swa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
           "swa_workspace_init")
 
@@ -193,7 +208,7 @@ def decode_attn(cache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
     if out is None:
         out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=q.device)
     _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
-    ws = cache.workspace() if ws is None else ws
+    ws = _workspace(cache, ws)
     check(lib().decode_attn(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)), "decode_attn")
     return out
@@ -216,7 +231,7 @@ def decode_attn_int8_witness(cache, q: torch.Tensor, out: Optional[torch.Tensor]
     _need(cmax, (cache.B, cache.H), torch.float32, "cmax")
     if c_all is not None:
         _need(c_all, (cache.B, cache.H, cache.W), torch.float32, "c_all")
-    ws = cache.workspace() if ws is None else ws
+    ws = _workspace(cache, ws)
     check(lib().decode_attn_int8_witness(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(cmax),
                                          _ptr(c_all), _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream(stream)), "decode_attn_int8_witness")
@@ -239,7 +254,7 @@ def decode_attn_int8_witness_tv(cache, q: torch.Tensor, tau: float = 0.2, out: O
     _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
     for t, name, dt in ((cmax, "cmax", torch.float32), (tv, "tv", torch.float32), (gate, "gate", torch.int32)):
         _need(t, BH, dt, name)
-    ws = cache.workspace() if ws is None else ws
+    ws = _workspace(cache, ws)
     check(lib().decode_attn_int8_witness_tv(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(cmax), _ptr(tv),
                                             _ptr(gate), float(tau), _ptr(c_all), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream)),
@@ -267,7 +282,7 @@ def decode_attn_int8_dither(cache, q: torch.Tensor, delta: float, tau: float = 0
         _need(tv, BH, torch.float32, "tv")
     if gate is not None:
         _need(gate, BH, torch.int32, "gate")
-    ws = cache.workspace() if ws is None else ws
+    ws = _workspace(cache, ws)
     check(lib().decode_attn_int8_dither(ctypes.byref(cache.desc), _ptr(q), _ptr(out), _ptr(cert), _ptr(tv),
                                         _ptr(gate), float(tau), float(delta), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)),
@@ -286,7 +301,7 @@ def decode_step(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor
     if out is None:
         out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=q.device)
     _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
-    ws = cache.workspace() if ws is None else ws
+    ws = _workspace(cache, ws)
     check(lib().decode_step(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)), "decode_step")
     return out
@@ -316,7 +331,7 @@ def decode_step_int8(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.T
         _need(tv, BH, torch.float32, "tv")
     if gate is not None:
         _need(gate, BH, torch.int32, "gate")
-    ws = cache.workspace() if ws is None else ws
+    ws = _workspace(cache, ws)
     check(lib().decode_step_int8(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(cmax),
                                  _ptr(tv), _ptr(gate), float(tau), float(delta), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)), "decode_step_int8")

@@ -62,3 +62,11 @@ def test_missing_library_raises():
                          timeout=120)
     assert res.returncode == 0, res.stderr
     assert "raised:" in res.stdout and "missing" in res.stdout
+
+
+def test_workspace_must_be_gpu_memory():
+    from sliding_window_attention_ring_amd import cache
+    with pytest.raises(ValueError, match="GPU tensor"):
+        cache.workspace_init(torch.zeros(64, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        cache._workspace(None, torch.zeros(64, dtype=torch.uint8))
