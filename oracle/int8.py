@@ -10,8 +10,7 @@ Follows [WitCert]:
 * "SGLang 生产级落地" section: one scale per block, so the scale is a scalar
   independent of the token inside the block.
 
-Readings taken where the pages are silent (each also listed in the design
-notes):
+Readings taken where the pages are silent:
 * Blocks are 16 consecutive absolute positions aligned at ``pos // 16``;
   one float32 absmax scale per (sequence, head, block) per tensor, symmetric
   codes in [-127, 127].  The scale and code steps are fixed in float32:
