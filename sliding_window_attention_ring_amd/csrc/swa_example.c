@@ -6,11 +6,12 @@
  *   2. with every visible key identical the weights are uniform, so the
  *      output is the mean of the visible value rows.
  * It also checks the position invariant with swa_validate and an error path.
- * A second part uses an INT8 cache with the witness bound, stepping it with
- * decode_step_int8 (append + decode in one call) on one cache and with
- * kv_append + decode_attn_int8_witness on a twin: the two must agree bit for
- * bit, and with identical keys and values that are exact multiples of their
- * block scale the output is the mean of the value rows.
+ * A second part uses an INT8 cache with the witness bound, then one with
+ * subtractive dither, stepping each with decode_step_int8 (append + decode
+ * in one call) on one cache and with kv_append + the separate decode on a
+ * twin: the two must agree bit for bit, and with identical keys and values
+ * that are exact multiples of their block scale the output is the mean of
+ * the value rows (within the dither's half step for the dithered kind).
  * Prints "swa_example ok" and returns 0 on success.
  */
 #include <hip/hip_runtime_api.h>
@@ -141,10 +142,8 @@ int main(void) {
   if (decode_attn(&c, dq, dout, ws, ws_bytes > 0 ? ws_bytes - 1 : 0, NULL) != SWA_EWORKSPACE && ws_bytes > 0)
     ++failures;
 
-  /* ---- INT8 with the witness bound: fused step vs append + decode ---- */
+  /* ---- INT8 (witness; then dithered): fused step vs append + decode ---- */
   const int T8 = 37, D8 = 128, W8 = 64;
-  swa_cache c8[2];
-  void *ws8[2];
   const size_t n8 = (size_t)B * H * T8 * D8;
   uint16_t *k8 = malloc(n8 * 2), *v8 = malloc(n8 * 2);
   for (int bh = 0; bh < B * H; ++bh)
@@ -156,83 +155,102 @@ int main(void) {
         const int m = d == 0 ? 127 : (bh * 13 + j * 7 + d * 3) % 255 - 127;
         v8[i] = to_bf16((float)m / 16.0f);
       }
-  void *dk8, *dv8, *dq8;
-  float *dout8[2], *dcm8[2];
-  CHECK_HIP(hipMalloc(&dk8, n8 * 2));
-  CHECK_HIP(hipMalloc(&dv8, n8 * 2));
+  void *dq8, *dkt, *dvt;
   CHECK_HIP(hipMalloc(&dq8, (size_t)B * H * D8 * 2));
-  CHECK_HIP(hipMemcpy(dk8, k8, n8 * 2, hipMemcpyHostToDevice));
-  CHECK_HIP(hipMemcpy(dv8, v8, n8 * 2, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dq8, hq, (size_t)B * H * D8 * 2, hipMemcpyHostToDevice));
-  for (int t = 0; t < 2; ++t) {
-    swa_cache *x = &c8[t];
-    memset(x, 0, sizeof *x);
-    x->kind = SWA_KV_INT8; x->B = B; x->H = H; x->D = D8; x->W = W8; x->layout = SWA_LAYOUT_RING;
-    CHECK_HIP(hipMalloc(&x->k, (size_t)B * H * W8 * D8));
-    CHECK_HIP(hipMalloc(&x->v, (size_t)B * H * W8 * D8));
-    CHECK_HIP(hipMalloc((void **)&x->k_scale, (size_t)B * H * (W8 / 16) * 4));
-    CHECK_HIP(hipMalloc((void **)&x->v_scale, (size_t)B * H * (W8 / 16) * 4));
-    CHECK_HIP(hipMalloc((void **)&x->witness, (size_t)B * H * W8 * (D8 / 8) * 2));
-    CHECK_HIP(hipMalloc(&x->k_stage, (size_t)B * H * 16 * D8 * 2));
-    CHECK_HIP(hipMalloc(&x->v_stage, (size_t)B * H * 16 * D8 * 2));
-    CHECK_HIP(hipMalloc((void **)&x->pos, (size_t)B * W8 * 4));
-    CHECK_HIP(hipMalloc((void **)&x->next_position, (size_t)B * 4));
-    CHECK_SWA(swa_cache_reset(x, NULL));
-    const size_t wsb = swa_workspace_bytes(x);
-    CHECK_HIP(hipMalloc(&ws8[t], wsb));
-    CHECK_SWA(swa_workspace_init(ws8[t], wsb, NULL));  /* the step counters start at zero */
-    CHECK_HIP(hipMalloc((void **)&dout8[t], (size_t)B * H * D8 * 4));
-    CHECK_HIP(hipMalloc((void **)&dcm8[t], (size_t)B * H * 4));
-  }
-  /* token j of every sequence, one step at a time; the rows are [B][H][1][D] */
-  void *dkt, *dvt;
-  uint16_t *kt = malloc((size_t)B * H * D8 * 2), *vt = malloc((size_t)B * H * D8 * 2);
   CHECK_HIP(hipMalloc(&dkt, (size_t)B * H * D8 * 2));
   CHECK_HIP(hipMalloc(&dvt, (size_t)B * H * D8 * 2));
+  uint16_t *kt = malloc((size_t)B * H * D8 * 2), *vt = malloc((size_t)B * H * D8 * 2);
   float *o0 = malloc((size_t)B * H * D8 * 4), *o1 = malloc((size_t)B * H * D8 * 4);
   float cm0[64], cm1[64];
-  int mismatches = 0;
-  for (int j = 0; j < T8; ++j) {
-    for (int bh = 0; bh < B * H; ++bh) {
-      memcpy(kt + (size_t)bh * D8, k8 + ((size_t)bh * T8 + j) * D8, D8 * 2);
-      memcpy(vt + (size_t)bh * D8, v8 + ((size_t)bh * T8 + j) * D8, D8 * 2);
+  uint64_t rid[2] = {0x0123456789abcdefull, 42u};  /* the dithered kind's request ids */
+  uint64_t *drid;
+  CHECK_HIP(hipMalloc((void **)&drid, sizeof rid));
+  CHECK_HIP(hipMemcpy(drid, rid, sizeof rid, hipMemcpyHostToDevice));
+  int mism[2] = {0, 0};
+  double worst8[2] = {0.0, 0.0};
+  for (int pass = 0; pass < 2; ++pass) {
+    const int kind = pass == 0 ? SWA_KV_INT8 : SWA_KV_INT8_DITHER;
+    swa_cache c8[2];
+    void *ws8[2];
+    float *dout8[2], *dcm8[2];
+    for (int t = 0; t < 2; ++t) {
+      swa_cache *x = &c8[t];
+      memset(x, 0, sizeof *x);
+      x->kind = kind; x->B = B; x->H = H; x->D = D8; x->W = W8; x->layout = SWA_LAYOUT_RING;
+      CHECK_HIP(hipMalloc(&x->k, (size_t)B * H * W8 * D8));
+      CHECK_HIP(hipMalloc(&x->v, (size_t)B * H * W8 * D8));
+      CHECK_HIP(hipMalloc((void **)&x->k_scale, (size_t)B * H * (W8 / 16) * 4));
+      CHECK_HIP(hipMalloc((void **)&x->v_scale, (size_t)B * H * (W8 / 16) * 4));
+      if (kind == SWA_KV_INT8) {
+        CHECK_HIP(hipMalloc((void **)&x->witness, (size_t)B * H * W8 * (D8 / 8) * 2));
+      } else {
+        x->request_id = drid;
+        x->layer = 3;
+      }
+      CHECK_HIP(hipMalloc(&x->k_stage, (size_t)B * H * 16 * D8 * 2));
+      CHECK_HIP(hipMalloc(&x->v_stage, (size_t)B * H * 16 * D8 * 2));
+      CHECK_HIP(hipMalloc((void **)&x->pos, (size_t)B * W8 * 4));
+      CHECK_HIP(hipMalloc((void **)&x->next_position, (size_t)B * 4));
+      CHECK_SWA(swa_cache_reset(x, NULL));
+      const size_t wsb = swa_workspace_bytes(x);
+      CHECK_HIP(hipMalloc(&ws8[t], wsb));
+      CHECK_SWA(swa_workspace_init(ws8[t], wsb, NULL));  /* the counters start at zero */
+      CHECK_HIP(hipMalloc((void **)&dout8[t], (size_t)B * H * D8 * 4));
+      CHECK_HIP(hipMalloc((void **)&dcm8[t], (size_t)B * H * 4));
     }
-    CHECK_HIP(hipMemcpy(dkt, kt, (size_t)B * H * D8 * 2, hipMemcpyHostToDevice));
-    CHECK_HIP(hipMemcpy(dvt, vt, (size_t)B * H * D8 * 2, hipMemcpyHostToDevice));
-    CHECK_SWA(decode_step_int8(&c8[0], dkt, dvt, dq8, dout8[0], dcm8[0], NULL, NULL, 0.2f, 1.0f, ws8[0],
-                               swa_workspace_bytes(&c8[0]), NULL));
-    CHECK_SWA(kv_append(&c8[1], dkt, dvt, 1, NULL));
-    CHECK_SWA(decode_attn_int8_witness(&c8[1], dq8, dout8[1], dcm8[1], NULL, ws8[1], swa_workspace_bytes(&c8[1]),
-                                       NULL));
-    CHECK_HIP(hipMemcpy(o0, dout8[0], (size_t)B * H * D8 * 4, hipMemcpyDeviceToHost));
-    CHECK_HIP(hipMemcpy(o1, dout8[1], (size_t)B * H * D8 * 4, hipMemcpyDeviceToHost));
-    CHECK_HIP(hipMemcpy(cm0, dcm8[0], (size_t)B * H * 4, hipMemcpyDeviceToHost));
-    CHECK_HIP(hipMemcpy(cm1, dcm8[1], (size_t)B * H * 4, hipMemcpyDeviceToHost));
-    if (memcmp(o0, o1, (size_t)B * H * D8 * 4) != 0 || memcmp(cm0, cm1, (size_t)B * H * 4) != 0) ++mismatches;
+    /* token j of every sequence, one step at a time; the rows are [B][H][1][D] */
+    for (int j = 0; j < T8; ++j) {
+      for (int bh = 0; bh < B * H; ++bh) {
+        memcpy(kt + (size_t)bh * D8, k8 + ((size_t)bh * T8 + j) * D8, D8 * 2);
+        memcpy(vt + (size_t)bh * D8, v8 + ((size_t)bh * T8 + j) * D8, D8 * 2);
+      }
+      CHECK_HIP(hipMemcpy(dkt, kt, (size_t)B * H * D8 * 2, hipMemcpyHostToDevice));
+      CHECK_HIP(hipMemcpy(dvt, vt, (size_t)B * H * D8 * 2, hipMemcpyHostToDevice));
+      const float delta = kind == SWA_KV_INT8 ? 1.0f : 1e-3f;
+      CHECK_SWA(decode_step_int8(&c8[0], dkt, dvt, dq8, dout8[0], dcm8[0], NULL, NULL, 0.2f, delta, ws8[0],
+                                 swa_workspace_bytes(&c8[0]), NULL));
+      CHECK_SWA(kv_append(&c8[1], dkt, dvt, 1, NULL));
+      if (kind == SWA_KV_INT8)
+        CHECK_SWA(decode_attn_int8_witness(&c8[1], dq8, dout8[1], dcm8[1], NULL, ws8[1],
+                                           swa_workspace_bytes(&c8[1]), NULL));
+      else
+        CHECK_SWA(decode_attn_int8_dither(&c8[1], dq8, dout8[1], dcm8[1], NULL, NULL, 0.2f, delta, ws8[1],
+                                          swa_workspace_bytes(&c8[1]), NULL));
+      CHECK_HIP(hipMemcpy(o0, dout8[0], (size_t)B * H * D8 * 4, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(o1, dout8[1], (size_t)B * H * D8 * 4, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(cm0, dcm8[0], (size_t)B * H * 4, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(cm1, dcm8[1], (size_t)B * H * 4, hipMemcpyDeviceToHost));
+      if (memcmp(o0, o1, (size_t)B * H * D8 * 4) != 0 || memcmp(cm0, cm1, (size_t)B * H * 4) != 0) ++mism[pass];
+    }
+    for (int bh = 0; bh < B * H; ++bh)
+      for (int d = 0; d < D8; ++d) {
+        double mean = 0.0;
+        for (int j = 0; j < T8; ++j) mean += from_bf16(v8[((size_t)bh * T8 + j) * D8 + d]);
+        mean /= T8;
+        const double err = fabs(o0[(size_t)bh * D8 + d] - mean);
+        if (err > worst8[pass]) worst8[pass] = err;
+      }
+    /* Witness kind: the values are exact multiples of their scale, so the output is the exact mean.  Dithered
+     * kind: each value reads back s*(code - u), within s/2 = 1/32 of the input, and the keys read back within
+     * 1/254 of 1, so the weights stay uniform to within a fraction of a percent. */
+    if (mism[pass] || worst8[pass] > (kind == SWA_KV_INT8 ? 2e-3 : 0.05)) ++failures;
+    int32_t np8[2];
+    CHECK_HIP(hipMemcpy(np8, c8[0].next_position, (size_t)B * 4, hipMemcpyDeviceToHost));
+    if (np8[0] != T8 || np8[1] != T8) ++failures;
+    for (int t = 0; t < 2; ++t) {
+      hipFree(c8[t].k); hipFree(c8[t].v); hipFree(c8[t].k_scale); hipFree(c8[t].v_scale);
+      if (c8[t].witness) hipFree(c8[t].witness);
+      hipFree(c8[t].k_stage); hipFree(c8[t].v_stage); hipFree(c8[t].pos); hipFree(c8[t].next_position);
+      hipFree(ws8[t]); hipFree(dout8[t]); hipFree(dcm8[t]);
+    }
   }
-  double worst8 = 0.0;
-  for (int bh = 0; bh < B * H; ++bh)
-    for (int d = 0; d < D8; ++d) {
-      double mean = 0.0;
-      for (int j = 0; j < T8; ++j) mean += from_bf16(v8[((size_t)bh * T8 + j) * D8 + d]);
-      mean /= T8;
-      const double err = fabs(o0[(size_t)bh * D8 + d] - mean);
-      if (err > worst8) worst8 = err;
-    }
-  if (mismatches || worst8 > 2e-3) ++failures;
-  int32_t np8[2];
-  CHECK_HIP(hipMemcpy(np8, c8[0].next_position, (size_t)B * 4, hipMemcpyDeviceToHost));
-  if (np8[0] != T8 || np8[1] != T8) ++failures;
 
   printf("swa_example %s: one-token rows exact, identical-key mean max err %.3g, violations %d; "
-         "int8 fused step == append+decode on %d steps (%d mismatches), exact-value mean max err %.3g\n",
-         failures ? "FAILED" : "ok", worst, viol, T8, mismatches, worst8);
-  for (int t = 0; t < 2; ++t) {
-    hipFree(c8[t].k); hipFree(c8[t].v); hipFree(c8[t].k_scale); hipFree(c8[t].v_scale); hipFree(c8[t].witness);
-    hipFree(c8[t].k_stage); hipFree(c8[t].v_stage); hipFree(c8[t].pos); hipFree(c8[t].next_position);
-    hipFree(ws8[t]); hipFree(dout8[t]); hipFree(dcm8[t]);
-  }
-  hipFree(dk8); hipFree(dv8); hipFree(dq8); hipFree(dkt); hipFree(dvt);
+         "int8 fused step == append+decode on %d steps (%d mismatches), exact-value mean max err %.3g; "
+         "dithered int8 fused step == append+decode (%d mismatches), mean max err %.3g\n",
+         failures ? "FAILED" : "ok", worst, viol, T8, mism[0], worst8[0], mism[1], worst8[1]);
+  hipFree(dq8); hipFree(dkt); hipFree(dvt); hipFree(drid);
   free(k8); free(v8); free(kt); free(vt); free(o0); free(o1);
   hipFree(c.k); hipFree(c.v); hipFree(c.pos); hipFree(c.next_position);
   hipFree(dk); hipFree(dv); hipFree(dq); hipFree(dout); hipFree(dviol); hipFree(ws); hipFree(dk1); hipFree(dv1);
