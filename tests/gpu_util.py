@@ -127,20 +127,32 @@ def check_int8_store(cache, b: int, h: int, k64: np.ndarray, v64: np.ndarray, n:
         np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])
 
 
+def fp16_witness_slack(q64) -> float:
+    """Absolute excess a bound may carry when band norms fall below fp16's
+    normal range (6.1e-5): each stored norm, rounded up, may sit one subnormal
+    step (2^-24) above the exact one, so c_t may exceed the exact bound by
+    sum_b ||q_b|| 2^-24 / sqrt(D)."""
+    q64 = np.asarray(q64, dtype=np.float64)
+    d = q64.shape[-1]
+    return float(np.sum(np.linalg.norm(q64.reshape(-1, 8), axis=1)) * 2.0 ** -24 / np.sqrt(d))
+
+
 def check_int8_decode(out, cmax, c_all, b, h, q64, k64, v64, n, W, what=""):
     """INT8 decode of (b, h) vs the oracle: output within TOL; cmax and every
-    per-slot c_t sound (>= the true logit error of that token) and tight."""
+    per-slot c_t sound (>= the true logit error of that token) and tight
+    (within (1 + 2^-9), plus the fp16 subnormal slack for tiny residuals)."""
     res = oint8.int8_decode(q64, k64, v64, n, W)
     err = assert_close(out, res["out"], f"int8 out {what} b={b} h={h}")
     e, c = res["e"], res["c"]
+    slack = fp16_witness_slack(q64) + 1e-30
     emax = float(np.max(e)) if e.size else 0.0
     assert cmax >= emax, f"cmax {cmax} below the true max logit error {emax}"
-    assert cmax <= res["cmax"] * (1 + 2.0 ** -9) + 1e-30, (cmax, res["cmax"])
+    assert cmax <= (res["cmax"] + slack) * (1 + 2.0 ** -9), (cmax, res["cmax"])
     if c_all is not None:
         slots = res["positions"] % W
         cg = np.asarray(c_all, dtype=np.float64)[slots]
         assert np.all(cg >= e), "per-token bound below the true logit error"
-        assert np.all(cg <= c * (1 + 2.0 ** -9) + 1e-30), "per-token bound not tight"
+        assert np.all(cg <= (c + slack) * (1 + 2.0 ** -9)), "per-token bound not tight"
         quant = res["positions"] < 16 * (n // 16)
         assert not np.any(cg[~quant]), "exact (staged) tokens must have c = 0"
         vis = np.zeros(W, dtype=bool)

@@ -27,7 +27,7 @@ import pytest
 import torch
 
 from oracle import attention, int8 as oint8
-from tests.gpu_util import assert_close, f64, host_bits, require_gpu, say
+from tests.gpu_util import assert_close, f64, fp16_witness_slack, host_bits, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -160,11 +160,8 @@ def test_int8_region_at_4gib(kind, layout):
     assert cm >= float(np.max(e_true)), (cm, e_true)
     if kind == "int8":
         c_or = [oint8.witness_bound(np.ones(D), oint8.band_norms(ks[i] - khat[i])) for i in range(2)]
-        # The spike residuals are ~1e-7, in fp16's subnormal range, where the
-        # stored norm (rounded up) may sit one subnormal step (2^-24) above the
-        # exact one: allow sum_b ||q_b|| 2^-24 / sqrt(D) on top of the relative pad.
-        slack = 16 * np.sqrt(8.0) * 2.0 ** -24 / np.sqrt(D)
-        assert cm <= max(c_or) * (1 + 2.0 ** -9) + slack, (cm, c_or)
+        # The spike residuals are ~1e-7, in fp16's subnormal range (see fp16_witness_slack).
+        assert cm <= (max(c_or) + fp16_witness_slack(np.ones(D))) * (1 + 2.0 ** -9), (cm, c_or)
         ca = c_all.cpu().numpy()[0, 0]  # slot-indexed in both layouts
         for i, p in enumerate(spikes):
             assert ca[p % W] >= e_true[i]
