@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 import torch
 
-from tests.gpu_util import assert_close, check_int8_decode, f64, oracle_out, require_gpu, say
+from tests.gpu_util import (assert_close, check_dither_decode, check_int8_decode, f64, oracle_out, request_ids,
+                            require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,8 +78,8 @@ def test_tiny_magnitudes(kind):
     assert swa.validate(cache) == 0
 
 
-@pytest.mark.parametrize("layout", ["ring", "paged"])
-def test_int8_outlier_blocks(layout):
+@pytest.mark.parametrize("kind,layout", [("int8", "ring"), ("int8", "paged"), ("int8_dither", "ring")])
+def test_int8_outlier_blocks(kind, layout):
     import sliding_window_attention_ring_amd as swa
     B, H, D, W = 2, 4, 128, 128
     n = 2 * W + 9
@@ -96,13 +97,21 @@ def test_int8_outlier_blocks(layout):
                 v[b, h, r, (d + 1) % D] *= 100.0
     k, v = k.to(torch.bfloat16), v.to(torch.bfloat16)
     q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
-    cache = swa.KVCache("int8", B, H, D, W, layout=layout)
+    cache = swa.KVCache(kind, B, H, D, W, layout=layout)
     _fill(swa, cache, k, v)
-    out, cmax, c_all = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
-    out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
+    if kind == "int8":
+        out, cmax, c_all = swa.decode_attn_int8_witness(cache, q.cuda(), want_c_all=True)
+        out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
+    else:
+        out, cmax, tv, gate = (x.cpu().numpy() for x in swa.decode_attn_int8_dither(cache, q.cuda(), delta=1e-3))
     assert swa.validate(cache) == 0
+    reqs = request_ids(cache) if kind == "int8_dither" else None
     for b in range(B):
         for h in range(H):
-            check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, f64(q[b, h]), f64(k[b, h]), f64(v[b, h]),
-                              n, W, f"outlier {layout}")
-    say(f"outlier blocks ({layout}): cmax up to {float(np.max(cmax)):.2f}")
+            if kind == "int8":
+                check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, f64(q[b, h]), f64(k[b, h]),
+                                  f64(v[b, h]), n, W, f"outlier {layout}")
+            else:
+                check_dither_decode(out[b, h], cmax[b, h], b, h, f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), n, W,
+                                    reqs[b], cache.layer, 1e-3, tv[b, h], gate[b, h], what=f"outlier {layout}")
+    say(f"outlier blocks ({kind}, {layout}): bound up to {float(np.max(cmax)):.2f}")
