@@ -1,19 +1,24 @@
 """Decode-step benchmark on one MI355X.
 
-A step is one pass of the decode hot path over the whole batch: append one
-token per sequence (``kv_append``), then one query per sequence attends to
-the cache (``decode_attn_int8_witness`` for INT8 workloads,
-``decode_attn_int8_dither`` with its TV bound and gate for the dithered INT8
-workload, ``decode_attn`` otherwise).  The default workload is the INT8 cache with the witness bound at
-32768 context (B=16, H=32, D=128), prefilled with 32768 rotary keys.
+A step is one pass of the decode hot path over the whole batch: one token
+per sequence is appended and one query per sequence attends to the cache.
+By default a step is one call of the fused entry point (``decode_step_int8``
+for the INT8 workloads, with the witness bound, or with the certificate, TV
+bound and gate for the dithered one; ``decode_step`` otherwise), which
+appends and attends in one launch plus a merge launch when a (b, h) has
+several splits.  ``--no-fuse`` times ``kv_append`` followed by the separate
+decode call instead.  The default workload is the INT8 cache with the
+witness bound at 32768 context (B=16, H=32, D=128), prefilled with 32768
+rotary keys.
 
 Prints ONE JSON line on stdout.  ``value`` is the whole step's algorithmic
-HBM bytes per second (GB/s); ``roofline`` reports the decode kernel alone,
+HBM bytes per second (GB/s); ``roofline`` reports the timed call alone,
 timed with HIP events on its launch stream; ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10]
-       [--workload NAME] [--no-cpu-baseline] [--calibrate-copy]
+       [--workload NAME] [--no-cpu-baseline] [--no-fuse]
+       [--flush auto|on|off] [--calibrate-copy]
 """
 
 from __future__ import annotations
