@@ -88,6 +88,32 @@ constexpr float kNegBig = -1e30f;  // finite start value of the running max
 #define SWA_ROW_U 4
 #endif
 
+// Grid order: (split, h, b), or (split, b, h) for paged pools, so that the
+// hardware's turn-by-turn hand-out of work-groups to the XCDs puts all heads
+// of a sequence on one XCD, whose L2 then reads the sequence's block-table
+// lines once, and whose reads of a page's heads (adjacent in the pool) come
+// together.
+#ifndef SWA_ROW_PAGED_SEQ_MAJOR
+#define SWA_ROW_PAGED_SEQ_MAJOR 1
+#endif
+#ifndef SWA_ROW_RING_SEQ_MAJOR
+#define SWA_ROW_RING_SEQ_MAJOR 0
+#endif
+template <bool PAGED>
+constexpr bool kRowSeqMajor = PAGED ? SWA_ROW_PAGED_SEQ_MAJOR : SWA_ROW_RING_SEQ_MAJOR;
+template <bool PAGED>
+__device__ __forceinline__ int row_grid_head() {
+  return kRowSeqMajor<PAGED> ? (int)blockIdx.z : (int)blockIdx.y;
+}
+template <bool PAGED>
+__device__ __forceinline__ int row_grid_seq() {
+  return kRowSeqMajor<PAGED> ? (int)blockIdx.y : (int)blockIdx.z;
+}
+inline dim3 row_grid(const swa_cache& c, int nsplit) {
+  const bool seq_major = c.layout == SWA_LAYOUT_PAGED ? kRowSeqMajor<true> : kRowSeqMajor<false>;
+  return seq_major ? dim3(nsplit, c.B, c.H) : dim3(nsplit, c.H, c.B);
+}
+
 // The decode of one (split, h, b) work-group, called by decode_kernel and
 // by the fused step kernel; n is next_position[b] as this decode sees it.
 // FINAL: the host plan has one split per (b, h), so the work-group writes
@@ -110,7 +136,7 @@ __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = row_grid_head<PAGED>(), b = row_grid_seq<PAGED>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * H + h;
@@ -272,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const uint4* __restrict__ K, const uint4* __restrict__ V, const int32_t* __restrict__ np,
     const int32_t* __restrict__ table, int64_t num_pages, const uint4* __restrict__ q, float* __restrict__ out,
     float* __restrict__ part, int H, int W, int chunk, int nsplit_max) {
-  decode_rows_wg<T, D, NW, U, PAGED, FINAL>(np[blockIdx.z], K, V, table, num_pages, q, out, part, H, W, chunk,
+  decode_rows_wg<T, D, NW, U, PAGED, FINAL>(np[row_grid_seq<PAGED>()], K, V, table, num_pages, q, out, part, H, W, chunk,
                                             nsplit_max);
 }
 
@@ -291,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
     const uint4* v_new, int64_t num_pages, const uint4* q, float* out, float* part, int H, int W, int chunk,
     int nsplit_max) {
   constexpr int VPR = D / RowFmt<T>::kEpv;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = row_grid_head<PAGED>(), b = row_grid_seq<PAGED>();
   const int64_t bh = (int64_t)b * H + h;
   const int n0 = np[b];
   if (n0 >= 0) {
@@ -350,7 +376,7 @@ hipError_t launch_one(const swa_cache& c, const void* q, float* out, void* ws, c
                       hipStream_t s) {
   constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
   float* part = reinterpret_cast<float*>(ws);
-  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  const dim3 grid = row_grid(c, plan.nsplit_max), block(NW * 64);
   const bool paged = c.layout == SWA_LAYOUT_PAGED;
   // paged: one int per 16-slot block of a split, plus slack
   const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
@@ -381,7 +407,7 @@ hipError_t launch_step_one(const swa_cache& c, const void* k_new, const void* v_
   const bool paged = c.layout == SWA_LAYOUT_PAGED;
   const bool final_pass = plan.nsplit_max == 1;
   const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
-  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  const dim3 grid = row_grid(c, plan.nsplit_max), block(NW * 64);
   float* part = reinterpret_cast<float*>(ws);
   int32_t* cnt = step_counters(c, plan, ws);
 #define SWA_ROW_STEP(P, F)                                                                                        \

@@ -16,7 +16,8 @@
 // The newest n mod 16 tokens are exact bf16 rows in the staging area and
 // carry c_t = 0; the last stage (finish_int8) folds them in.
 //
-// Layout of the work: grid (split, h, b), NW waves; a split owns `cb`
+// Layout of the work: grid (split, h, b) (paged pools: (split, b, h), see
+// grid_head below), NW waves; a split owns `cb`
 // consecutive blocks; a wave takes UB blocks per iteration.  When the plan
 // has one split per (b, h) (FINAL), the work-group runs the last stage
 // itself.  Otherwise every split writes a partial (m, l, cmax, acc[D]) and
@@ -280,6 +281,33 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
 // filled before the commit (lines are shared across heads).  The pointers
 // carry no restrict qualifier because the fused step writes the same
 // buffers first.
+// Grid order.  A paged pool keeps the fp32 block scales of every head of a
+// page in one [P][H] line.  The hardware hands work-groups to the XCDs in
+// turn, so with the grid (split, h, b) the heads of a sequence spread over
+// all XCDs and each XCD's L2 fetches every scale line; with (split, b, h)
+// all heads of a sequence share one XCD (B a multiple of 8 keeps the XCDs
+// evenly loaded) and the line is fetched once.
+#ifndef SWA_INT8_PAGED_SEQ_MAJOR
+#define SWA_INT8_PAGED_SEQ_MAJOR 1
+#endif
+#ifndef SWA_INT8_RING_SEQ_MAJOR
+#define SWA_INT8_RING_SEQ_MAJOR 0
+#endif
+template <bool PAGED>
+constexpr bool kSeqMajor = PAGED ? SWA_INT8_PAGED_SEQ_MAJOR : SWA_INT8_RING_SEQ_MAJOR;
+template <bool PAGED>
+__device__ __forceinline__ int grid_head() {
+  return kSeqMajor<PAGED> ? (int)blockIdx.z : (int)blockIdx.y;
+}
+template <bool PAGED>
+__device__ __forceinline__ int grid_seq() {
+  return kSeqMajor<PAGED> ? (int)blockIdx.y : (int)blockIdx.z;
+}
+inline dim3 int8_grid(const swa_cache& c, int nsplit) {
+  const bool seq_major = c.layout == SWA_LAYOUT_PAGED ? kSeqMajor<true> : kSeqMajor<false>;
+  return seq_major ? dim3(nsplit, c.B, c.H) : dim3(nsplit, c.H, c.B);
+}
+
 template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER, bool APPEND>
 __device__ __forceinline__ void decode_int8_wg(
     int n, int kb_new, float sk_new, float sv_new, const int8_t* Kc, const int8_t* Vc, const float* ksc,
@@ -292,7 +320,7 @@ __device__ __forceinline__ void decode_int8_wg(
   __shared__ float sm_acc[NW][D];
   __shared__ float sm_s[16];
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = grid_head<PAGED>(), b = grid_seq<PAGED>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int t = threadIdx.x;
@@ -579,13 +607,12 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
     const uint16_t* __restrict__ kst, const uint16_t* __restrict__ vst, float* __restrict__ out,
     float* __restrict__ cmax_out, float* __restrict__ tv, int32_t* __restrict__ gate, float tau,
     const uint64_t* __restrict__ req, uint32_t layer, float delta) {
-  decode_int8_wg<NW, UB, PAGED, FINAL, DITHER, false>(np[blockIdx.z], -1, 0.f, 0.f, Kc, Vc, ksc, vsc, wit, table,
+  decode_int8_wg<NW, UB, PAGED, FINAL, DITHER, false>(np[grid_seq<PAGED>()], -1, 0.f, 0.f, Kc, Vc, ksc, vsc, wit, table,
                                                       num_pages, q, c_all, part, H, W, cb, nsplit_max, kst, vst,
                                                       out, cmax_out, tv, gate, tau, req, layer, delta);
 }
 
-// Fused decode step (one token per sequence): grid (split, h, b) as the
-// decode's.  First the token is appended: into the staging rows (by split
+// Fused decode step (one token per sequence): the decode's grid.  First the token is appended: into the staging rows (by split
 // 0), or -- when the token completes a 16-token block -- by quantizing that
 // block (waves 0 and 1 of the split that owns the block, exactly as
 // kv_append does).  After a barrier every work-group decodes its split with
@@ -606,7 +633,7 @@ __global__ __launch_bounds__(NW * 64) void decode_step_int8_kernel(
     const uint16_t* q, float* part, int H, int W, int cb, int nsplit_max, uint16_t* kst, uint16_t* vst, float* out,
     float* cmax_out, float* tv, int32_t* gate, float tau, float delta) {
   __shared__ float sm_scale[2];
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = grid_head<PAGED>(), b = grid_seq<PAGED>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * H + h;
   const int n0 = np[b];
@@ -715,7 +742,7 @@ hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const 
   const Dither dz{dither ? c.request_id : nullptr, c.layer};
   float* part = reinterpret_cast<float*>(ws);
   int32_t* cnt = step_counters(c, plan, ws);
-  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  const dim3 grid = int8_grid(c, plan.nsplit_max), block(NW * 64);
   const size_t lds = paged ? ((size_t)plan.unit_per_split + 1) * sizeof(int32_t) : 0;
   const int32_t* table = paged ? c.block_table : nullptr;
   const int64_t npages = paged ? c.num_pages : 0;
@@ -756,7 +783,7 @@ hipError_t launch_decode_int8(const swa_cache& c, const void* q, float* out, flo
     if (e != hipSuccess) return e;
   }
   float* part = reinterpret_cast<float*>(ws);
-  const dim3 grid(plan.nsplit_max, c.H, c.B), block(NW * 64);
+  const dim3 grid = int8_grid(c, plan.nsplit_max), block(NW * 64);
   const bool paged = c.layout == SWA_LAYOUT_PAGED;
   const size_t lds = paged ? ((size_t)plan.unit_per_split + 1) * sizeof(int32_t) : 0;
   const int8_t* kc = reinterpret_cast<const int8_t*>(c.k);
