@@ -702,8 +702,7 @@ __global__ __launch_bounds__(256) void merge_int8_kernel(
   float M = kNegBig, L = 0.f, A = 0.f, CM = 0.f;
   if (t < D) {
     const float* pp = part + bh * nsplit_max * PF;
-    merge_partials<PF>(pp, nsplit, t, M, L, A);
-    for (int sp = 0; sp < nsplit; ++sp) CM = fmaxf(CM, pp[sp * PF + 2]);
+    merge_partials<PF, true>(pp, nsplit, t, M, L, A, &CM);
   }
   finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta, &st);
 }

@@ -153,44 +153,45 @@ struct RowMap {
 
 // Log-sum-exp merge of split partials laid out as [nsplit][PF] floats with
 // m at 0, l at 1 and acc at 4.. (base-2 scores): M = max m_s, L = sum
-// 2^(m_s-M) l_s, A = sum 2^(m_s-M) acc_s[t].  Loads are issued eight splits
-// at a time so their latencies overlap.
-template <int PF>
+// 2^(m_s-M) l_s, A = sum 2^(m_s-M) acc_s[t]; with CMAX also CM = max of the
+// floats at 2.  One pass: eight splits' values are loaded together (a
+// short last group re-reads its last split, masked out of the sums, so
+// every load is unconditional and the waits stay exact), then folded in
+// with a running maximum.  Up to eight splits cost one memory round trip.
+template <int PF, bool CMAX = false>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int nsplit, int t, float& M,
-                                               float& L, float& A) {
+                                               float& L, float& A, float* CM = nullptr) {
   M = -1e30f;
-  int sp = 0;
-  for (; sp + 8 <= nsplit; sp += 8) {
-    float m8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m8[i] = pp[(sp + i) * PF];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) M = fmaxf(M, m8[i]);
-  }
-  for (; sp < nsplit; ++sp) M = fmaxf(M, pp[sp * PF]);
   L = 0.f;
   A = 0.f;
-  sp = 0;
-  for (; sp + 8 <= nsplit; sp += 8) {
-    float m8[8], l8[8], a8[8];
+  float cm = 0.f;
+  for (int sp = 0; sp < nsplit; sp += 8) {
+    const int n = nsplit - sp < 8 ? nsplit - sp : 8;
+    float m8[8], l8[8], a8[8], c8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      m8[i] = pp[(sp + i) * PF];
-      l8[i] = pp[(sp + i) * PF + 1];
-      a8[i] = pp[(sp + i) * PF + 4 + t];
+      const float* pi = pp + (sp + (i < n ? i : n - 1)) * PF;
+      m8[i] = pi[0];
+      l8[i] = pi[1];
+      a8[i] = pi[4 + t];
+      if constexpr (CMAX) c8[i] = pi[2];
     }
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mc = fmaxf(mc, m8[i]);
+    const float r = exp2_fast(M - mc);
+    L *= r;
+    A *= r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float sc = exp2_fast(m8[i] - M);
+      const float sc = i < n ? exp2_fast(m8[i] - mc) : 0.f;
       L = fmaf(l8[i], sc, L);
       A = fmaf(a8[i], sc, A);
+      if constexpr (CMAX) cm = fmaxf(cm, c8[i]);
     }
+    M = mc;
   }
-  for (; sp < nsplit; ++sp) {
-    const float sc = exp2_fast(pp[sp * PF] - M);
-    L = fmaf(pp[sp * PF + 1], sc, L);
-    A = fmaf(pp[sp * PF + 4 + t], sc, A);
-  }
+  if constexpr (CMAX) *CM = cm;
 }
 
 }  // namespace swa
