@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 import torch
 
-from tests.gpu_util import assert_close, check_ring_rows, f64, host_bits, oracle_out, require_gpu, say
+from tests.gpu_util import (assert_close, check_dither_decode, check_int8_decode, check_ring_rows, f64, host_bits,
+                            oracle_out, request_ids, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,3 +165,48 @@ def test_ragged_fused_step_graph():
     k64, v64, q64 = f64(k), f64(v), f64(qs[-1])
     _check_all(out.cpu().numpy(), k64, v64, q64, [n + steps for n in lens], W, "graph last replay")
     assert swa.validate(cg) == 0
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "int8_dither"])
+def test_unwritten_partials_are_never_read(kind):
+    """A caller's workspace whose partial slots hold NaN bit patterns (only
+    the step counters, the last B 256-byte lines, zeroed as the C ABI
+    requires): with lengths that leave most of the planned splits empty, the
+    merge must read only the splits that were written this call."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, D, W = 3, 2, 128, 1024
+    lens = [1, 100, W + 37]
+    say("NaN workspace", kind)
+    g = torch.Generator().manual_seed(19)
+    N = max(lens) + 1
+    k = torch.randn((B, H, N, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, N, D), generator=g).to(torch.bfloat16)
+    qs = torch.randn((2, B, H, D), generator=g).to(torch.bfloat16)
+    cache = swa.KVCache(kind, B, H, D, W)
+    _prefill(swa, cache, k, v, lens)
+    ws = torch.full((swa.workspace_bytes(cache),), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[-B * 256:].zero_()
+    k64, v64, q64 = f64(k), f64(v), f64(qs)
+    if kind == "bf16":
+        out = swa.decode_attn(cache, qs[0].cuda(), ws=ws).cpu().numpy()
+        _check_all(out, k64, v64, q64[0], lens, W, "NaN workspace decode")
+        kn = torch.stack([k[b, :, n:n + 1] for b, n in enumerate(lens)]).contiguous().cuda()
+        vn = torch.stack([v[b, :, n:n + 1] for b, n in enumerate(lens)]).contiguous().cuda()
+        out = swa.decode_step(cache, kn, vn, qs[1].cuda(), ws=ws).cpu().numpy()
+        _check_all(out, k64, v64, q64[1], [n + 1 for n in lens], W, "NaN workspace step")
+    elif kind == "int8":
+        out, cmax, c_all = swa.decode_attn_int8_witness(cache, qs[0].cuda(), ws=ws, want_c_all=True)
+        out, cmax, c_all = out.cpu().numpy(), cmax.cpu().numpy(), c_all.cpu().numpy()
+        for b, n in enumerate(lens):
+            for h in range(H):
+                check_int8_decode(out[b, h], cmax[b, h], c_all[b, h], b, h, q64[0, b, h], k64[b, h], v64[b, h], n,
+                                  W, "NaN workspace")
+    else:
+        out, cert, tv, gate = (x.cpu().numpy() for x in swa.decode_attn_int8_dither(cache, qs[0].cuda(),
+                                                                                      delta=1e-3, ws=ws))
+        reqs = request_ids(cache)
+        for b, n in enumerate(lens):
+            for h in range(H):
+                check_dither_decode(out[b, h], cert[b, h], b, h, q64[0, b, h], k64[b, h], v64[b, h], n, W, reqs[b],
+                                    cache.layer, 1e-3, tv[b, h], gate[b, h], what="NaN workspace")
+    assert swa.validate(cache) == 0
