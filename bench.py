@@ -346,7 +346,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": read_traffic(wl.name, wl.kind),
-            "kernel": ("decode step call" if fuse else
+            "kernel": ((("decode_step_int8_kernel" if wl.kind.startswith("int8") else "decode_step_rows_kernel")
+                        + " (the step call; plus the merge kernel when a (b, h) has several splits)") if fuse else
                        "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel"),
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_median": round(kern_median, 4),
