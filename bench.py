@@ -283,26 +283,42 @@ def main():
     # compete with the timed step (measured: 3-20% slower steps, most for the smallest).
     scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev) if flush else None
     sink = torch.zeros((), dtype=torch.float32, device=dev) if flush else None
+    # Per-call event pairs only where the timed call must be told apart from
+    # other work in the stream (the flush, or the append of --no-fuse): each
+    # event marker costs the stream about 4 us.  Otherwise one pair of events
+    # spans the K calls, and a call's time is their average, launch gaps
+    # included.
+    per_call = flush or not fuse
+    span = tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    if not per_call:
+        span[0].record(stream)
     for i in range(args.steps):
         j = args.warmup + i
         if flush:
             sink.copy_(scratch.amax())
-            evs[i][0].record(stream)  # only needed to time a flushed step; each marker costs queue latency
+            evs[i][0].record(stream)
         if fuse:
-            evs[i][1].record(stream)
+            if per_call:
+                evs[i][1].record(stream)
             fused(j)
         else:
             swa.kv_append(cache, ks[j], vs[j])
             evs[i][1].record(stream)
             decode(qs[j])
-        evs[i][2].record(stream)
+        if per_call:
+            evs[i][2].record(stream)
+    if not per_call:
+        span[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    dec_ms = sorted(e1.elapsed_time(e2) for _, e1, e2 in evs)
-    kern_ms = sum(dec_ms) / args.steps
-    kern_median = dec_ms[args.steps // 2] if args.steps % 2 else 0.5 * (dec_ms[args.steps // 2 - 1] + dec_ms[args.steps // 2])
+    if per_call:
+        dec_ms = sorted(e1.elapsed_time(e2) for _, e1, e2 in evs)
+        kern_ms = sum(dec_ms) / args.steps
+        kern_median = dec_ms[args.steps // 2] if args.steps % 2 else 0.5 * (dec_ms[args.steps // 2 - 1] + dec_ms[args.steps // 2])
+    else:
+        kern_ms = kern_median = span[0].elapsed_time(span[1]) / args.steps
     if flush:
         # the flush is not part of the step: time the steps by their events
         elapsed = sum(e0.elapsed_time(e2) for e0, _, e2 in evs) * 1e-3
@@ -351,6 +367,9 @@ def main():
                        "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel"),
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_median": round(kern_median, 4),
+            "timing": ("HIP event pair around each timed call on its stream" if per_call else
+                       "HIP event pair around the K timed calls on their stream (average per call, launch gaps "
+                       "included)"),
             "algorithmic_bytes_per_launch": timed_bytes / args.steps,
         },
         "cpu_baseline": None,
