@@ -16,7 +16,7 @@ HBM bytes per second (GB/s); ``roofline`` reports the timed call alone,
 timed with HIP events on its launch stream; ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 20]
        [--workload NAME] [--no-cpu-baseline] [--no-fuse]
        [--flush auto|on|off] [--calibrate-copy]
 """
@@ -174,7 +174,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=INT8_32K.name, choices=sorted(ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fuse", action="store_true",
