@@ -169,8 +169,9 @@ constexpr float kDitherBeta = 0x1p-9f + 0x1p-16f;
 // DITHER: CM is the largest key scale S of the visible blocks, and the bound
 // written to cmax_out is the Tier B certificate built from S, the query
 // norms, n_q and delta (see the top of this file).
-// The staging-tail inputs of the last stage, loaded ahead by the merge
-// kernel so that their latency overlaps the loads of the split partials:
+// The staging-tail inputs of the last stage, loaded ahead (by the merge
+// kernel before the split partials, by a one-split work-group before its
+// wave merge) so that their latencies overlap:
 // thread t (< 256)'s 8 dims of staged key row t/16 and of q, and for t < D
 // the staged values of dim t.  All 16 staging rows are allocated, so the
 // loads need no guard (rows at or past the staged count are read but not
@@ -273,14 +274,6 @@ __device__ __forceinline__ void finish_int8(int t, int64_t bh, int n, float M, f
   }
 }
 
-// The decode of one (split, h, b) work-group, called by decode_int8_kernel
-// and by the fused step kernel; n is next_position[b] as this decode sees
-// it.  APPEND (fused step): block kb_new, unless -1, was committed by this
-// work-group in this launch, and its two scales are taken from sk_new /
-// sv_new, not from memory -- a scalar-cache line holding them may have been
-// filled before the commit (lines are shared across heads).  The pointers
-// carry no restrict qualifier because the fused step writes the same
-// buffers first.
 // Grid order.  A paged pool keeps the fp32 block scales of every head of a
 // page in one [P][H] line.  The hardware hands work-groups to the XCDs in
 // turn, so with the grid (split, h, b) the heads of a sequence spread over
@@ -308,6 +301,14 @@ inline dim3 int8_grid(const swa_cache& c, int nsplit) {
   return seq_major ? dim3(nsplit, c.B, c.H) : dim3(nsplit, c.H, c.B);
 }
 
+// The decode of one (split, h, b) work-group, called by decode_int8_kernel
+// and by the fused step kernel; n is next_position[b] as this decode sees
+// it.  APPEND (fused step): block kb_new, unless -1, was committed by this
+// work-group in this launch, and its two scales are taken from sk_new /
+// sv_new, not from memory -- a scalar-cache line holding them may have been
+// filled before the commit (lines are shared across heads).  The pointers
+// carry no restrict qualifier because the fused step writes the same
+// buffers first.
 template <int NW, int UB, bool PAGED, bool FINAL, bool DITHER, bool APPEND>
 __device__ __forceinline__ void decode_int8_wg(
     int n, int kb_new, float sk_new, float sv_new, const int8_t* Kc, const int8_t* Vc, const float* ksc,
@@ -546,6 +547,12 @@ __device__ __forceinline__ void decode_int8_wg(
     }
   }
 
+  // FINAL: the staging rows and the query for the fold in finish_int8, all
+  // requested at once, while the waves merge (one memory round trip instead
+  // of one per staged token).
+  StageRows st;
+  if constexpr (FINAL) load_stage(st, t, bh, kst, vst, q);
+
   if constexpr (DITHER) {
     // the -(127.5/256) sum p s_V term of every element (code - u = (t - 127.5)/256)
 #pragma unroll
@@ -588,7 +595,7 @@ __device__ __forceinline__ void decode_int8_wg(
   }
 
   if constexpr (FINAL) {
-    finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta);
+    finish_int8<DITHER>(t, bh, n, M, L, A, CM, sm_s, kst, vst, q, out, cmax_out, tv, gate, tau, W, delta, &st);
   } else {
     float* my = part + (bh * nsplit_max + split) * PF;
     if (t < D) my[4 + t] = A;
