@@ -99,8 +99,8 @@ __device__ __forceinline__ float commit_block_wave(int lane, bool key, const uin
     pw[i] = (uint32_t)(uint8_t)cq[4 * i] | ((uint32_t)(uint8_t)cq[4 * i + 1] << 8) |
             ((uint32_t)(uint8_t)cq[4 * i + 2] << 16) | ((uint32_t)(uint8_t)cq[4 * i + 3] << 24);
   }
-  reinterpret_cast<uint4*>(dst)[0] = packed[0];
-  reinterpret_cast<uint4*>(dst)[1] = packed[1];
+  store_stream(reinterpret_cast<uint4*>(dst), packed[0]);
+  store_stream(reinterpret_cast<uint4*>(dst) + 1, packed[1]);
   if (lane == 0) scale[map.block(b, h, slot)] = s;
   if (key && pos_b != nullptr && part == 0) pos_b[slot] = (int32_t)p;
   if (key && !dith) {
@@ -119,7 +119,7 @@ __device__ __forceinline__ float commit_block_wave(int lane, bool key, const uin
     uint2 o;
     o.x = (uint32_t)wb[0] | ((uint32_t)wb[1] << 16);
     o.y = (uint32_t)wb[2] | ((uint32_t)wb[3] << 16);
-    reinterpret_cast<uint2*>(witness + row_idx * (kD8 / 8))[part] = o;
+    store_stream(reinterpret_cast<uint2*>(witness + row_idx * (kD8 / 8)) + part, o);
   }
   return s;
 }

@@ -325,8 +325,8 @@ __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
     if (slot / chunk == split) {
       const int64_t row = map.row(b, h, slot);
       for (int i = threadIdx.x; i < 2 * VPR; i += NW * 64) {
-        if (i < VPR) K[row * VPR + i] = k_new[bh * VPR + i];
-        else V[row * VPR + (i - VPR)] = v_new[bh * VPR + (i - VPR)];
+        if (i < VPR) store_stream(K + row * VPR + i, k_new[bh * VPR + i]);
+        else store_stream(V + row * VPR + (i - VPR), v_new[bh * VPR + (i - VPR)]);
       }
       if (h == 0 && threadIdx.x == 0) pos[(int64_t)b * W + slot] = n0;
     }

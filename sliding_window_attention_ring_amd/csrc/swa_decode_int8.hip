@@ -667,7 +667,7 @@ __global__ __launch_bounds__(NW * 64) void decode_step_int8_kernel(
       const bool key = threadIdx.x < 16;
       const uint4* src = reinterpret_cast<const uint4*>(key ? k_new : v_new) + bh * 16 + v16;
       uint4* dst = reinterpret_cast<uint4*>(key ? kst : vst) + (bh * 16 + (n0 & 15)) * 16 + v16;
-      *dst = *src;
+      store_stream(dst, *src);
     }
   }
   __syncthreads();

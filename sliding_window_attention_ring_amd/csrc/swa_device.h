@@ -122,6 +122,18 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Non-temporal vector store, for the few rows a decode step writes: a line
+// left dirty in L2 would be written back in the middle of the step's read
+// stream, and each such write costs DRAM a read/write turnaround.
+__device__ __forceinline__ void store_stream(uint4* p, const uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(uint2* p, const uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+
 // A page id read from a caller-filled block table, clamped into the pool so
 // that a bad entry can never address memory outside it (swa_validate
 // reports such entries).
