@@ -13,7 +13,9 @@ What pins it:
   pairs, and the textbook relative-position property of rotary embeddings;
 * exactly quantizable data (zero residual) reduces INT8 attention to the
   plain masked attention;
-* the storage format printed on the page (16 bands, 32 B per token-head).
+* the storage format printed on the page (16 bands, 32 B per token-head);
+* every field of the expected INT8 ring store (slot positions, key and value
+  codes and scales, witness rows) against brute force from exact rationals.
 """
 
 from fractions import Fraction
@@ -186,6 +188,66 @@ def test_expected_store_consistent():
         sc, codes = int8.quantize_block(k[blk * 16:(blk + 1) * 16])
         assert st["k_scale"][s // 16] == sc
         np.testing.assert_array_equal(st["k_codes"][s], codes[p % 16])
+
+
+def _brute_block(x32: np.ndarray):
+    """Scale and codes of one [16, D] float32 block from exact rationals:
+    s = nearest float32 of max|x| / 127; code = nearest integer (ties to even)
+    of the nearest float32 of x / s, clamped to +-127; s = 0 gives zeros."""
+    a = max(abs(Fraction(float(x))) for x in x32.ravel())
+    s = nearest_f32(a / 127)
+    if s == 0:
+        return s, np.zeros(x32.shape, dtype=np.int64)
+    codes = np.zeros(x32.shape, dtype=np.int64)
+    for idx in np.ndindex(x32.shape):
+        quot = Fraction(float(nearest_f32(Fraction(float(x32[idx])) / Fraction(float(s)))))
+        lo = quot.numerator // quot.denominator          # floor
+        rest = quot - lo
+        c = lo + 1 if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and lo % 2) else lo
+        codes[idx] = max(-127, min(127, c))
+    return s, codes
+
+
+@pytest.mark.parametrize("n,w,zero_block", [(16 * 9 + 5, 64, None), (40, 64, 1), (16 * 12, 32, 10)])
+def test_expected_store_values_and_witness_brute_force(n, w, zero_block):
+    """Every stored field of ``expected_int8_store`` against brute force from
+    exact rationals, slot by slot: the slot's position (newest committed
+    position congruent to the slot), the key and value codes and scales of
+    the block that position belongs to, and the witness rows (band norms of
+    the exact key residual k - s_K code, compared through their squares,
+    exactly).  Covers a wrapped ring, an unfilled one and an all-zero block."""
+    rng = np.random.default_rng(n + w)
+    d = 32
+    k = (rng.standard_normal((n, d)) * 3).astype(np.float32)
+    v = (rng.standard_normal((n, d)) * 0.5).astype(np.float32)
+    if zero_block is not None:
+        k[zero_block * 16:(zero_block + 1) * 16] = 0
+        v[zero_block * 16:(zero_block + 1) * 16] = 0
+    st = decoder.expected_int8_store(k, v, n, w)
+    nb = n // 16
+    blocks = {}
+    for blk in range(max(0, nb - w // 16), nb):
+        rows = slice(blk * 16, blk * 16 + 16)
+        blocks[blk] = (_brute_block(k[rows]), _brute_block(v[rows]))
+    for slot in range(w):
+        cands = [p for p in range(16 * nb) if p % w == slot]
+        want = max(cands) if cands else -1
+        assert st["slot_pos"][slot] == want, slot
+        if want < 0:
+            assert not st["k_codes"][slot].any() and not st["v_codes"][slot].any()
+            assert not st["witness"][slot].any()
+            continue
+        (sk, ck), (sv, cv) = blocks[want // 16]
+        r = want % 16
+        assert st["k_scale"][slot // 16] == sk and st["v_scale"][slot // 16] == sv, slot
+        np.testing.assert_array_equal(st["k_codes"][slot], ck[r])
+        np.testing.assert_array_equal(st["v_codes"][slot], cv[r])
+        res = [Fraction(float(k[want, c])) - Fraction(float(sk)) * int(ck[r, c]) for c in range(d)]
+        for band in range(d // 8):
+            exact = sum(x * x for x in res[8 * band:8 * band + 8])
+            got = Fraction(float(st["witness"][slot, band])) ** 2
+            assert abs(got - exact) <= Fraction(1, 10 ** 14) * exact, (slot, band)
+    assert st["staged_positions"] == list(range(16 * nb, n))
 
 
 def test_storage_format(golden):
