@@ -2,14 +2,19 @@
  * swa.h -- C ABI of the sliding-window ring-buffer KV cache and its decode
  * step, built as hand-written HIP for AMD gfx950 (MI355X).
  *
- * The cache follows the record described on the page "LLM 機制實驗（五）"
- * (huhohoo.com, section 哪些東西必須一起裁剪): keys, values, the absolute
- * position of every stored row, and next_position, the position the next
- * token receives.  Its physical form is the fixed array of W slots of the page
- * "用Lean4形式化验证滑动窗口KV Cache的正确性" (framerc.cn, §3.4): the token at
- * absolute position p lives in slot p mod W and overwrites the oldest.  The
- * decode query of step t attends to exactly the positions [t-len+1, t],
- * len = min(W, t+1) (same page, §2.1 window and causal masks; §2.4 goal 3).
+ * Pages cited, by title (sections as named on each page):
+ *  [Lean-SWA]     "用Lean4形式化验证滑动窗口KV Cache的正确性"
+ *  [Prefix-Reuse] "LLM 機制實驗（五）：改了歷史，能否只重算變化的後綴？"
+ *  [KV-Loop]      "【AI 工业核题 D4】KV Cache 自回归生成推理（增量更新与状态拼接）"
+ *  [WitCert]      "WitCert：运行时误差仪表盘，把崩溃的KV量化从22.8拉回79.7"
+ *
+ * The cache follows the record of [Prefix-Reuse] (section 哪些東西必須一起裁剪):
+ * keys, values, the absolute position of every stored row, and
+ * next_position, the position the next token receives.  Its physical form is
+ * the fixed array of W slots of [Lean-SWA] §3.4: the token at absolute
+ * position p lives in slot p mod W and overwrites the oldest.  The decode
+ * query of step t attends to exactly the positions [t-len+1, t],
+ * len = min(W, t+1) ([Lean-SWA] §2.1 window and causal masks; §2.4 goal 3).
  *
  * Conventions shared by every entry point
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -37,11 +42,13 @@ extern "C" {
 
 enum {
   SWA_OK = 0,
-  SWA_EINVAL = -1,       /* B, H, W < 1, T < 0, W*D*elem >= 2^32, unknown layout, or W not a
-                            multiple of 16 for INT8 kinds or PAGED */
+  SWA_EINVAL = -1,       /* B, H, W < 1, T < 1, D not in {16, 32, 64, 128, 256},
+                            W*D*elem >= 2^32, unknown layout, or W not a multiple of 16
+                            for INT8 kinds or PAGED */
   SWA_ENULL = -2,        /* a required pointer is NULL */
   SWA_EALIGN = -3,       /* a K/V/q/out/staging/workspace pointer is not 16-byte aligned */
-  SWA_EUNSUPPORTED = -4, /* head_dim or kind not supported by this entry point */
+  SWA_EUNSUPPORTED = -4, /* unknown kind, a kind this entry point does not take, or an
+                            INT8 kind with D != 128 */
   SWA_EWORKSPACE = -5,   /* ws_bytes < swa_workspace_bytes(cache) */
   SWA_EHIP = -6          /* a kernel launch failed */
 };
@@ -54,15 +61,18 @@ enum {
 };
 
 /* Physical layout of the rows (the logical cache is the same either way:
- * the window lastWindow(W, history), framerc.cn §3.4 and §6.1).
+ * the window lastWindow(W, history), [Lean-SWA] §3.4 and §6.1).
  * RING:  one contiguous ring of W slots per (b, h).
  * PAGED: pools of 16-token pages shared by all sequences (the paging of
- *        airsota.com §八, pages of 16 tokens); block_table[b][j] names the
+ *        [KV-Loop] §八, pages of 16 tokens); block_table[b][j] names the
  *        page holding ring slots 16j..16j+15 of sequence b.  Needs W % 16 == 0. */
 enum { SWA_LAYOUT_RING = 0, SWA_LAYOUT_PAGED = 1 };
 
-/* Cache descriptor.  Supported head_dim D: BF16 {64, 128, 256}; FP32
- * {16, 32, 64, 128}; INT8 and INT8_DITHER {128} (16 bands of 8 dims).
+/* Cache descriptor.  head_dim D is one of {16, 32, 64, 128, 256} for the
+ * BF16 and FP32 kinds ([KV-Loop] §三 takes head_dim as a free parameter).
+ * The INT8 kinds take D = 128 only: [WitCert] (section 频带酉性与双层证书)
+ * fixes 16 bands of 8 dims and 32 witness bytes per token and head at its
+ * head_dim of 128; another D is SWA_EUNSUPPORTED.
  *
  *  RING layout                   PAGED layout (P = num_pages)
  *  k, v       [B][H][W][D]       [P][H][16][D]    bf16 | fp32 | int8 codes
@@ -87,6 +97,15 @@ enum { SWA_LAYOUT_RING = 0, SWA_LAYOUT_PAGED = 1 };
  *                                entries for blocks the sequence uses must be
  *                                in [0, P), and no two sequences may share a
  *                                page; unused entries are ignored
+ *  step_sync      [B][64] int32  completion counters of the fused decode step
+ *                                (decode_step, decode_step_int8): element
+ *                                [b][0] counts the work-groups of sequence b
+ *                                that finished the current step (the rest of
+ *                                the 256-byte line is padding, so sequences
+ *                                never queue on one line).  Zero after
+ *                                swa_cache_reset, and every fused step leaves
+ *                                it zero.  May be NULL if the fused steps are
+ *                                not used (they return SWA_ENULL then).
  */
 typedef struct swa_cache {
   int32_t kind, B, H, D, W;
@@ -101,29 +120,30 @@ typedef struct swa_cache {
   int64_t num_pages;    /* PAGED only */
   uint64_t *request_id; /* INT8_DITHER only */
   uint32_t layer;       /* INT8_DITHER only */
+  int32_t *step_sync;   /* fused decode steps only */
 } swa_cache;
 
-/* Empty the cache: next_position[b] = 0 and pos[b][*] = -1 for every b (a
- * RING cache of an INT8 kind also clears its block scales; PAGED pools, which other
- * caches may share, are not touched).  Row contents are left as they are; no
+/* Empty the cache: next_position[b] = 0, pos[b][*] = -1 and step_sync[b][*]
+ * = 0 (when set) for every b (a RING cache of an INT8 kind also clears its
+ * block scales; PAGED pools, which other caches may share, are not touched).  Row contents are left as they are; no
  * slot is visible until written.  Errors: SWA_EINVAL, SWA_ENULL, SWA_EHIP. */
 int swa_cache_reset(const swa_cache *c, void *stream);
 
-/* Append T tokens per sequence (prefill chunk or one decode token).
- * framerc.cn §2.2 and §3.3-§3.4: write, evict the oldest when over W;
- * airsota.com §三 step 1 (write at the current position); huhohoo.com
- * (next_position advances with the rows).
+/* Append T >= 1 tokens per sequence (prefill chunk or one decode token).
+ * [Lean-SWA] §2.2 and §3.3-§3.4: write, evict the oldest when over W;
+ * [KV-Loop] §三 step 1 (write at the current position); [Prefix-Reuse]
+ * (section 哪些東西必須一起裁剪: next_position advances with the rows).
  *  k_new, v_new  [B][H][T][D] in the cache's input dtype (INT8 kinds: bf16).
  * Token j of sequence b gets position p = next_position[b] + j and slot
  * p mod W; pos[b][slot] = p; afterwards next_position[b] += T.  Only the last
  * min(T, W) tokens are stored (the others would be overwritten).
- * INT8 kind (agifrontier.github.io WitCert, section 频带酉性与双层证书: the
+ * INT8 kind ([WitCert], section 频带酉性与双层证书: the
  * write path quantizes and records band norms of the residual): a token first
  * goes to the staging rows; when the block of positions [16m, 16m+16) is
  * complete it is quantized into slots (16m mod W).. with one fp32 absmax/127
  * scale per block and tensor, codes rint(x/s) clamped to +-127, and the key
  * residual's 16 band norms written rounded up to fp16.
- * INT8_DITHER kind (WitCert, section 频带酉性与双层证书, Tier B: a uniform
+ * INT8_DITHER kind ([WitCert], section 频带酉性与双层证书, Tier B: a uniform
  * pseudo-random dither is added before rounding at write time and subtracted
  * at read time; section SGLang 生产级落地: Philox keyed by request, layer,
  * KV head, token and channel): the same blocks and scales, and
@@ -132,23 +152,25 @@ int swa_cache_reset(const swa_cache *c, void *stream);
  * (request_id mod 2^32, request_id div 2^32) and counter (position, c / 16,
  * head, layer); the words are taken in order, each little-endian.  Keys and
  * values of one token share u.  request_id must be set.  No witness is
- * written.  T = 0 is a no-op. */
+ * written.  T < 1 is SWA_EINVAL. */
 int kv_append(const swa_cache *c, const void *k_new, const void *v_new, int32_t T, void *stream);
 
 /* Decode attention for one query per sequence over the last min(W, n) tokens,
- * n = next_position[b] (append first, then attend: airsota.com §三 steps 2-4;
+ * n = next_position[b] (append first, then attend: [KV-Loop] §三 steps 2-4;
  * scores q.k/sqrt(D), max-subtracted softmax, weighted V).  BF16 and FP32
  * kinds.  Split over the context with an online softmax; a second kernel
  * merges the splits of each (b, h).
  *  q    [B][H][D]  cache input dtype
  *  out  [B][H][D]  fp32; a sequence with n = 0 gets zeros
  *  ws   device workspace of ws_bytes >= swa_workspace_bytes(c) holding the
- *       split partials; its contents need no initialization.  Calls sharing
- *       one workspace must be ordered on one stream. */
+ *       split partials; its contents need no initialization, and no call
+ *       leaves state in it that a later call reads.  One workspace may serve
+ *       any caches (of any shape) as long as it is large enough for each and
+ *       the calls that use it are ordered on one stream. */
 int decode_attn(const swa_cache *c, const void *q, float *out, void *ws, size_t ws_bytes,
                 void *stream);
 
-/* INT8 decode attention with the fused witness bound (WitCert, section
+/* INT8 decode attention with the fused witness bound ([WitCert], section
  * 频带酉性与双层证书: |q.r_t|/sqrt(d) <= c_t = (1/sqrt(d)) sum_b ||q_b|| w_{t,b};
  * section SGLang 生产级落地: per-block scales fold into per-token scalars).
  * Visible tokens in committed blocks are read as scale*code, the newest
@@ -164,7 +186,7 @@ int decode_attn_int8_witness(const swa_cache *c, const void *q, float *out, floa
                              float *c_all, void *ws, size_t ws_bytes, void *stream);
 
 /* decode_attn_int8_witness plus a total-variation bound and a gate flag
- * (WitCert, section 为什么在线监控 KV 误差如此困难: prior work bounds the TV of
+ * ([WitCert], section 为什么在线监控 KV 误差如此困难: prior work bounds the TV of
  * the attention weights by tanh of the largest logit error; section SGLang
  * 生产级落地: the decode pass emits a per-step TV bound for the gate).
  * Every visible logit moved by at most cmax, so
@@ -180,7 +202,7 @@ int decode_attn_int8_witness_tv(const swa_cache *c, const void *q, float *out, f
                                 int32_t *gate, float tau, float *c_all, void *ws, size_t ws_bytes,
                                 void *stream);
 
-/* Tier B decode (WitCert, section 频带酉性与双层证书: with dithered INT8 the
+/* Tier B decode ([WitCert], section 频带酉性与双层证书: with dithered INT8 the
  * residual is uniform and independent of the data, so a sub-Gaussian
  * concentration bound with a failure budget replaces the stored witness).
  * INT8_DITHER kind.  Committed tokens are read as s * (code - u), with u
@@ -211,64 +233,56 @@ int decode_attn_int8_dither(const swa_cache *c, const void *q, float *out, float
                             int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes, void *stream);
 
 /* One decode step in one call for the BF16 and FP32 kinds: kv_append of
- * one token per sequence, then decode_attn (airsota.com §三: write at the
+ * one token per sequence, then decode_attn ([KV-Loop] §三: write at the
  * current position, then attend).  The result is bit for bit that of
  * kv_append(c, k_new, v_new, 1) followed by decode_attn.  The append and
  * the decode are one kernel launch: the work-group whose split holds slot
  * next_position mod W of a (b, h) writes the token's rows there, then every
- * work-group decodes its split; the last work-group of a sequence to finish
- * advances next_position.  A plan with several splits per (b, h) adds the
- * merge launch, as decode_attn does.
+ * work-group decodes its split; the last work-group of a sequence to finish,
+ * counted in the cache's step_sync, advances next_position.  A plan with
+ * several splits per (b, h) adds the merge launch, as decode_attn does.
  *  k_new, v_new  [B][H][1][D] in the cache's input dtype
- *  q, out        as for decode_attn
- *  ws            as for decode_step_int8 (its counters zero before the
- *                first call; swa_workspace_init does that)
- * Errors: descriptor errors, SWA_EUNSUPPORTED for an INT8 kind, SWA_ENULL,
- * SWA_EALIGN, SWA_EWORKSPACE, SWA_EHIP. */
+ *  q, out, ws    as for decode_attn
+ * Errors: descriptor errors, SWA_EUNSUPPORTED for an INT8 kind, SWA_ENULL
+ * (also for a NULL step_sync), SWA_EALIGN, SWA_EWORKSPACE, SWA_EHIP. */
 int decode_step(const swa_cache *c, const void *k_new, const void *v_new, const void *q, float *out, void *ws,
                 size_t ws_bytes, void *stream);
 
 /* One decode step in one call: kv_append of one token per sequence, then
- * the INT8 decode of that sequence's query (airsota.com §三: write at the
- * current position, then attend; WitCert, section SGLang 生产级落地: one
+ * the INT8 decode of that sequence's query ([KV-Loop] §三: write at the
+ * current position, then attend; [WitCert], section SGLang 生产级落地: one
  * fused pass per step).  INT8 kinds only.  The result is bit for bit that
  * of kv_append(c, k_new, v_new, 1) followed by decode_attn_int8_witness_tv
  * (INT8) or decode_attn_int8_dither (INT8_DITHER) with the same arguments.
  * The append and the decode are one kernel launch: for each (b, h) one
  * work-group appends the token (quantizing the block it completes, in the
  * work-group whose split decodes that block), then every work-group decodes
- * its split; the last work-group of a sequence to finish advances
- * next_position.  A plan with several splits per (b, h) adds the merge
- * launch, as the decode entry points do.
+ * its split; the last work-group of a sequence to finish, counted in the
+ * cache's step_sync, advances next_position.  A plan with several splits per
+ * (b, h) adds the merge launch, as the decode entry points do.
  *  k_new, v_new  [B][H][1][D] bf16
  *  q, out, cmax, tv, gate, tau  as for decode_attn_int8_witness_tv; cmax is
  *                the certificate for INT8_DITHER
  *  delta         INT8_DITHER failure budget, in (0, 1]; ignored for INT8
- *  ws            the decode workspace; its B per-sequence counters (after
- *                the split partials) must be zero before the first call --
- *                swa_workspace_init does that -- and every call leaves them
- *                zero.  Calls sharing a workspace must be ordered on one
- *                stream.
+ *  ws            as for decode_attn
  * Errors: descriptor errors, SWA_EUNSUPPORTED for a non-INT8 kind,
- * SWA_ENULL, SWA_EALIGN, SWA_EINVAL (NaN tau; delta outside (0, 1] for
- * INT8_DITHER), SWA_EWORKSPACE, SWA_EHIP. */
+ * SWA_ENULL (also for a NULL step_sync), SWA_EALIGN, SWA_EINVAL (NaN tau;
+ * delta outside (0, 1] for INT8_DITHER), SWA_EWORKSPACE, SWA_EHIP. */
 int decode_step_int8(const swa_cache *c, const void *k_new, const void *v_new, const void *q, float *out,
                      float *cmax, float *tv, int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes,
                      void *stream);
 
 /* Workspace bytes the decode entry points need for this cache shape: the
- * split partials (B*H*nsplit*(D+4) floats) padded to 256 bytes, then B
- * int32 counters for decode_step and decode_step_int8, one per 256-byte
- * line.  0 for an invalid descriptor. */
+ * split partials, B*H*nsplit*(D+4) floats, padded to 256 bytes (nsplit is
+ * the largest number of context splits any (b, h) can need under the
+ * library's split plan).  0 for an invalid descriptor. */
 size_t swa_workspace_bytes(const swa_cache *c);
 
-/* Zero-fill a workspace.  The decode entry points overwrite the partials
- * they read; decode_step and decode_step_int8 need the counters zero
- * before their first call.
- * Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
+/* Zero-fill a workspace (optional: the decode entry points overwrite every
+ * partial they read).  Errors: SWA_ENULL, SWA_EALIGN, SWA_EHIP. */
 int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* Prefix reuse (huhohoo.com, sections 哪些東西必須一起裁剪 and
+/* Prefix reuse ([Prefix-Reuse], sections 哪些東西必須一起裁剪 and
  * 為什麼滑窗部分命中必須回退): truncate sequence b to its first cut[b] tokens,
  * so the next appended token gets position cut[b] -- when that is exact.
  * It is exact iff every row of the shorter history's window is still
@@ -282,7 +296,7 @@ int swa_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * Errors: SWA_ENULL, SWA_EALIGN, descriptor errors, SWA_EHIP. */
 int kv_truncate(const swa_cache *c, const int32_t *cut, int32_t *ok, void *stream);
 
-/* Debug check of the position invariant (framerc.cn §3.2 PositionInvariant,
+/* Debug check of the position invariant ([Lean-SWA] §3.2 PositionInvariant,
  * §6.3 the invariant as a runtime assertion): adds to *violations (device
  * int32, caller zeroes it) the number of slots whose pos differs from the
  * newest position p < n (INT8 kinds: p < 16*(n/16)) with p mod W == slot, or -1;

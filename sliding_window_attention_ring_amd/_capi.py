@@ -33,6 +33,7 @@ class SwaCacheDesc(ctypes.Structure):
         ("k_stage", ctypes.c_void_p), ("v_stage", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("num_pages", ctypes.c_int64),
         ("request_id", ctypes.c_void_p), ("layer", ctypes.c_uint32),
+        ("step_sync", ctypes.c_void_p),
     ]
 
 

@@ -54,7 +54,8 @@ class KVCache:
     D/8]) and ``block_table`` [B, W/16] int32 names the page of each ring
     block; by default every sequence gets W/16 distinct pages in a seeded
     shuffled order.  Per-sequence tensors: ``pos`` [B, W], ``next_position``
-    [B] and, for INT8, ``k_stage``/``v_stage`` [B, H, 16, D].
+    [B], ``step_sync`` [B, 64] (the fused step's completion counters, zero
+    between calls) and, for INT8, ``k_stage``/``v_stage`` [B, H, 16, D].
     """
 
     def __init__(self, kind: str, B: int, H: int, D: int, W: int, device="cuda", layout: str = "ring",
@@ -81,6 +82,7 @@ class KVCache:
         self.v = torch.empty_like(self.k)
         self.pos = torch.empty((B, W), dtype=torch.int32, device=dev)
         self.next_position = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.step_sync = torch.empty((B, 64), dtype=torch.int32, device=dev)
         self.k_scale = self.v_scale = self.witness = self.k_stage = self.v_stage = None
         if kind in ("int8", "int8_dither"):
             scales = (self.num_pages, H) if paged else (B, H, W // 16)
@@ -127,7 +129,7 @@ class KVCache:
                             per_seq(self.next_position), pool(self.k_scale), pool(self.v_scale),
                             pool(self.witness), per_seq(self.k_stage), per_seq(self.v_stage),
                             per_seq(self.block_table), self.num_pages, per_seq(self.request_id),
-                            self.layer & 0xFFFFFFFF)
+                            self.layer & 0xFFFFFFFF, per_seq(self.step_sync))
 
     def seq_view(self, b: int) -> "SeqView":
         """Descriptor of sequence ``b`` alone (B = 1), for ragged appends."""
@@ -138,11 +140,10 @@ class KVCache:
         return _INPUT_DTYPE[self.kind]
 
     def workspace(self) -> torch.Tensor:
-        """The decode workspace of this cache, allocated and zero-filled once."""
+        """The decode workspace of this cache (split partials), allocated once."""
         if self._ws is None:
             nbytes = workspace_bytes(self)
             self._ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.k.device)
-            workspace_init(self._ws)
         return self._ws
 
 

@@ -17,15 +17,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool is_int8(int kind) { return kind == SWA_KV_INT8 || kind == SWA_KV_INT8_DITHER; }
 
-bool head_dim_supported(int kind, int D) {
-  switch (kind) {
-    case SWA_KV_BF16: return D == 64 || D == 128 || D == 256;
-    case SWA_KV_FP32: return D == 16 || D == 32 || D == 64 || D == 128;
-    case SWA_KV_INT8:
-    case SWA_KV_INT8_DITHER: return D == 128;
-  }
-  return false;
-}
+bool head_dim_valid(int D) { return D == 16 || D == 32 || D == 64 || D == 128 || D == 256; }
 
 // Descriptor checks common to every entry point.
 int check_cache(const swa_cache* c) {
@@ -34,7 +26,9 @@ int check_cache(const swa_cache* c) {
   if (c->B < 1 || c->H < 1 || c->W < 1) return SWA_EINVAL;
   if (c->layout != SWA_LAYOUT_RING && c->layout != SWA_LAYOUT_PAGED) return SWA_EINVAL;
   if (c->B > 65535 || c->H > 65535) return SWA_EINVAL;  // grid y/z limits
-  if (!head_dim_supported(c->kind, c->D)) return SWA_EUNSUPPORTED;
+  if (!head_dim_valid(c->D)) return SWA_EINVAL;
+  // The INT8 kinds keep 16 bands of 8 dims per key (32 witness bytes).
+  if (is_int8(c->kind) && c->D != 128) return SWA_EUNSUPPORTED;
   if (is_int8(c->kind) && c->W % 16 != 0) return SWA_EINVAL;
   // The decode kernels address one (b, h) region with 32-bit byte offsets.
   const int64_t esz = c->kind == SWA_KV_FP32 ? 4 : c->kind == SWA_KV_BF16 ? 2 : 1;
@@ -61,6 +55,7 @@ int check_cache(const swa_cache* c) {
     if (!c->request_id) return SWA_ENULL;
     if ((uintptr_t)c->request_id & 7u) return SWA_EALIGN;
   }
+  if ((uintptr_t)c->step_sync & 3u) return SWA_EALIGN;
   return SWA_OK;
 }
 
@@ -96,15 +91,18 @@ int target_wgs(int kind) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 __global__ void reset_kernel(int32_t* __restrict__ pos, int32_t* __restrict__ np, float* __restrict__ ks,
-                             float* __restrict__ vs, int B, int H, int W, int int8) {
+                             float* __restrict__ vs, int32_t* __restrict__ sync, int B, int H, int W, int int8) {
   const int64_t npos = (int64_t)B * W;
   const int64_t nsc = int8 ? (int64_t)B * H * (W / 16) : 0;
-  const int64_t total = npos > nsc ? npos : nsc;
+  const int64_t nsync = sync != nullptr ? (int64_t)B * kCounterStride : 0;
+  int64_t total = npos > nsc ? npos : nsc;
+  total = total > nsync ? total : nsync;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     if (i < npos) pos[i] = -1;
     if (i < B) np[i] = 0;
     if (i < nsc) { ks[i] = 0.f; vs[i] = 0.f; }
+    if (i < nsync) sync[i] = 0;
   }
 }
 
@@ -167,12 +165,13 @@ SplitPlan plan_decode(const swa_cache& c) {
 }
 
 hipError_t launch_reset(const swa_cache& c, hipStream_t s) {
-  const int64_t n = (int64_t)c.B * c.W > (int64_t)c.B * c.H * (c.W / 16) ? (int64_t)c.B * c.W
-                                                                          : (int64_t)c.B * c.H * (c.W / 16);
+  int64_t n = (int64_t)c.B * c.W > (int64_t)c.B * c.H * (c.W / 16) ? (int64_t)c.B * c.W
+                                                                    : (int64_t)c.B * c.H * (c.W / 16);
+  if (n < (int64_t)c.B * kCounterStride) n = (int64_t)c.B * kCounterStride;
   // Pools of a paged cache may be shared with other caches: leave them alone.
   const int clear_scales = is_int8(c.kind) && c.layout == SWA_LAYOUT_RING ? 1 : 0;
-  hipLaunchKernelGGL(reset_kernel, dim3(grid_for(n > c.B ? n : c.B, 256, 1 << 16)), dim3(256), 0, s, c.pos,
-                     c.next_position, c.k_scale, c.v_scale, c.B, c.H, c.W, clear_scales);
+  hipLaunchKernelGGL(reset_kernel, dim3(grid_for(n, 256, 1 << 16)), dim3(256), 0, s, c.pos, c.next_position,
+                     c.k_scale, c.v_scale, c.step_sync, c.B, c.H, c.W, clear_scales);
   return hipGetLastError();
 }
 
@@ -230,8 +229,7 @@ int swa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 int kv_append(const swa_cache* c, const void* k_new, const void* v_new, int32_t T, void* stream) {
   int st = check_cache(c);
   if (st != SWA_OK) return st;
-  if (T < 0) return SWA_EINVAL;
-  if (T == 0) return SWA_OK;
+  if (T < 1) return SWA_EINVAL;
   if (k_new == nullptr || v_new == nullptr) return SWA_ENULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return SWA_EALIGN;
   const hipStream_t s = (hipStream_t)stream;
@@ -300,7 +298,9 @@ int decode_step(const swa_cache* c, const void* k_new, const void* v_new, const 
   int st = check_cache(c);
   if (st != SWA_OK) return st;
   if (is_int8(c->kind)) return SWA_EUNSUPPORTED;
-  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || ws == nullptr) return SWA_ENULL;
+  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || ws == nullptr ||
+      c->step_sync == nullptr)
+    return SWA_ENULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) || !aligned16(ws))
     return SWA_EALIGN;
   if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
@@ -315,7 +315,8 @@ int decode_step_int8(const swa_cache* c, const void* k_new, const void* v_new, c
   int st = check_cache(c);
   if (st != SWA_OK) return st;
   if (!is_int8(c->kind)) return SWA_EUNSUPPORTED;
-  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || cmax == nullptr || ws == nullptr)
+  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || cmax == nullptr || ws == nullptr ||
+      c->step_sync == nullptr)
     return SWA_ENULL;
   if (gate != nullptr && tv == nullptr) return SWA_ENULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) || !aligned16(ws))

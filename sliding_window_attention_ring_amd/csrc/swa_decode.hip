@@ -130,8 +130,12 @@ __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint
   constexpr int RPL = 64 / LPR;         // rows per wave load
   constexpr int RPI = RPL * U;          // rows per wave iteration
   constexpr int PF = D + 4;             // floats per split partial
-  static_assert(LPR >= 2 && LPR <= 32, "row must span 2..32 lanes");
-  static_assert(16 % RPL == 0, "a wave load must not straddle a 16-row page");
+  // A row spans 2..64 lanes.  A wave load covers RPL rows: up to 16 rows
+  // (one page, wave-uniform), or 32 rows of two pages (bf16 D = 16), whose
+  // page is then looked up per lane.
+  static_assert(LPR >= 2 && LPR <= 64, "row must span 2..64 lanes");
+  static_assert(16 % RPL == 0 || RPL == 32, "a wave load spans at most two 16-row pages");
+  constexpr bool kLanePage = RPL > 16;
 
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
@@ -181,12 +185,18 @@ __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint
       int row = base + u * RPL + g;
       row = row < r1 ? row : r1 - 1;  // past the end: re-read a live row, masked below
       if constexpr (PAGED) {
-        // The RPL rows of load u lie in one 16-row page (RPL divides 16 and
-        // the split starts on a page), also after clamping at the end, so the
+        // The RPL rows of load u lie in one 16-row page when RPL divides 16
+        // (the split starts on a page), also after clamping at the end, so the
         // page is wave-uniform: a scalar base plus a 32-bit lane offset.
-        int first = base + u * RPL;
-        first = first < r1 ? first : r1 - 1;
-        const int64_t page = __builtin_amdgcn_readfirstlane(sm_pages[(first >> 4) - pb0]);
+        // With 32 rows per load each lane looks its own page up.
+        int64_t page;
+        if constexpr (kLanePage) {
+          page = sm_pages[(row >> 4) - pb0];
+        } else {
+          int first = base + u * RPL;
+          first = first < r1 ? first : r1 - 1;
+          page = __builtin_amdgcn_readfirstlane(sm_pages[(first >> 4) - pb0]);
+        }
         const int64_t pbase = (page * H + h) * (16 * VPR * 16);
         const uint32_t off = (uint32_t)((row & 15) * VPR + vec) * 16u;
         kb[u] = load_stream(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(K) + pbase + off));
@@ -308,8 +318,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 // h == 0, the slot's position); after a barrier every work-group decodes its
 // split with next_position + 1.  The rows are read only by the work-group
 // that wrote them.  next_position[b] is advanced by the last of the work-groups
-// of sequence b to finish, elected by a per-sequence counter in the
-// workspace, as in the INT8 step kernel.  A negative next_position (a
+// of sequence b to finish, elected by the sequence's counter in the cache's
+// step_sync, as in the INT8 step kernel.  A negative next_position (a
 // violated precondition) appends nothing and advances nothing.
 template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
 __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
@@ -409,7 +419,7 @@ hipError_t launch_step_one(const swa_cache& c, const void* k_new, const void* v_
   const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
   const dim3 grid = row_grid(c, plan.nsplit_max), block(NW * 64);
   float* part = reinterpret_cast<float*>(ws);
-  int32_t* cnt = step_counters(c, plan, ws);
+  int32_t* cnt = c.step_sync;
 #define SWA_ROW_STEP(P, F)                                                                                        \
   hipLaunchKernelGGL((decode_step_rows_kernel<T, D, NW, U, P, F>), grid, block, lds, s,                           \
                      reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.next_position, c.pos, cnt,    \
@@ -433,6 +443,8 @@ hipError_t launch_decode_step_rows(const swa_cache& c, const void* k_new, const 
                                    float* out, void* ws, const SplitPlan& plan, hipStream_t s) {
   if (c.kind == SWA_KV_BF16) {
     switch (c.D) {
+      case 16: return launch_step_one<uint16_t, 16>(c, k_new, v_new, q, out, ws, plan, s);
+      case 32: return launch_step_one<uint16_t, 32>(c, k_new, v_new, q, out, ws, plan, s);
       case 64: return launch_step_one<uint16_t, 64>(c, k_new, v_new, q, out, ws, plan, s);
       case 128: return launch_step_one<uint16_t, 128>(c, k_new, v_new, q, out, ws, plan, s);
       case 256: return launch_step_one<uint16_t, 256>(c, k_new, v_new, q, out, ws, plan, s);
@@ -443,6 +455,7 @@ hipError_t launch_decode_step_rows(const swa_cache& c, const void* k_new, const 
       case 32: return launch_step_one<float, 32>(c, k_new, v_new, q, out, ws, plan, s);
       case 64: return launch_step_one<float, 64>(c, k_new, v_new, q, out, ws, plan, s);
       case 128: return launch_step_one<float, 128>(c, k_new, v_new, q, out, ws, plan, s);
+      case 256: return launch_step_one<float, 256>(c, k_new, v_new, q, out, ws, plan, s);
     }
   }
   return hipErrorInvalidValue;
@@ -460,6 +473,8 @@ hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws
                          hipStream_t s) {
   if (c.kind == SWA_KV_BF16) {
     switch (c.D) {
+      case 16: return launch_one<uint16_t, 16>(c, q, out, ws, plan, s);
+      case 32: return launch_one<uint16_t, 32>(c, q, out, ws, plan, s);
       case 64: return launch_one<uint16_t, 64>(c, q, out, ws, plan, s);
       case 128: return launch_one<uint16_t, 128>(c, q, out, ws, plan, s);
       case 256: return launch_one<uint16_t, 256>(c, q, out, ws, plan, s);
@@ -470,6 +485,7 @@ hipError_t launch_decode(const swa_cache& c, const void* q, float* out, void* ws
       case 32: return launch_one<float, 32>(c, q, out, ws, plan, s);
       case 64: return launch_one<float, 64>(c, q, out, ws, plan, s);
       case 128: return launch_one<float, 128>(c, q, out, ws, plan, s);
+      case 256: return launch_one<float, 256>(c, q, out, ws, plan, s);
     }
   }
   return hipErrorInvalidValue;

@@ -627,8 +627,8 @@ __global__ __launch_bounds__(NW * 64) void decode_int8_kernel(
 // only by the work-group that wrote them (the staging rows only by the last
 // stage, FINAL or the merge kernel), and the new block's scales come through
 // LDS (see decode_int8_wg).  next_position[b] is shared by the work-groups
-// of sequence b: each reads it first, and a per-sequence counter in the
-// workspace elects the last of them to finish, which writes
+// of sequence b: each reads it first, and the sequence's counter in the
+// cache's step_sync elects the last of them to finish, which writes
 // next_position + 1 and clears the counter.  Every work-group of b has read
 // next_position before it counts, so none reads the new value; the merge
 // kernel and the next launch do.  A negative next_position (a violated
@@ -747,7 +747,7 @@ hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const 
   const bool final_pass = plan.nsplit_max == 1;
   const Dither dz{dither ? c.request_id : nullptr, c.layer};
   float* part = reinterpret_cast<float*>(ws);
-  int32_t* cnt = step_counters(c, plan, ws);
+  int32_t* cnt = c.step_sync;
   const dim3 grid = int8_grid(c, plan.nsplit_max), block(NW * 64);
   const size_t lds = paged ? ((size_t)plan.unit_per_split + 1) * sizeof(int32_t) : 0;
   const int32_t* table = paged ? c.block_table : nullptr;

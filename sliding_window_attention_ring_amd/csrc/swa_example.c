@@ -192,10 +192,10 @@ int main(void) {
       CHECK_HIP(hipMalloc(&x->v_stage, (size_t)B * H * 16 * D8 * 2));
       CHECK_HIP(hipMalloc((void **)&x->pos, (size_t)B * W8 * 4));
       CHECK_HIP(hipMalloc((void **)&x->next_position, (size_t)B * 4));
-      CHECK_SWA(swa_cache_reset(x, NULL));
+      CHECK_HIP(hipMalloc((void **)&x->step_sync, (size_t)B * 64 * 4)); /* fused-step counters */
+      CHECK_SWA(swa_cache_reset(x, NULL));                                /* zeroes them too */
       const size_t wsb = swa_workspace_bytes(x);
-      CHECK_HIP(hipMalloc(&ws8[t], wsb));
-      CHECK_SWA(swa_workspace_init(ws8[t], wsb, NULL));  /* the counters start at zero */
+      CHECK_HIP(hipMalloc(&ws8[t], wsb > 16 ? wsb : 16));
       CHECK_HIP(hipMalloc((void **)&dout8[t], (size_t)B * H * D8 * 4));
       CHECK_HIP(hipMalloc((void **)&dcm8[t], (size_t)B * H * 4));
     }

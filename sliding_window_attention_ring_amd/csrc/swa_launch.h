@@ -53,21 +53,17 @@ hipError_t launch_decode_step_int8(const swa_cache& c, const void* k_new, const 
 hipError_t launch_decode_step_rows(const swa_cache& c, const void* k_new, const void* v_new, const void* q,
                                    float* out, void* ws, const SplitPlan& plan, hipStream_t s);
 
-// Workspace layout: split partials (B*H*nsplit_max*(D+4) floats), padded to
-// 256 bytes, then the B int32 counters of the fused step (zero between
-// calls), each in its own 256-byte line: atomics on one line are serialized,
+// Workspace layout: the split partials, B*H*nsplit_max*(D+4) floats,
+// padded to 256 bytes.  Nothing else: the fused step's per-sequence
+// completion counters live in the cache (step_sync), so a workspace carries
+// no state from one call to the next and any caches may share one.
+// Counters are one per 256-byte line: atomics on one line are serialized,
 // so sequences sharing a line would queue behind each other as their
 // work-groups finish together.
-constexpr int kCounterStride = 64;  // int32 per counter line
-inline size_t partials_bytes(const swa_cache& c, const SplitPlan& p) {
+constexpr int kCounterStride = 64;  // int32 per step_sync line
+inline size_t workspace_bytes_for(const swa_cache& c, const SplitPlan& p) {
   const size_t b = (size_t)c.B * c.H * (size_t)p.nsplit_max * partial_floats(c.D) * sizeof(float);
   return (b + 255) / 256 * 256;
-}
-inline size_t workspace_bytes_for(const swa_cache& c, const SplitPlan& p) {
-  return partials_bytes(c, p) + (size_t)c.B * kCounterStride * sizeof(int32_t);
-}
-inline int32_t* step_counters(const swa_cache& c, const SplitPlan& p, void* ws) {
-  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + partials_bytes(c, p));
 }
 
 hipError_t launch_reset(const swa_cache& c, hipStream_t s);

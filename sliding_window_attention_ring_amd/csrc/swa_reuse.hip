@@ -1,7 +1,7 @@
 // Prefix reuse: truncate each sequence of the cache to a common prefix, or
 // report that it must fall back to recomputation.
 //
-// Page "LLM 機制實驗（五）" (huhohoo.com): the reusable part of a cache is the
+// Page "LLM 機制實驗（五）：改了歷史，能否只重算變化的後綴？": the reusable part of a cache is the
 // leading run of unchanged tokens; K, V and positions of the first `cut`
 // rows are kept and the next token gets position `cut` (section
 // 哪些東西必須一起裁剪); a window cache that already evicted rows of that

@@ -32,6 +32,7 @@ static swa_cache desc(int kind, int B, int H, int D, int W, int layout) {
   c.witness = (uint16_t *)0x70000; c.k_stage = (void *)0x80000; c.v_stage = (void *)0x90000;
   c.block_table = (int32_t *)0xC0000; c.num_pages = 8;
   c.request_id = (uint64_t *)0xD0000; c.layer = 3;
+  c.step_sync = (int32_t *)0xE0000;
   return c;
 }
 
@@ -41,6 +42,7 @@ int main(void) {
   int32_t *I = (int32_t *)0xA0000;
   const int kinds[4] = {SWA_KV_BF16, SWA_KV_FP32, SWA_KV_INT8, SWA_KV_INT8_DITHER};
   const int dims[4] = {128, 16, 128, 128};
+  const int all_dims[5] = {16, 32, 64, 128, 256};
 
   for (int s = -8; s <= 1; ++s) {
     const char *t = swa_status_string(s);
@@ -60,7 +62,7 @@ int main(void) {
       EXPECT(kv_append(&c, ODD, A, 1, NULL), SWA_EALIGN);
       EXPECT(kv_append(&c, NULL, A, 1, NULL), SWA_ENULL);
       EXPECT(kv_append(&c, A, A, -3, NULL), SWA_EINVAL);
-      EXPECT(kv_append(&c, A, A, 0, NULL), SWA_OK);
+      EXPECT(kv_append(&c, A, A, 0, NULL), SWA_EINVAL);
       EXPECT(decode_attn(&c, A, F, ws, need - 1, NULL), i < 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
       EXPECT(decode_attn_int8_witness(&c, A, F, NULL, NULL, ws, need, NULL),
              kinds[i] == SWA_KV_INT8 ? SWA_ENULL : SWA_EUNSUPPORTED);
@@ -71,10 +73,32 @@ int main(void) {
       EXPECT(decode_step_int8(&c, A, A, A, F, F, NULL, NULL, 0.2f, 0.1f, ws, need - 1, NULL),
              i >= 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
       EXPECT(decode_step(&c, A, A, A, F, ws, need - 1, NULL), i < 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
+      swa_cache ns = c;
+      ns.step_sync = NULL; /* the fused steps need the completion counters */
+      EXPECT(decode_step(&ns, A, A, A, F, ws, need, NULL), i < 2 ? SWA_ENULL : SWA_EUNSUPPORTED);
+      EXPECT(decode_step_int8(&ns, A, A, A, F, F, NULL, NULL, 0.2f, 0.1f, ws, need, NULL),
+             i >= 2 ? SWA_ENULL : SWA_EUNSUPPORTED);
+      EXPECT(kv_append(&ns, NULL, A, 1, NULL), SWA_ENULL); /* the other calls do not */
+      ns.step_sync = (int32_t *)0xE0002;
+      EXPECT(kv_append(&ns, NULL, A, 1, NULL), SWA_EALIGN);
       EXPECT(kv_truncate(&c, NULL, NULL, NULL), SWA_ENULL);
       EXPECT(kv_truncate(&c, (const int32_t *)0xA0002, NULL, NULL), SWA_EALIGN);
       EXPECT(swa_validate(&c, NULL, NULL), SWA_ENULL);
     }
+  }
+
+  /* head dims: every kind takes {16, 32, 64, 128, 256}, except that the
+     INT8 kinds take 128 only; anything else is invalid.  A valid
+     descriptor reaches the argument checks (k_new NULL). */
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j) {
+      swa_cache d = desc(kinds[i], 2, 4, all_dims[j], 64, 0);
+      EXPECT(kv_append(&d, NULL, A, 1, NULL), i < 2 || all_dims[j] == 128 ? SWA_ENULL : SWA_EUNSUPPORTED);
+    }
+    swa_cache d = desc(kinds[i], 2, 4, 48, 64, 0);
+    EXPECT(kv_append(&d, NULL, A, 1, NULL), SWA_EINVAL);
+    d = desc(kinds[i], 2, 4, 512, 64, 0);
+    EXPECT(kv_append(&d, NULL, A, 1, NULL), SWA_EINVAL);
   }
 
   /* descriptor limits */
@@ -83,15 +107,19 @@ int main(void) {
   c = desc(SWA_KV_BF16, 1, 65536, 128, 64, 0);
   EXPECT(kv_append(&c, A, A, 1, NULL), SWA_EINVAL);            /* H above the grid limit */
   c = desc(SWA_KV_BF16, 1, 1, 256, 8388608, 0);
-  EXPECT(kv_append(&c, A, A, 0, NULL), SWA_EINVAL);            /* one (b, h) region reaches 4 GiB */
+  EXPECT(kv_append(&c, NULL, A, 1, NULL), SWA_EINVAL);         /* one (b, h) region reaches 4 GiB */
+  c = desc(SWA_KV_FP32, 1, 1, 256, 4194303, 0);
+  EXPECT(kv_append(&c, NULL, A, 1, NULL), SWA_ENULL);          /* largest fp32 D=256 window below 4 GiB */
+  c.W = 4194304;
+  EXPECT(kv_append(&c, NULL, A, 1, NULL), SWA_EINVAL);
   c = desc(SWA_KV_INT8, 1, 1, 128, 33554416, 0);
-  EXPECT(kv_append(&c, A, A, 0, NULL), SWA_OK);                /* largest INT8 window below 4 GiB */
+  EXPECT(kv_append(&c, NULL, A, 1, NULL), SWA_ENULL);          /* largest INT8 window below 4 GiB */
   if (swa_workspace_bytes(&c) == 0) ++failures;
   c = desc(SWA_KV_BF16, 65535, 65535, 128, 16, 0);
   if (swa_workspace_bytes(&c) < (size_t)65535 * 65535 * (128 + 4) * 4) ++failures;  /* no 32-bit overflow */
   c = desc(SWA_KV_INT8, 65535, 65535, 128, 2048, 1);
   c.num_pages = (int64_t)1 << 40;
-  EXPECT(kv_append(&c, A, A, 0, NULL), SWA_OK);
+  EXPECT(kv_append(&c, NULL, A, 1, NULL), SWA_ENULL);
   if (swa_workspace_bytes(&c) == 0) ++failures;
   c = desc(7, 1, 1, 128, 64, 0);
   EXPECT(kv_append(&c, A, A, 1, NULL), SWA_EUNSUPPORTED);

@@ -37,7 +37,8 @@ def desc(**kw):
     from sliding_window_attention_ring_amd._capi import SwaCacheDesc
     base = dict(kind=0, B=2, H=4, D=128, W=64, layout=0, k=0x10000, v=0x20000, pos=0x30000,
                 next_position=0x40000, k_scale=0x50000, v_scale=0x60000, witness=0x70000,
-                k_stage=0x80000, v_stage=0x90000, block_table=0xC0000, num_pages=8, request_id=None, layer=0)
+                k_stage=0x80000, v_stage=0x90000, block_table=0xC0000, num_pages=8, request_id=None, layer=0,
+                step_sync=0xE0000)
     base.update(kw)
     return SwaCacheDesc(**base)
 
@@ -63,17 +64,17 @@ def test_argument_checks_return_codes():
     assert L.kv_append(p(desc(layout=1, num_pages=0)), A16, A16, 1, None) == -1
     assert L.kv_append(p(desc(layout=1, block_table=None)), A16, A16, 1, None) == -2
     assert L.kv_append(p(desc(layout=1, block_table=0xC0002)), A16, A16, 1, None) == -3
-    assert L.kv_append(p(desc(layout=1)), A16, A16, 0, None) == 0
-    assert L.kv_append(p(desc(D=100)), A16, A16, 1, None) == -4             # head_dim
+    assert L.kv_append(p(desc(layout=1)), None, A16, 1, None) == -2         # valid: reaches the argument checks
+    assert L.kv_append(p(desc(D=100)), A16, A16, 1, None) == -1             # head_dim outside {16..256}
     assert L.kv_append(p(desc(kind=7)), A16, A16, 1, None) == -4
     assert L.kv_append(p(desc(kind=2, W=20)), A16, A16, 1, None) == -1      # INT8 W % 16
-    assert L.kv_append(p(desc(kind=2, D=64)), A16, A16, 1, None) == -4
+    assert L.kv_append(p(desc(kind=2, D=64)), A16, A16, 1, None) == -4      # INT8 takes D = 128 only
     assert L.kv_append(p(desc(kind=2, witness=None)), A16, A16, 1, None) == -2
     assert L.kv_append(p(desc(k=0x10004)), A16, A16, 1, None) == -3         # alignment
     assert L.kv_append(p(d), ODD, A16, 1, None) == -3
     assert L.kv_append(p(d), None, A16, 1, None) == -2
     assert L.kv_append(p(d), A16, A16, -1, None) == -1
-    assert L.kv_append(p(d), A16, A16, 0, None) == 0                        # T = 0: no-op
+    assert L.kv_append(p(d), A16, A16, 0, None) == -1                       # T < 1
     need = L.swa_workspace_bytes(p(d))
     assert need > 0 and L.swa_workspace_bytes(p(desc(D=100))) == 0
     assert L.decode_attn(p(d), A16, A16, ws, need - 1, None) == -5           # small workspace
@@ -89,8 +90,8 @@ def test_argument_checks_return_codes():
     # Tier B kind: no witness needed, request ids required, delta in (0, 1]
     dz = desc(kind=3, witness=None, request_id=0xD0000)
     nz = L.swa_workspace_bytes(p(dz))
-    assert nz > 0 and nz % 256 == 0  # partials and step counters, each padded to 256 bytes
-    assert L.kv_append(p(dz), A16, A16, 0, None) == 0
+    assert nz > 0 and nz % 256 == 0  # split partials, padded to 256 bytes
+    assert L.kv_append(p(dz), None, A16, 1, None) == -2
     assert L.kv_append(p(desc(kind=3, request_id=None)), A16, A16, 1, None) == -2
     assert L.kv_append(p(desc(kind=3, request_id=0xD0004)), A16, A16, 1, None) == -3
     assert L.kv_append(p(desc(kind=3, request_id=0xD0000, D=64)), A16, A16, 1, None) == -4
@@ -125,7 +126,7 @@ def test_argument_checks_return_codes():
 
 def test_workspace_size_follows_split_plan():
     """Workspace = B*H*nsplit*(D+4) floats of split partials, padded to 256
-    bytes, then B int32 step counters, one per 256-byte line."""
+    bytes, and nothing else (the fused step's counters live in the cache)."""
     from sliding_window_attention_ring_amd._capi import lib
     L = lib()
     for kw in [dict(kind=0, B=16, H=32, D=128, W=32768), dict(kind=2, B=16, H=32, D=128, W=32768),
@@ -133,7 +134,34 @@ def test_workspace_size_follows_split_plan():
         d = desc(**kw)
         nb = L.swa_workspace_bytes(ctypes.byref(d))
         per = kw["B"] * kw["H"] * (kw["D"] + 4) * 4
-        counters = kw["B"] * 256
-        assert nb % 256 == 0 and nb > counters
-        partials = nb - counters
-        assert any((ns * per + 255) // 256 * 256 == partials for ns in range(1, kw["W"] + 1))
+        assert nb % 256 == 0 and nb > 0
+        assert any((ns * per + 255) // 256 * 256 == nb for ns in range(1, kw["W"] + 1))
+
+
+def test_every_head_dim_of_the_contract():
+    """D in {16, 32, 64, 128, 256} for the bf16 and fp32 kinds; the INT8 kinds
+    take 128 only (SWA_EUNSUPPORTED otherwise); any other D is SWA_EINVAL."""
+    from sliding_window_attention_ring_amd._capi import lib
+    L = lib()
+    A16 = ctypes.c_void_p(0xA0000)
+    for kind in range(4):
+        for D in (16, 32, 64, 128, 256):
+            extra = dict(request_id=0xD0000) if kind == 3 else {}
+            d = desc(kind=kind, D=D, **extra)
+            want = -2 if (kind < 2 or D == 128) else -4   # valid: kv_append reaches its NULL k_new check
+            assert L.kv_append(ctypes.byref(d), None, A16, 1, None) == want, (kind, D)
+            assert (L.swa_workspace_bytes(ctypes.byref(d)) > 0) == (want == -2)
+        for D in (0, 8, 48, 96, 512):
+            assert L.kv_append(ctypes.byref(desc(kind=kind, D=D)), None, A16, 1, None) == -1
+
+
+def test_fused_steps_need_the_completion_counters():
+    from sliding_window_attention_ring_amd._capi import lib
+    L = lib()
+    p = ctypes.byref
+    A16, ws = ctypes.c_void_p(0xA0000), ctypes.c_void_p(0xB0000)
+    d, i8 = desc(step_sync=None), desc(kind=2, step_sync=None)
+    assert L.decode_step(p(d), A16, A16, A16, A16, ws, 1 << 30, None) == -2
+    assert L.decode_step_int8(p(i8), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, 1 << 30, None) == -2
+    assert L.kv_append(p(d), None, A16, 1, None) == -2                   # the other calls do not need them
+    assert L.kv_append(p(desc(step_sync=0xE0002)), None, A16, 1, None) == -3   # misaligned counters

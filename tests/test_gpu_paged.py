@@ -25,6 +25,9 @@ def _gpu():
     ("bf16", 128, 336, [1, 100, 700]),
     ("bf16", 64, 48, [3, 40]),
     ("bf16", 256, 32, [1, 70]),
+    ("bf16", 16, 80, [1, 33, 170]),
+    ("bf16", 32, 48, [5, 60]),
+    ("fp32", 256, 32, [1, 50]),
 ])
 def test_paged_rows(kind, D, W, Ts):
     for T in Ts:

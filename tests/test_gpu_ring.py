@@ -76,6 +76,8 @@ def test_bruteforce_small_windows_fp32(W):
 
 
 @pytest.mark.parametrize("kind,D,W,Ts", [
+    ("bf16", 16, 40, [1, 5, 33, 90]),
+    ("bf16", 32, 24, [1, 23, 50]),
     ("bf16", 64, 7, [1, 3, 8, 15]),
     ("bf16", 128, 64, [1, 17, 64, 65, 150]),
     ("bf16", 128, 333, [1, 100, 333, 700]),
@@ -83,6 +85,7 @@ def test_bruteforce_small_windows_fp32(W):
     ("fp32", 32, 20, [1, 7, 41]),
     ("fp32", 64, 50, [1, 49, 120]),
     ("fp32", 128, 70, [3, 71]),
+    ("fp32", 256, 30, [1, 29, 62]),
 ])
 def test_chunked_appends_all_head_dims(kind, D, W, Ts):
     say("sweep", kind, D, W, Ts)

@@ -154,7 +154,9 @@ def test_fused_step_headline_shape_and_graph():
 
 @pytest.mark.parametrize("kind,B,H,D,W,layout", [("bf16", 16, 32, 128, 64, "ring"), ("bf16", 16, 32, 128, 64, "paged"),
                                                  ("fp32", 1, 2, 16, 4, "ring"), ("bf16", 1, 2, 64, 4096, "ring"),
-                                                 ("bf16", 1, 2, 64, 4096, "paged"), ("fp32", 2, 3, 32, 1024, "ring")])
+                                                 ("bf16", 1, 2, 64, 4096, "paged"), ("fp32", 2, 3, 32, 1024, "ring"),
+                                                 ("bf16", 2, 3, 16, 2048, "paged"), ("bf16", 3, 2, 32, 96, "ring"),
+                                                 ("fp32", 2, 2, 256, 512, "ring")])
 def test_fused_row_step_equals_append_then_decode(kind, B, H, D, W, layout):
     """decode_step (bf16 / fp32 kinds) against kv_append + decode_attn on twin
     caches, bit for bit in the output and the ring state, over 3W ragged
@@ -325,3 +327,54 @@ def test_fused_step_several_splits_graph(kind):
             assert torch.equal(getattr(cg, name), getattr(ce, name)), f"replay {i}: {name}"
     assert host_bits(cg.next_position).tolist() == [n + steps for n in lens]
     assert swa.validate(cg) == 0
+
+
+def test_one_workspace_shared_by_caches_of_different_shapes():
+    """One caller workspace, filled with 0xFF bytes, serves fused steps on
+    three caches whose split plans differ (bf16 B=1 W=1024: 16 splits per
+    (b, h); bf16 B=3 W=16384: 43 splits; INT8 B=2 W=2048), interleaved on one
+    stream.  The workspace holds only split partials, so each step must equal
+    kv_append + the separate decode on a twin that has a workspace of its own
+    -- outputs bit for bit, next_position advanced by one every step."""
+    import sliding_window_attention_ring_amd as swa
+    shapes = [("bf16", 1, 2, 1024, [700]), ("bf16", 3, 2, 16384, [9000, 16384, 20000]),
+              ("int8", 2, 2, 2048, [1500, 2047])]
+    g = torch.Generator(device="cuda").manual_seed(23)
+    pairs = []
+    for kind, B, H, W, lens in shapes:
+        N = max(lens) + 40
+        k = torch.randn((B, H, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, H, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+        twin = []
+        for _ in range(2):
+            c = swa.KVCache(kind, B, H, 128, W)
+            for b, n in enumerate(lens):
+                swa.kv_append(c.seq_view(b), k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous())
+            twin.append(c)
+        pairs.append((twin, k, v, list(lens)))
+    need = max(swa.workspace_bytes(t[0]) for t, _, _, _ in pairs)
+    assert len({swa.workspace_bytes(t[0]) for t, _, _, _ in pairs}) == 3
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    say("shared workspace", need)
+    for step in range(12):
+        for i in (step % 3, (step + 1) % 3, (step + 2) % 3):
+            (cf, cs), k, v, lens = pairs[i]
+            n = lens
+            kn = torch.stack([k[b, :, x:x + 1] for b, x in enumerate(n)]).contiguous()
+            vn = torch.stack([v[b, :, x:x + 1] for b, x in enumerate(n)]).contiguous()
+            q = torch.randn((cf.B, cf.H, 128), generator=g, device="cuda").to(torch.bfloat16)
+            if cf.kind == "bf16":
+                got = (swa.decode_step(cf, kn, vn, q, ws=ws),)
+                swa.kv_append(cs, kn, vn)
+                ref = (swa.decode_attn(cs, q),)
+            else:
+                got = swa.decode_step_int8(cf, kn, vn, q, want_tv=True, ws=ws)
+                ref = separate(swa, cs, kn, vn, q, 0.2, 1e-6)
+            for a, b_ in zip(got, ref):
+                assert torch.equal(a, b_), f"step {step} cache {i}"
+            pairs[i] = ((cf, cs), k, v, [x + 1 for x in n])
+            assert host_bits(cf.next_position).tolist() == pairs[i][3], (step, i)
+    for (cf, cs), _, _, _ in pairs:
+        assert torch.equal(cf.pos, cs.pos) and torch.equal(cf.k, cs.k)
+        assert not cf.step_sync.any(), "every fused step leaves its counters zero"
+        assert swa.validate(cf) == 0

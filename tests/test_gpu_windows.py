@@ -19,7 +19,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("kind,W,D", [("bf16", 37, 128), ("bf16", 1000, 64), ("bf16", 4097, 128),
-                                       ("fp32", 1000, 32), ("fp32", 37, 16)])
+                                       ("fp32", 1000, 32), ("fp32", 37, 16), ("bf16", 1000, 16),
+                                       ("bf16", 37, 32), ("fp32", 333, 256)])
 def test_odd_windows(kind, W, D):
     import sliding_window_attention_ring_amd as swa
     B, H = 3, 2

@@ -41,8 +41,9 @@ def tokens(wl, which: str, n: int, device="cpu", b_range: Optional[range] = None
 
     ``which`` is "k" or "v".  Keys of a workload with ``spike_frac`` get that
     fraction of rows per (b, h) multiplied by ``spike_mul`` (exact in bf16 for
-    a power of two).  Keys and values of a workload with ``rope_base`` are
-    rotated at their absolute positions (interleaved pairs) before rounding.
+    a power of two).  Keys of a workload with ``rope_base`` are rotated at
+    their absolute positions (interleaved pairs) before rounding; values are
+    never rotated.
     """
     b_range = range(wl.B) if b_range is None else b_range
     out = torch.empty((len(b_range), wl.H, n, wl.D), dtype=storage_dtype(wl.kind), device=device)
