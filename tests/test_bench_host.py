@@ -94,3 +94,21 @@ def test_traffic_from_another_kernel_source_is_not_reported(tmp_path, monkeypatc
     assert bench.read_traffic(name, "int8") == 123456.0
     # the bf16 kernels hash other files
     assert bench.kernel_source_hash("bf16") != bench.kernel_source_hash("int8")
+
+
+def test_cpu_baseline_times_ragged_lengths():
+    """The oracle leg of the bench runs on a ragged workload too: each sampled
+    pair is timed at its own sequence's length, and its bytes follow it."""
+    import torch
+    from dataclasses import replace
+    from workloads import gen
+    wl = replace(workloads.ALL["full-cache-ragged-4096-bf16"], B=3, H=2, W=64)
+    ns = [10, 64, 100]
+    k = gen.tokens(wl, "k", 100)
+    v = gen.tokens(wl, "v", 100)
+    q = gen.query(wl, 0)
+    r = bench.cpu_baseline(wl, k, v, q, ns, budget_s=0.05)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    assert "contexts 10..64" in r["sample"]
+    assert r["kv_token_heads_per_s"] > 0
+    assert isinstance(k, torch.Tensor)

@@ -348,6 +348,9 @@ def test_one_workspace_shared_by_caches_of_different_shapes():
         twin = []
         for _ in range(2):
             c = swa.KVCache(kind, B, H, 128, W)
+            for name in ("k", "v", "k_scale", "v_scale", "witness", "k_stage", "v_stage"):
+                if getattr(c, name) is not None:  # never-written rows equal in both twins
+                    getattr(c, name).zero_()
             for b, n in enumerate(lens):
                 swa.kv_append(c.seq_view(b), k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous())
             twin.append(c)

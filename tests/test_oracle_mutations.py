@@ -139,7 +139,7 @@ def _copy_tree(dst: str) -> None:
     shutil.copytree(os.path.join(ROOT, "workloads"), os.path.join(dst, "workloads"), ignore=ign)
     os.makedirs(os.path.join(dst, "tests"))
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(dst, "tests", "golden"), ignore=ign)
-    for f in ["conftest.py", "gpu_util.py", *PIN_TESTS]:
+    for f in ["conftest.py", "gpu_util.py", "parity_checks.py", *PIN_TESTS]:
         shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(dst, "tests", f))
 
 
