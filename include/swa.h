@@ -272,6 +272,22 @@ int decode_step_int8(const swa_cache *c, const void *k_new, const void *v_new, c
                      float *cmax, float *tv, int32_t *gate, float tau, float delta, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* decode_step_int8 for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks and results (bit for bit) as
+ * decode_step_int8, without ws and ws_bytes: the split partials live in a
+ * static device array of the library, 16 MiB per GPU, held until the
+ * process ends.  Its device address is looked up on the first call on each
+ * device.  The call allocates nothing and needs nothing cleared: the merge
+ * reads only partials written in the same call.  All calls on one GPU share
+ * that GPU's array, so calls that overlap on one GPU (on different streams,
+ * or from several threads without ordering) race and give wrong results;
+ * order them on one stream.
+ * Errors: those of decode_step_int8, and SWA_EWORKSPACE when the shape
+ * needs more than 16 MiB of partials (swa_workspace_bytes(c) > 16 MiB). */
+int decode_step_int8_static(const swa_cache *c, const void *k_new, const void *v_new, const void *q, float *out,
+                            float *cmax, float *tv, int32_t *gate, float tau, float delta, void *stream);
+
 /* Workspace bytes the decode entry points need for this cache shape: the
  * split partials, B*H*nsplit*(D+4) floats, padded to 256 bytes (nsplit is
  * the largest number of context splits any (b, h) can need under the

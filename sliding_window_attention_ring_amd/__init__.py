@@ -10,11 +10,12 @@ is the thin Python binding: torch supplies device memory and the stream.
 
 from ._capi import EXPORTS, SwaError, lib
 from .cache import (KVCache, SeqView, cache_reset, decode_attn, decode_attn_int8_dither, decode_step, decode_step_int8,
-                    decode_attn_int8_witness, decode_attn_int8_witness_tv, kv_append, kv_truncate, status_string,
-                    validate, workspace_bytes, workspace_init)
+                    decode_step_int8_static, decode_attn_int8_witness, decode_attn_int8_witness_tv, kv_append,
+                    kv_truncate, status_string, validate, workspace_bytes, workspace_init)
 
 __all__ = ["KVCache", "SeqView", "SwaError", "EXPORTS", "lib", "cache_reset", "kv_append",
            "decode_attn", "decode_attn_int8_witness", "decode_attn_int8_witness_tv",
-           "decode_attn_int8_dither", "decode_step", "decode_step_int8", "workspace_bytes",
+           "decode_attn_int8_dither", "decode_step", "decode_step_int8", "decode_step_int8_static",
+           "workspace_bytes",
            "workspace_init", "kv_truncate",
            "validate", "status_string"]

@@ -16,8 +16,9 @@ LAYOUT = {"ring": 0, "paged": 1}
 
 # Every symbol include/swa.h declares.
 EXPORTS = ("swa_cache_reset", "kv_append", "decode_attn", "decode_attn_int8_witness",
-           "decode_attn_int8_witness_tv", "decode_attn_int8_dither", "decode_step", "decode_step_int8", "kv_truncate",
-           "swa_workspace_bytes", "swa_workspace_init", "swa_validate", "swa_status_string")
+           "decode_attn_int8_witness_tv", "decode_attn_int8_dither", "decode_step", "decode_step_int8",
+           "decode_step_int8_static", "kv_truncate", "swa_workspace_bytes", "swa_workspace_init", "swa_validate",
+           "swa_status_string")
 
 
 class SwaCacheDesc(ctypes.Structure):
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "decode_step": (ctypes.c_int, [P, VP, VP, VP, VP, VP, SZ, VP]),
             "decode_step_int8": (ctypes.c_int, [P, VP, VP, VP, VP, VP, VP, VP, ctypes.c_float, ctypes.c_float, VP,
                                                 SZ, VP]),
+            "decode_step_int8_static": (ctypes.c_int, [P, VP, VP, VP, VP, VP, VP, VP, ctypes.c_float,
+                                                       ctypes.c_float, VP]),
             "kv_truncate": (ctypes.c_int, [P, VP, VP, VP]),
             "swa_workspace_bytes": (SZ, [P]),
             "swa_workspace_init": (ctypes.c_int, [VP, SZ, VP]),

@@ -339,6 +339,34 @@ def decode_step_int8(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.T
     return out, cmax, tv, gate
 
 
+def decode_step_int8_static(cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, tau: float = 0.2,
+                            delta: float = 1e-6, out: Optional[torch.Tensor] = None,
+                            cmax: Optional[torch.Tensor] = None, tv: Optional[torch.Tensor] = None,
+                            gate: Optional[torch.Tensor] = None, stream=None):
+    """``decode_step_int8_static``: ``decode_step_int8`` with the split partials in the
+    library's static device scratch (no workspace).  The caller passes every output
+    tensor it wants written (``out`` and ``cmax`` are allocated here if not given, so a
+    caller that must not allocate passes them).  Returns (out, cmax, tv, gate)."""
+    shape = (cache.B, cache.H, 1, cache.D)
+    _need(k_new, shape, torch.bfloat16, "k_new")
+    _need(v_new, shape, torch.bfloat16, "v_new")
+    _need(q, (cache.B, cache.H, cache.D), torch.bfloat16, "q")
+    dev = q.device
+    BH = (cache.B, cache.H)
+    out = torch.empty((cache.B, cache.H, cache.D), dtype=torch.float32, device=dev) if out is None else out
+    cmax = torch.empty(BH, dtype=torch.float32, device=dev) if cmax is None else cmax
+    _need(out, (cache.B, cache.H, cache.D), torch.float32, "out")
+    _need(cmax, BH, torch.float32, "cmax")
+    if tv is not None:
+        _need(tv, BH, torch.float32, "tv")
+    if gate is not None:
+        _need(gate, BH, torch.int32, "gate")
+    check(lib().decode_step_int8_static(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                        _ptr(cmax), _ptr(tv), _ptr(gate), float(tau), float(delta),
+                                        _stream(stream)), "decode_step_int8_static")
+    return out, cmax, tv, gate
+
+
 def kv_truncate(cache, cut: torch.Tensor, stream=None) -> torch.Tensor:
     """``kv_truncate``: returns ok [B] int32 (1 truncated, 0 must recompute)."""
     _need(cut, (cache.B,), torch.int32, "cut")

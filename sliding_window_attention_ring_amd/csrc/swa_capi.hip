@@ -3,6 +3,8 @@
 // maintenance kernels (reset, workspace fill, position-invariant check).
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "swa_device.h"
 #include "swa_launch.h"
 
@@ -193,6 +195,40 @@ hipError_t launch_validate(const swa_cache& c, int32_t* violations, hipStream_t 
 
 using namespace swa;
 
+namespace {
+
+// Scratch of decode_step_int8_static: the split partials of a step live in
+// this file-scope device array instead of a caller's workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never passes the array's name to a kernel (in host code the name is a
+// host-side stand-in, not a device address): the device address is looked
+// up once per device with hipGetSymbolAddress, with that device current, and
+// that pointer is what the kernels get.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (SWA_OK), or SWA_EHIP /
+// SWA_EUNSUPPORTED when it cannot be found.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SWA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SWA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SWA_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return SWA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* swa_status_string(int status) {
@@ -330,6 +366,20 @@ int decode_step_int8(const swa_cache* c, const void* k_new, const void* v_new, c
                                  c->kind == SWA_KV_INT8_DITHER ? delta : 1.0f, ws, p, (hipStream_t)stream) == hipSuccess
              ? SWA_OK
              : SWA_EHIP;
+}
+
+int decode_step_int8_static(const swa_cache* c, const void* k_new, const void* v_new, const void* q, float* out,
+                            float* cmax, float* tv, int32_t* gate, float tau, float delta, void* stream) {
+  // The checks of decode_step_int8, then the partials' size against the
+  // static scratch; nothing is allocated.
+  const int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  const size_t need = swa_workspace_bytes(c);
+  if (need > kScratchBytes) return SWA_EWORKSPACE;
+  void* ws = nullptr;
+  const int sst = current_scratch(&ws);
+  if (sst != SWA_OK) return sst;
+  return decode_step_int8(c, k_new, v_new, q, out, cmax, tv, gate, tau, delta, ws, kScratchBytes, stream);
 }
 
 int kv_truncate(const swa_cache* c, const int32_t* cut, int32_t* ok, void* stream) {
