@@ -127,27 +127,26 @@ def cpu_baseline(wl, k_all, v_all, q, ns, budget_s: float = 12.0, threads: int =
     from oracle import attention, bits, dither as odither, int8 as oint8
     from workloads import gen
 
+    # A seeded sample of (b, h) pairs, as many as fit in 2 GiB of float64
+    # inputs (at most 256), widened once outside the timed oracle calls; the
+    # calls then cycle over the sample until the time budget is spent.
     rng = np.random.default_rng(2026)
-    pairs = [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(256)]
+    pair_bytes = 2 * min(wl.W, max(int(n) for n in ns)) * wl.D * 8
+    n_pairs = max(1, min(256, (2 << 30) // pair_bytes))
+    pairs = [(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(n_pairs)]
     qb = gen.to_bits(q)
     one = replace(wl, B=1)
-    done, t_used, nbytes, kv = 0, 0.0, 0.0, 0
-    # Inputs of the sampled pairs, widened to float64 once (outside the timed
-    # oracle call) and kept while they fit in 2 GiB, so that a workload whose
-    # pairs take well under the budget cycles over the sample again.
-    held, held_bytes = {}, 0
+    held = {}
+    for b, h in pairs:
+        if (b, h) not in held:
+            n = int(ns[b])
+            held[(b, h)] = (bits.to_f64(gen.to_bits(k_all[b, h, :n])), bits.to_f64(gen.to_bits(v_all[b, h, :n])))
+    done, t_used, nbytes, kv, t_log = 0, 0.0, 0.0, 0, time.time()
     with threadpool_limits(limits=threads):
         for i in range(256 * 1000):
             b, h = pairs[i % len(pairs)]
             n = int(ns[b])
-            if (b, h) in held:
-                kk, vv = held[(b, h)]
-            else:
-                kk = bits.to_f64(gen.to_bits(k_all[b, h, :n]))
-                vv = bits.to_f64(gen.to_bits(v_all[b, h, :n]))
-                if held_bytes + kk.nbytes + vv.nbytes <= 2 << 30:
-                    held[(b, h)] = (kk, vv)
-                    held_bytes += kk.nbytes + vv.nbytes
+            kk, vv = held[(b, h)]
             qq = bits.to_f64(qb[b, h])
             t0 = time.perf_counter()
             if wl.kind == "int8":
@@ -160,6 +159,9 @@ def cpu_baseline(wl, k_all, v_all, q, ns, budget_s: float = 12.0, threads: int =
             done += 1
             nbytes += step_bytes(one, n)[0] / wl.H
             kv += min(wl.W, n)
+            if time.time() - t_log > 10:
+                log(f"[bench] oracle: {done} calls, {t_used:.1f} s")
+                t_log = time.time()
             if t_used >= budget_s:
                 break
     lo, hi = min(min(wl.W, int(n)) for n in ns), max(min(wl.W, int(n)) for n in ns)
@@ -169,7 +171,7 @@ def cpu_baseline(wl, k_all, v_all, q, ns, budget_s: float = 12.0, threads: int =
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} oracle calls on {min(done, len(pairs))} sampled (b,h) pairs of {wl.name} at {ctx}, "
+        "sample": f"{done} oracle calls on {min(done, len(held))} sampled (b,h) pairs of {wl.name} at {ctx}, "
                   f"float64 NumPy, {threads} thread(s) of "
                   f"{len(os.sched_getaffinity(0))} affinity cores ({cpu_model()}), {t_used:.1f} s "
                   f"({kv / t_used:.3g} KV-token-heads/s)",
