@@ -11,6 +11,12 @@ decode call instead.  The default workload is the INT8 cache with the
 witness bound at 32768 context (B=16, H=32, D=128), prefilled with 32768
 rotary keys.
 
+A workload whose step reads under 2 GiB (the ring of 4096, the ragged
+batch, the one-GPU shard shapes, the tiny window) would find part of its
+bytes in the 256 MB MALL left by the step before; its calls rotate over 3-8
+identical instances of the cache instead, so each step reads its K/V from
+HBM and one pair of events still spans all timed calls.
+
 Prints ONE JSON line on stdout.  ``value`` is the whole step's algorithmic
 HBM bytes per second (GB/s); ``roofline`` reports the timed call alone,
 timed with HIP events on its launch stream; ``cpu_baseline`` times the CPU
@@ -18,7 +24,7 @@ oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 20]
        [--workload NAME] [--no-cpu-baseline] [--no-fuse]
-       [--flush auto|on|off] [--calibrate-copy]
+       [--rotate auto|on|off] [--calibrate-copy]
 """
 
 from __future__ import annotations
@@ -196,9 +202,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fuse", action="store_true",
                     help="time kv_append + the decode call instead of the one decode_step / decode_step_int8 call")
-    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
-                    help="read a 512 MiB scratch buffer before each timed step so no K/V bytes are served from "
-                         "the 256 MB MALL or L2; auto = on when a step reads under 2 GiB")
+    ap.add_argument("--rotate", choices=("auto", "on", "off"), default="auto",
+                    help="rotate the calls over 3-8 instances of the cache, so that no K/V bytes of a step are "
+                         "served from the 256 MB MALL or L2; auto = on when a step reads under 2 GiB")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -220,39 +226,43 @@ def main():
     torch.cuda.set_device(dev)
     n_steps = args.warmup + args.steps
     prefill = wl.prefill or wl.W
-    total = prefill + n_steps
     lens = gen.ragged_lengths(wl) if wl.ragged else None  # per-sequence prefill lengths
+    # Cold steps: a step that reads under 2 GiB would find part of its K/V
+    # bytes in the 256 MB MALL (and L2) left by the step before.  The calls
+    # then rotate over several instances of the cache, so that between two
+    # steps on one instance the others read at least 2 GiB; no flush kernel
+    # and no per-call event marker enters the timed region.
+    est = step_bytes(wl, prefill + 1 if lens is None else [int(n) + 1 for n in lens])[0]
+    cold = args.rotate == "on" or (args.rotate == "auto" and est < 2 * (1 << 30))
+    n_inst = min(8, max(3, -(-(2 << 30) // int(est)) + 1)) if cold else 1
+    per_inst = -(-n_steps // n_inst)  # steps each instance takes
+    total = prefill + per_inst
     log(f"[bench] workload {wl.name}: B={wl.B} H={wl.H} D={wl.D} W={wl.W} prefill={prefill} "
-        f"steps={args.steps} warmup={args.warmup}")
+        f"steps={args.steps} warmup={args.warmup} cache instances={n_inst}")
 
     t0 = time.time()
     k_all = gen.tokens(wl, "k", total, device=dev)
     v_all = gen.tokens(wl, "v", total, device=dev)
-    cache = swa.KVCache(wl.kind, wl.B, wl.H, wl.D, wl.W, device=dev, layout=wl.layout)
-    if lens is not None:
-        for b, n in enumerate(lens):
-            swa.kv_append(cache.seq_view(b), k_all[b:b + 1, :, :n].contiguous(), v_all[b:b + 1, :, :n].contiguous())
-    else:
-        chunk = wl.prefill_chunk or prefill
-        for c0 in range(0, prefill, chunk):
-            c1 = min(prefill, c0 + chunk)
-            swa.kv_append(cache, k_all[:, :, c0:c1].contiguous(), v_all[:, :, c0:c1].contiguous())
+    caches = []
+    for _ in range(n_inst):
+        cache = swa.KVCache(wl.kind, wl.B, wl.H, wl.D, wl.W, device=dev, layout=wl.layout)
+        if lens is not None:
+            for b, n in enumerate(lens):
+                swa.kv_append(cache.seq_view(b), k_all[b:b + 1, :, :n].contiguous(),
+                              v_all[b:b + 1, :, :n].contiguous())
+        else:
+            chunk = wl.prefill_chunk or prefill
+            for c0 in range(0, prefill, chunk):
+                c1 = min(prefill, c0 + chunk)
+                swa.kv_append(cache, k_all[:, :, c0:c1].contiguous(), v_all[:, :, c0:c1].contiguous())
+        caches.append((cache, cache.workspace()))
     ks = [k_all[:, :, p:p + 1].contiguous() for p in range(prefill, total)]
     vs = [v_all[:, :, p:p + 1].contiguous() for p in range(prefill, total)]
     qs = [gen.query(wl, p, device=dev) for p in range(prefill, total)]
-    ws = cache.workspace()
     out = torch.empty((wl.B, wl.H, wl.D), dtype=torch.float32, device=dev)
     cmax = torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev)
     tv = torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev)
     gate = torch.empty((wl.B, wl.H), dtype=torch.int32, device=dev)
-
-    def decode(q):
-        if wl.kind == "int8":
-            swa.decode_attn_int8_witness(cache, q, out=out, cmax=cmax, ws=ws)
-        elif wl.kind == "int8_dither":
-            swa.decode_attn_int8_dither(cache, q, delta=DITHER_DELTA, out=out, cert=cmax, tv=tv, gate=gate, ws=ws)
-        else:
-            swa.decode_attn(cache, q, out=out, ws=ws)
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t0:.1f} s")
 
@@ -264,81 +274,79 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # Call c goes to instance c mod n_inst, as that instance's step c div n_inst.
     # One call per step: kv_append of the token and the decode, fused into
     # one launch (plus the merge launch when a (b, h) has several splits).
     fuse = not args.no_fuse
     dither = wl.kind == "int8_dither"
 
-    def fused(i):
+    def decode(cache, ws, q):
+        if wl.kind == "int8":
+            swa.decode_attn_int8_witness(cache, q, out=out, cmax=cmax, ws=ws)
+        elif wl.kind == "int8_dither":
+            swa.decode_attn_int8_dither(cache, q, delta=DITHER_DELTA, out=out, cert=cmax, tv=tv, gate=gate, ws=ws)
+        else:
+            swa.decode_attn(cache, q, out=out, ws=ws)
+
+    def fused(c):
+        cache, ws = caches[c % n_inst]
+        i = c // n_inst
         if wl.kind in ("int8", "int8_dither"):
             swa.decode_step_int8(cache, ks[i], vs[i], qs[i], tau=0.2, delta=DITHER_DELTA, out=out, cmax=cmax,
                                  tv=tv if dither else None, gate=gate if dither else None, ws=ws)
         else:
             swa.decode_step(cache, ks[i], vs[i], qs[i], out=out, ws=ws)
 
-    def step(i):
-        if fuse:
-            fused(i)
-        else:
-            swa.kv_append(cache, ks[i], vs[i])
-            decode(qs[i])
+    def append(c):
+        cache, _ = caches[c % n_inst]
+        swa.kv_append(cache, ks[c // n_inst], vs[c // n_inst])
 
-    for i in range(args.warmup):
-        step(i)
+    for c in range(args.warmup):
+        if fuse:
+            fused(c)
+        else:
+            append(c)
+            decode(*caches[c % n_inst], qs[c // n_inst])
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    # per step: start (flushed runs only), after append, after decode
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     dec_bytes = app_bytes = vis_tokens = 0.0
-    for i in range(args.steps):
-        done = args.warmup + i + 1
+    positions = []
+    for c in range(args.warmup, n_steps):
+        done = c // n_inst + 1  # the instance's steps after this call
+        positions.append(prefill + done - 1)
         d, a, vis = step_bytes(wl, prefill + done if lens is None else [int(n) + done for n in lens])
         dec_bytes, app_bytes, vis_tokens = dec_bytes + d, app_bytes + a, vis_tokens + vis
-    flush = args.flush == "on" or (args.flush == "auto" and dec_bytes / args.steps < 2 * (1 << 30))
-    # A read, not a write: a written buffer leaves dirty lines whose write-back would
-    # compete with the timed step (measured: 3-20% slower steps, most for the smallest).
-    scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev) if flush else None
-    sink = torch.zeros((), dtype=torch.float32, device=dev) if flush else None
-    # Per-call event pairs only where the timed call must be told apart from
-    # other work in the stream (the flush, or the append of --no-fuse): each
-    # event marker costs the stream about 4 us.  Otherwise one pair of events
-    # spans the K calls, and a call's time is their average, launch gaps
-    # included.
-    per_call = flush or not fuse
+    # An event pair around each decode call only where the timed call must be
+    # told apart from other work in the stream (the append of --no-fuse):
+    # each event marker costs the stream about 4 us.  Otherwise one pair of
+    # events spans the K calls, and a call's time is their average, launch
+    # gaps included.
+    per_call = not fuse
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
     span = tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     if not per_call:
         span[0].record(stream)
-    for i in range(args.steps):
-        j = args.warmup + i
-        if flush:
-            sink.copy_(scratch.amax())
-            evs[i][0].record(stream)
+    for i, c in enumerate(range(args.warmup, n_steps)):
         if fuse:
-            if per_call:
-                evs[i][1].record(stream)
-            fused(j)
+            fused(c)
         else:
-            swa.kv_append(cache, ks[j], vs[j])
+            append(c)
+            evs[i][0].record(stream)
+            decode(*caches[c % n_inst], qs[c // n_inst])
             evs[i][1].record(stream)
-            decode(qs[j])
-        if per_call:
-            evs[i][2].record(stream)
     if not per_call:
         span[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     if per_call:
-        dec_ms = sorted(e1.elapsed_time(e2) for _, e1, e2 in evs)
+        dec_ms = sorted(e1.elapsed_time(e2) for e1, e2 in evs)
         kern_ms = sum(dec_ms) / args.steps
         kern_median = dec_ms[args.steps // 2] if args.steps % 2 else 0.5 * (dec_ms[args.steps // 2 - 1] + dec_ms[args.steps // 2])
     else:
         kern_ms = kern_median = span[0].elapsed_time(span[1]) / args.steps
-    if flush:
-        # the flush is not part of the step: time the steps by their events
-        elapsed = sum(e0.elapsed_time(e2) for e0, _, e2 in evs) * 1e-3
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = (dec_bytes + app_bytes) / elapsed / 1e9
@@ -361,8 +369,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "head_dim": wl.D, "window": wl.W,
                    "context": min(wl.W, prefill) if lens is None else [int(n) for n in lens],
-                   "kv_dtype": wl.kind, "layout": wl.layout, "cache_flush": flush,
-                   "positions": [prefill + args.warmup, prefill + n_steps - 1],
+                   "kv_dtype": wl.kind, "layout": wl.layout, "cache_instances": n_inst,
+                   "positions": [min(positions), max(positions)],
                    "step": ("decode_step (kv_append of one token + decode_attn, one call)" if wl.kind in ("bf16", "fp32")
                             else "decode_step_int8 (kv_append of one token + the decode, one call; "
                             + ("cert, tv, gate, delta=%g)" % DITHER_DELTA if dither else "witness bound)")) if fuse
@@ -384,7 +392,7 @@ def main():
                        "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel"),
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_median": round(kern_median, 4),
-            "timing": ("HIP event pair around each timed call on its stream" if per_call else
+            "timing": ("HIP event pair around each timed decode call on its stream" if per_call else
                        "HIP event pair around the K timed calls on their stream (average per call, launch gaps "
                        "included)"),
             "algorithmic_bytes_per_launch": timed_bytes / args.steps,
