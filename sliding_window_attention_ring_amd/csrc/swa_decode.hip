@@ -118,11 +118,17 @@ inline dim3 row_grid(const swa_cache& c, int nsplit) {
 // by the fused step kernel; n is next_position[b] as this decode sees it.
 // FINAL: the host plan has one split per (b, h), so the work-group writes
 // the output itself (zeros for an empty sequence) and no merge kernel runs.
+// INMERGE (fused step, several splits): the splits of a (b, h) publish
+// their partials with device-coherent stores and count themselves on
+// pair_cnt (zero between launches); the last to arrive merges them, so no
+// merge kernel runs either.  Each wave waits for its partial stores to
+// complete before the count, and the merge reads them with device-coherent
+// loads, so no L2 write-back or invalidation is needed.
 // No restrict qualifiers: the fused step writes a row of K and V first.
-template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
+template <typename T, int D, int NW, int U, bool PAGED, bool FINAL, bool INMERGE = false>
 __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint4* V, const int32_t* table,
                                                int64_t num_pages, const uint4* q, float* out, float* part, int H,
-                                               int W, int chunk, int nsplit_max) {
+                                               int W, int chunk, int nsplit_max, int32_t* pair_cnt = nullptr) {
   using F = RowFmt<T>;
   constexpr int EPV = F::kEpv;
   constexpr int VPR = D / EPV;          // 16-byte vectors per row
@@ -139,6 +145,7 @@ __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint
 
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
+  __shared__ int sm_last;
 
   const int split = blockIdx.x, h = row_grid_head<PAGED>(), b = row_grid_seq<PAGED>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -297,10 +304,29 @@ __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint
     return;
   }
 
-  // Publish this split's partial for the merge kernel.
   float* my = part + (bh * nsplit_max + split) * PF;
-  if (t < D) my[4 + t] = A;
-  if (t == 0) { my[0] = M; my[1] = L; }
+  if constexpr (INMERGE) {
+    // Publish this split's partial; the last split of the (b, h) to arrive merges.
+    if (t < D) store_coherent(my + 4 + t, A);
+    if (t == 0) { store_coherent(my, M); store_coherent(my + 1, L); }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+    __syncthreads();
+    if (t == 0) {
+      const int last = atomicAdd(pair_cnt, 1) == nsplit - 1;
+      if (last) atomicExch(pair_cnt, 0);
+      sm_last = last;
+    }
+    __syncthreads();
+    if (sm_last && t < D) {
+      float M2, L2, A2;
+      merge_partials<PF, false, true>(part + bh * nsplit_max * PF, nsplit, t, M2, L2, A2);
+      out[bh * D + t] = A2 / L2;
+    }
+  } else {
+    // Publish this split's partial for the merge kernel.
+    if (t < D) my[4 + t] = A;
+    if (t == 0) { my[0] = M; my[1] = L; }
+  }
 }
 
 template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
@@ -313,7 +339,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 }
 
 // Fused decode step (one token per sequence) for row caches: grid (split,
-// h, b) as the decode's.  The work-group of the split whose slots hold slot
+// h, b) as the decode's.  INMERGE (several splits per (b, h), H <= 63): the
+// splits of a (b, h) merge in this launch, counted on int [b][1 + h] of the
+// cache's step_sync line of sequence b (int [b][0] counts the sequence's
+// work-groups).  The work-group of the split whose slots hold slot
 // next_position mod W writes its token's key and value rows there (and, for
 // h == 0, the slot's position); after a barrier every work-group decodes its
 // split with next_position + 1.  The rows are read only by the work-group
@@ -321,7 +350,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 // of sequence b to finish, elected by the sequence's counter in the cache's
 // step_sync, as in the INT8 step kernel.  A negative next_position (a
 // violated precondition) appends nothing and advances nothing.
-template <typename T, int D, int NW, int U, bool PAGED, bool FINAL>
+template <typename T, int D, int NW, int U, bool PAGED, bool FINAL, bool INMERGE>
 __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
     uint4* K, uint4* V, int32_t* np, int32_t* pos, int32_t* cnt, RowMap map, const uint4* k_new,
     const uint4* v_new, int64_t num_pages, const uint4* q, float* out, float* part, int H, int W, int chunk,
@@ -342,8 +371,9 @@ __global__ __launch_bounds__(NW * 64) void decode_step_rows_kernel(
     }
   }
   __syncthreads();
-  decode_rows_wg<T, D, NW, U, PAGED, FINAL>(n0 >= 0 ? n0 + 1 : n0, K, V, map.table, num_pages, q, out, part, H, W,
-                                            chunk, nsplit_max);
+  decode_rows_wg<T, D, NW, U, PAGED, FINAL, INMERGE>(n0 >= 0 ? n0 + 1 : n0, K, V, map.table, num_pages, q, out, part,
+                                                     H, W, chunk, nsplit_max,
+                                                     INMERGE ? cnt + (int64_t)b * kCounterStride + 1 + h : nullptr);
   if (threadIdx.x == 0 && n0 >= 0) {
     int32_t* c = cnt + (int64_t)b * kCounterStride;
     if (atomicAdd(c, 1) == H * (int)gridDim.x - 1) {
@@ -416,24 +446,31 @@ hipError_t launch_step_one(const swa_cache& c, const void* k_new, const void* v_
   constexpr int NW = SWA_ROW_NW, U = SWA_ROW_U;
   const bool paged = c.layout == SWA_LAYOUT_PAGED;
   const bool final_pass = plan.nsplit_max == 1;
+  // Several splits per (b, h): merged in the step kernel when each head has
+  // a counter in its sequence's step_sync line, else by the merge kernel.
+  const bool inmerge = !final_pass && c.H <= kCounterStride - 1;
   const size_t lds = paged ? ((size_t)plan.unit_per_split / 16 + 2) * sizeof(int32_t) : 0;
   const dim3 grid = row_grid(c, plan.nsplit_max), block(NW * 64);
   float* part = reinterpret_cast<float*>(ws);
   int32_t* cnt = c.step_sync;
-#define SWA_ROW_STEP(P, F)                                                                                        \
-  hipLaunchKernelGGL((decode_step_rows_kernel<T, D, NW, U, P, F>), grid, block, lds, s,                           \
+#define SWA_ROW_STEP(P, F, M)                                                                                     \
+  hipLaunchKernelGGL((decode_step_rows_kernel<T, D, NW, U, P, F, M>), grid, block, lds, s,                        \
                      reinterpret_cast<uint4*>(c.k), reinterpret_cast<uint4*>(c.v), c.next_position, c.pos, cnt,    \
                      row_map(c), reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),    \
                      paged ? c.num_pages : 0, reinterpret_cast<const uint4*>(q), out, part, c.H, c.W,               \
                      plan.unit_per_split, plan.nsplit_max)
   if (paged) {
-    if (final_pass) SWA_ROW_STEP(true, true); else SWA_ROW_STEP(true, false);
+    if (final_pass) SWA_ROW_STEP(true, true, false);
+    else if (inmerge) SWA_ROW_STEP(true, false, true);
+    else SWA_ROW_STEP(true, false, false);
   } else {
-    if (final_pass) SWA_ROW_STEP(false, true); else SWA_ROW_STEP(false, false);
+    if (final_pass) SWA_ROW_STEP(false, true, false);
+    else if (inmerge) SWA_ROW_STEP(false, false, true);
+    else SWA_ROW_STEP(false, false, false);
   }
 #undef SWA_ROW_STEP
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || final_pass) return e;
+  if (e != hipSuccess || final_pass || inmerge) return e;
   return launch_merge<D>(c, out, part, plan, s);
 }
 

@@ -163,6 +163,17 @@ struct RowMap {
   }
 };
 
+// A partial published inside one launch for a work-group on another XCD:
+// device-scope (agent) atomic stores and loads, which are served where the
+// device is coherent, past the XCD-local L2 caches (no L2 write-back or
+// invalidation, which a release/acquire fence would cost for the whole L2).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Log-sum-exp merge of split partials laid out as [nsplit][PF] floats with
 // m at 0, l at 1 and acc at 4.. (base-2 scores): M = max m_s, L = sum
 // 2^(m_s-M) l_s, A = sum 2^(m_s-M) acc_s[t]; with CMAX also CM = max of the
@@ -170,9 +181,13 @@ struct RowMap {
 // short last group re-reads its last split, masked out of the sums, so
 // every load is unconditional and the waits stay exact), then folded in
 // with a running maximum.  Up to eight splits cost one memory round trip.
-template <int PF, bool CMAX = false>
+// COHERENT: the partials were written in the same launch by other
+// work-groups (store_coherent), so they are read with load_coherent; the
+// arithmetic is the same either way, and so are the results.
+template <int PF, bool CMAX = false, bool COHERENT = false>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int nsplit, int t, float& M,
                                                float& L, float& A, float* CM = nullptr) {
+  auto ld = [](const float* p) { return COHERENT ? load_coherent(p) : *p; };
   M = -1e30f;
   L = 0.f;
   A = 0.f;
@@ -183,10 +198,10 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ pp, int
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float* pi = pp + (sp + (i < n ? i : n - 1)) * PF;
-      m8[i] = pi[0];
-      l8[i] = pi[1];
-      a8[i] = pi[4 + t];
-      if constexpr (CMAX) c8[i] = pi[2];
+      m8[i] = ld(pi);
+      l8[i] = ld(pi + 1);
+      a8[i] = ld(pi + 4 + t);
+      if constexpr (CMAX) c8[i] = ld(pi + 2);
     }
     float mc = M;
 #pragma unroll
