@@ -278,7 +278,8 @@ int decode_step_int8(const swa_cache *c, const void *k_new, const void *v_new, c
  * decode_step_int8, without ws and ws_bytes: the split partials live in a
  * static device array of the library, 16 MiB per GPU, held until the
  * process ends.  Its device address is looked up on the first call on each
- * device.  The call allocates nothing and needs nothing cleared: the merge
+ * device (make that first call outside graph capture; later calls can be
+ * captured).  The call allocates nothing and needs nothing cleared: the merge
  * reads only partials written in the same call.  All calls on one GPU share
  * that GPU's array, so calls that overlap on one GPU (on different streams,
  * or from several threads without ordering) race and give wrong results;

@@ -21,18 +21,24 @@ def _gpu():
     require_gpu()
 
 
-@pytest.mark.parametrize("kind,layout,W,seed", [("bf16", "ring", 48, 1), ("bf16", "paged", 64, 2),
-                                                ("int8", "ring", 64, 3), ("int8", "paged", 48, 4),
-                                                ("int8_dither", "ring", 48, 5), ("int8_dither", "paged", 64, 6),
-                                                # several splits per (b, h) in the decode plans
-                                                ("bf16", "paged", 1024, 7), ("int8", "ring", 1024, 8),
-                                                ("int8_dither", "paged", 1024, 9), ("bf16", "ring", 2048, 10),
-                                                ("int8", "paged", 2048, 11), ("int8_dither", "ring", 1024, 12)])
-def test_mixed_operation_fuzz(kind, layout, W, seed):
+@pytest.mark.parametrize("kind,layout,W,seed,D", [("bf16", "ring", 48, 1, 128), ("bf16", "paged", 64, 2, 128),
+                                                  ("int8", "ring", 64, 3, 128), ("int8", "paged", 48, 4, 128),
+                                                  ("int8_dither", "ring", 48, 5, 128),
+                                                  ("int8_dither", "paged", 64, 6, 128),
+                                                  # several splits per (b, h) in the decode plans
+                                                  ("bf16", "paged", 1024, 7, 128), ("int8", "ring", 1024, 8, 128),
+                                                  ("int8_dither", "paged", 1024, 9, 128),
+                                                  ("bf16", "ring", 2048, 10, 128), ("int8", "paged", 2048, 11, 128),
+                                                  ("int8_dither", "ring", 1024, 12, 128),
+                                                  # the other head dims of the row kinds (32 rows per wave load
+                                                  # over two pages at D = 16; 4 and 32 splits at D = 32 and 256)
+                                                  ("bf16", "paged", 96, 13, 16), ("bf16", "ring", 1024, 14, 32),
+                                                  ("bf16", "ring", 1024, 15, 256)])
+def test_mixed_operation_fuzz(kind, layout, W, seed, D):
     import sliding_window_attention_ring_amd as swa
     rng = np.random.default_rng(seed)
     g = torch.Generator().manual_seed(seed)
-    B, H, D = 3, 2, 128
+    B, H = 3, 2
     cache = swa.KVCache(kind, B, H, D, W, layout=layout)
     hist_k = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
     hist_v = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]

@@ -84,3 +84,59 @@ def test_oversized_shape_is_rejected_before_any_launch():
     assert lib().swa_workspace_bytes(ctypes.byref(d)) > 16 << 20
     a = ctypes.c_void_p(0xA0000)
     assert lib().decode_step_int8_static(ctypes.byref(d), a, a, a, a, a, None, None, 0.2, 0.1, None) == -5
+
+
+@pytest.mark.parametrize("kind", ["int8", "int8_dither"])
+def test_static_scratch_step_under_graph_capture(kind):
+    """The callers it is for: one decode_step_int8_static call captured in a
+    graph (after a first eager call on the device, which looks the scratch
+    address up) and replayed for 20 tokens, across block commits, equals the
+    eager decode_step_int8 on a twin after every replay, with eager work and
+    a synchronization between the replays."""
+    import sliding_window_attention_ring_amd as swa
+    B, H, W, n, steps = 2, 3, 1024, 1000, 20
+    g = torch.Generator(device="cuda").manual_seed(43)
+    k = torch.randn((B, H, n + steps + 1, 128), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, n + steps + 1, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qs = torch.randn((steps + 1, B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache(kind, B, H, 128, W)
+        for name in ("k", "v", "k_scale", "v_scale", "witness", "k_stage", "v_stage"):
+            if getattr(c, name) is not None:
+                getattr(c, name).zero_()
+        swa.kv_append(c, k[:, :, :n].contiguous(), v[:, :, :n].contiguous())
+        caches.append(c)
+    cg, ce = caches
+    sk = k[:, :, n:n + 1].contiguous()
+    sv = v[:, :, n:n + 1].contiguous()
+    sq = qs[0].clone()
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    cmax = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    tv = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    gate = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    args = dict(delta=1e-3, out=out, cmax=cmax, tv=tv, gate=gate)
+    swa.decode_step_int8_static(cg, sk, sv, sq, **args)   # first call on the device: eager
+    eo = swa.decode_step_int8(ce, sk, sv, sq, delta=1e-3, want_tv=True)
+    torch.cuda.synchronize()
+    for a, b in zip((out, cmax, tv, gate), eo):
+        assert torch.equal(a, b)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        swa.decode_step_int8_static(cg, sk, sv, sq, **args)
+    torch.cuda.synchronize()
+    assert host_bits(cg.next_position).tolist() == [n + 1] * B  # capture does not run the step
+    names = ["k", "v", "k_scale", "v_scale", "k_stage", "v_stage", "pos", "next_position"] + \
+        (["witness"] if kind == "int8" else [])
+    for i in range(1, steps + 1):
+        sk.copy_(k[:, :, n + i:n + i + 1])
+        sv.copy_(v[:, :, n + i:n + i + 1])
+        sq.copy_(qs[i])
+        graph.replay()
+        eo = swa.decode_step_int8(ce, sk, sv, sq, delta=1e-3, want_tv=True)
+        torch.cuda.synchronize()
+        for a, b in zip((out, cmax, tv, gate), eo):
+            assert torch.equal(a, b), f"replay {i}"
+        for name in names:
+            assert torch.equal(getattr(cg, name), getattr(ce, name)), f"replay {i}: {name}"
+    assert host_bits(cg.next_position).tolist() == [n + steps + 1] * B
