@@ -147,7 +147,7 @@ int swa_cache_reset(const swa_cache *c, void *stream);
  * pseudo-random dither is added before rounding at write time and subtracted
  * at read time; section SGLang 生产级落地: Philox keyed by request, layer,
  * KV head, token and channel): the same blocks and scales, and
- * code = rint(f32(x/s) + u) with u = (m + 1/2)/256 - 1/2, where m is byte
+ * code = rint(f32(x/s) + u) with u = 1/2 - (m + 1/2)/256, where m is byte
  * c mod 16 of Philox-4x32-10 (Salmon et al., SC 2011) with key
  * (request_id mod 2^32, request_id div 2^32) and counter (position, c / 16,
  * head, layer); the words are taken in order, each little-endian.  Keys and

@@ -21,7 +21,7 @@ constexpr int kD8 = 128;
 // second tier; section SGLang 生产级落地 for the Philox five-tuple).  req ==
 // nullptr selects Tier A (plain rounding plus the witness).  Otherwise the
 // element of channel c of the token at position p in head h gets
-// u = (m + 1/2)/256 - 1/2, m = byte c mod 16 of Philox-4x32-10 with key
+// u = 1/2 - (m + 1/2)/256, m = byte c mod 16 of Philox-4x32-10 with key
 // (req[b] low word, high word) and counter (p, c / 16, h, layer), words in
 // order, least significant byte first; code = rint(f32(x / s) + u).  Since
 // |u| <= 1/2 - 2^-9 the sum stays inside +-127.5 and the clamp never acts.
@@ -83,7 +83,7 @@ __device__ __forceinline__ float commit_block_wave(int lane, bool key, const uin
     float c = 0.f;
     if (s > 0.f) {
       float y = __fdiv_rn(x[e], s);
-      if (dith) y = y + fmaf(u8f(dw[e >> 2], e & 3), 1.0f / 256.0f, -255.0f / 512.0f);  // u is exact
+      if (dith) y = y + fmaf(u8f(dw[e >> 2], e & 3), -1.0f / 256.0f, 255.0f / 512.0f);  // u is exact
       c = fminf(fmaxf(rintf(y), -127.f), 127.f);
     }
     cf[e] = c;

@@ -28,14 +28,14 @@
 // 128-byte row, rows g and g+8) and 8 B of witness (4 lanes per token).
 //
 // Tier B (DITHER; same page, section 频带酉性与双层证书, second tier): the
-// codes carry a subtractive dither u = (m + 1/2)/256 - 1/2 that is
+// codes carry a subtractive dither u = 1/2 - (m + 1/2)/256 that is
 // regenerated here from the Philox stream the write path used (key = the
 // request id, counter = (position, channel / 16, head, layer); section SGLang
 // 生产级落地 for the five-tuple).  A token is read as s * (code - u), with no
 // witness.  The lane that holds dims [16*(lane%8), +16) of rows g and g+8
 // needs exactly one Philox block per row, shared by the key and the value.
-// With t = 256 code + 255 - m, a signed 16-bit integer that one byte
-// permute builds from the code byte and the complemented dither byte (two
+// With t = 256 code + m, a signed 16-bit integer that one byte permute
+// builds from the code byte and the dither byte as Philox returns it (two
 // elements per permute), code - u = (t - 127.5)/256.  So the key dot is
 // (1/256) sum q t - (127.5/256) sum q, and the value sum gets (p s_V/256) t
 // per element, with -(127.5/256) times the running weight sum added once
@@ -104,13 +104,13 @@ struct KeyDot {
   }
 };
 
-// Tier B element values t = 256 code + 255 - m for the 4 codes of word cw,
-// given nm = ~m: bytes (~m0, c0, ~m1, c1) and (~m2, c2, ~m3, c3) as two
-// signed 16-bit halves each (a byte permute takes bytes 0-3 from its second
-// operand and 4-7 from its first).
-__device__ __forceinline__ void dither_t(uint32_t cw, uint32_t nm, float (&t)[4]) {
-  const uint32_t lo = __builtin_amdgcn_perm(cw, nm, 0x05010400u);
-  const uint32_t hi = __builtin_amdgcn_perm(cw, nm, 0x07030602u);
+// Tier B element values t = 256 code + m for the 4 codes of word cw and
+// the 4 dither bytes of word mw: bytes (m0, c0, m1, c1) and (m2, c2, m3, c3)
+// as two signed 16-bit halves each (a byte permute takes bytes 0-3 from its
+// second operand and 4-7 from its first).
+__device__ __forceinline__ void dither_t(uint32_t cw, uint32_t mw, float (&t)[4]) {
+  const uint32_t lo = __builtin_amdgcn_perm(cw, mw, 0x05010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(cw, mw, 0x07030602u);
   t[0] = s16lo(lo); t[1] = s16hi(lo);
   t[2] = s16lo(hi); t[3] = s16hi(hi);
 }
@@ -136,10 +136,10 @@ struct DitherKeyDot {
     }
     qc = sum * (-127.5f / 256.0f);
   }
-  // nm: the complemented dither bytes of the row
-  __device__ __forceinline__ float dot(const uint4 c, const uint4 nm) const {
+  // m: the dither bytes of the row
+  __device__ __forceinline__ float dot(const uint4 c, const uint4 m) const {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    const uint32_t mw[4] = {nm.x, nm.y, nm.z, nm.w};
+    const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
     float d = qc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -440,7 +440,7 @@ __device__ __forceinline__ void decode_int8_wg(
 
   auto step = [&](const Blk (&cur)[UB], int kb0) {
     float s[2 * UB], sv[UB];
-    uint4 dm[2 * UB];  // Tier B complemented dither bytes of rows g and g+8 of each block
+    uint4 dm[2 * UB];  // Tier B dither bytes of rows g and g+8 of each block
 #pragma unroll
     for (int ub = 0; ub < UB; ++ub) {
       const int kb = kb0 + ub;
@@ -461,7 +461,7 @@ __device__ __forceinline__ void decode_int8_wg(
         if constexpr (DITHER) {
           const uint4 r = philox4x32_10(make_uint4((uint32_t)(kbc * 16 + g + 8 * half), (uint32_t)vq,
                                                    (uint32_t)h, layer), rk0, rk1);
-          dm[2 * ub + half] = make_uint4(~r.x, ~r.y, ~r.z, ~r.w);
+          dm[2 * ub + half] = r;
           d = kd.dot(half ? cur[ub].k1 : cur[ub].k0, dm[2 * ub + half]);
           d = group_sum<8>(d) * sk;
         } else {

@@ -86,7 +86,7 @@ def test_dither_byte_order_from_known_answer():
         want += [(w >> (8 * i)) & 0xFF for i in range(4)]
     assert list(m) == want
     u = dither.dither_values(m)
-    assert np.all(np.abs(u) < 0.5) and np.all(((u + 0.5) * 256 - 0.5) == m)
+    assert np.all(np.abs(u) < 0.5) and np.all(((0.5 - u) * 256 - 0.5) == m)
 
 
 def test_tuple_fields_from_known_answer():
@@ -160,7 +160,7 @@ def test_ties_round_to_even():
     x = np.zeros(16, dtype=np.float32)
     x[0] = 127
     u = np.zeros(16)
-    m = 191                                                    # u = 1/4 - 1/512
+    m = 64                                                     # u = 1/4 - 1/512
     for j, y in enumerate([2.25 + 1 / 512, 3.25 + 1 / 512, -2.75 + 1 / 512, -5.75 + 1 / 512], start=1):
         x[j] = y
         u[j] = dither.dither_values(m)
@@ -239,7 +239,11 @@ def test_grid_law_is_strictly_sub_gaussian():
 
 def test_certificate_scale_matches_monte_carlo_spread():
     # One key row, many independent dither streams (requests): the logit
-    # error's spread fixes the bound's Gaussian part.
+    # error's spread fixes the bound's Gaussian part.  8000 draws estimate
+    # the spread to about 0.8% (relative standard error 1/sqrt(2N)), so the
+    # 2.5% tolerance holds the bound's scale factor, union-bound term
+    # included, to within about 3 standard errors; ln(n_q/delta) in place of
+    # ln(2 n_q/delta) would move it by 4.4%.
     rng = np.random.default_rng(11)
     d, n, delta = 128, 16, 0.01
     k = rng.standard_normal((n, d))
@@ -247,7 +251,7 @@ def test_certificate_scale_matches_monte_carlo_spread():
     v = np.zeros((n, d))
     q = rng.standard_normal(d)
     errs = []
-    for req in range(2000):
+    for req in range(8000):
         r = dither.int8_dither_decode(q, k, v, n, n, request=req, layer=0, head=0, delta=delta)
         errs.append((r["k_codes"][0].astype(np.float64) - dither.dither_values(r["m"][0])) * float(r["k_scales"][0])
                     - k[0])
@@ -257,7 +261,7 @@ def test_certificate_scale_matches_monte_carlo_spread():
     bias = s0 / np.sqrt(d) * np.sum(np.abs(q)) * dither.BETA
     c = float(dither.token_bound(q, np.array([s0]), 16, delta)[0])
     gauss = (c - bias) / np.sqrt(2 * np.log(2 * 16 / delta))
-    assert gauss / sigma == pytest.approx(1.0, abs=0.07)
+    assert gauss / sigma == pytest.approx(1.0, abs=0.025)
     assert abs(float(np.mean(e))) <= bias + 4 * sigma / np.sqrt(len(e))
 
 

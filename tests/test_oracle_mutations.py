@@ -108,8 +108,10 @@ MUTATIONS = [
      "ctr[i, g] = philox_counter(layer, head, int(p) + 1, g)"),
     ("oracle/dither.py", '.astype("<u4").view(np.uint8)', '.astype(">u4").view(np.uint8)'),
     ("oracle/dither.py", "return np.array([r & 0xFFFFFFFF, r >> 32]", "return np.array([r >> 32, r & 0xFFFFFFFF]"),
-    ("oracle/dither.py", "return (np.asarray(m, dtype=np.float64) + 0.5) / LEVELS - 0.5",
-     "return np.asarray(m, dtype=np.float64) / LEVELS - 0.5"),
+    ("oracle/dither.py", "return 0.5 - (np.asarray(m, dtype=np.float64) + 0.5) / LEVELS",
+     "return 0.5 - np.asarray(m, dtype=np.float64) / LEVELS"),
+    ("oracle/dither.py", "return 0.5 - (np.asarray(m, dtype=np.float64) + 0.5) / LEVELS",
+     "return (np.asarray(m, dtype=np.float64) + 0.5) / LEVELS - 0.5"),
     ("oracle/dither.py", "return np.clip(np.rint(t), -QMAX, QMAX)",
      "return np.clip(np.floor(t + np.float32(0.5)), -QMAX, QMAX)"),
     ("oracle/dither.py", "t = y + np.asarray(u, dtype=np.float32)", "t = y - np.asarray(u, dtype=np.float32)"),
