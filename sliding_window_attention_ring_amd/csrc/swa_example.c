@@ -9,9 +9,10 @@
  * A second part uses an INT8 cache with the witness bound, then one with
  * subtractive dither, stepping each with decode_step_int8 (append + decode
  * in one call) on one cache and with kv_append + the separate decode on a
- * twin: the two must agree bit for bit, and with identical keys and values
- * that are exact multiples of their block scale the output is the mean of
- * the value rows (within the dither's half step for the dithered kind).
+ * twin, and with decode_step_int8_static (no workspace) on a third: the
+ * three must agree bit for bit, and with identical keys and values that are
+ * exact multiples of their block scale the output is the mean of the value
+ * rows (within the dither's half step for the dithered kind).
  * Prints "swa_example ok" and returns 0 on success.
  */
 #include <hip/hip_runtime_api.h>
@@ -162,19 +163,21 @@ int main(void) {
   CHECK_HIP(hipMalloc(&dvt, (size_t)B * H * D8 * 2));
   uint16_t *kt = malloc((size_t)B * H * D8 * 2), *vt = malloc((size_t)B * H * D8 * 2);
   float *o0 = malloc((size_t)B * H * D8 * 4), *o1 = malloc((size_t)B * H * D8 * 4);
-  float cm0[64], cm1[64];
+  float *o2 = malloc((size_t)B * H * D8 * 4);
+  float cm0[64], cm1[64], cm2[64];
   uint64_t rid[2] = {0x0123456789abcdefull, 42u};  /* the dithered kind's request ids */
   uint64_t *drid;
   CHECK_HIP(hipMalloc((void **)&drid, sizeof rid));
   CHECK_HIP(hipMemcpy(drid, rid, sizeof rid, hipMemcpyHostToDevice));
-  int mism[2] = {0, 0};
+  int mism[2] = {0, 0}, mism_static[2] = {0, 0};
   double worst8[2] = {0.0, 0.0};
   for (int pass = 0; pass < 2; ++pass) {
     const int kind = pass == 0 ? SWA_KV_INT8 : SWA_KV_INT8_DITHER;
-    swa_cache c8[2];
-    void *ws8[2];
-    float *dout8[2], *dcm8[2];
-    for (int t = 0; t < 2; ++t) {
+    /* c8[0]: decode_step_int8; c8[1]: kv_append + the decode; c8[2]: decode_step_int8_static (no workspace) */
+    swa_cache c8[3];
+    void *ws8[3];
+    float *dout8[3], *dcm8[3];
+    for (int t = 0; t < 3; ++t) {
       swa_cache *x = &c8[t];
       memset(x, 0, sizeof *x);
       x->kind = kind; x->B = B; x->H = H; x->D = D8; x->W = W8; x->layout = SWA_LAYOUT_RING;
@@ -210,6 +213,7 @@ int main(void) {
       const float delta = kind == SWA_KV_INT8 ? 1.0f : 1e-3f;
       CHECK_SWA(decode_step_int8(&c8[0], dkt, dvt, dq8, dout8[0], dcm8[0], NULL, NULL, 0.2f, delta, ws8[0],
                                  swa_workspace_bytes(&c8[0]), NULL));
+      CHECK_SWA(decode_step_int8_static(&c8[2], dkt, dvt, dq8, dout8[2], dcm8[2], NULL, NULL, 0.2f, delta, NULL));
       CHECK_SWA(kv_append(&c8[1], dkt, dvt, 1, NULL));
       if (kind == SWA_KV_INT8)
         CHECK_SWA(decode_attn_int8_witness(&c8[1], dq8, dout8[1], dcm8[1], NULL, ws8[1],
@@ -221,7 +225,11 @@ int main(void) {
       CHECK_HIP(hipMemcpy(o1, dout8[1], (size_t)B * H * D8 * 4, hipMemcpyDeviceToHost));
       CHECK_HIP(hipMemcpy(cm0, dcm8[0], (size_t)B * H * 4, hipMemcpyDeviceToHost));
       CHECK_HIP(hipMemcpy(cm1, dcm8[1], (size_t)B * H * 4, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(o2, dout8[2], (size_t)B * H * D8 * 4, hipMemcpyDeviceToHost));
+      CHECK_HIP(hipMemcpy(cm2, dcm8[2], (size_t)B * H * 4, hipMemcpyDeviceToHost));
       if (memcmp(o0, o1, (size_t)B * H * D8 * 4) != 0 || memcmp(cm0, cm1, (size_t)B * H * 4) != 0) ++mism[pass];
+      if (memcmp(o0, o2, (size_t)B * H * D8 * 4) != 0 || memcmp(cm0, cm2, (size_t)B * H * 4) != 0)
+        ++mism_static[pass];
     }
     for (int bh = 0; bh < B * H; ++bh)
       for (int d = 0; d < D8; ++d) {
@@ -234,24 +242,26 @@ int main(void) {
     /* Witness kind: the values are exact multiples of their scale, so the output is the exact mean.  Dithered
      * kind: each value reads back s*(code - u), within s/2 = 1/32 of the input, and the keys read back within
      * 1/254 of 1, so the weights stay uniform to within a fraction of a percent. */
-    if (mism[pass] || worst8[pass] > (kind == SWA_KV_INT8 ? 2e-3 : 0.05)) ++failures;
+    if (mism[pass] || mism_static[pass] || worst8[pass] > (kind == SWA_KV_INT8 ? 2e-3 : 0.05)) ++failures;
     int32_t np8[2];
     CHECK_HIP(hipMemcpy(np8, c8[0].next_position, (size_t)B * 4, hipMemcpyDeviceToHost));
     if (np8[0] != T8 || np8[1] != T8) ++failures;
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 3; ++t) {
       hipFree(c8[t].k); hipFree(c8[t].v); hipFree(c8[t].k_scale); hipFree(c8[t].v_scale);
       if (c8[t].witness) hipFree(c8[t].witness);
       hipFree(c8[t].k_stage); hipFree(c8[t].v_stage); hipFree(c8[t].pos); hipFree(c8[t].next_position);
-      hipFree(ws8[t]); hipFree(dout8[t]); hipFree(dcm8[t]);
+      hipFree(c8[t].step_sync); hipFree(ws8[t]); hipFree(dout8[t]); hipFree(dcm8[t]);
     }
   }
 
   printf("swa_example %s: one-token rows exact, identical-key mean max err %.3g, violations %d; "
-         "int8 fused step == append+decode on %d steps (%d mismatches), exact-value mean max err %.3g; "
-         "dithered int8 fused step == append+decode (%d mismatches), mean max err %.3g\n",
-         failures ? "FAILED" : "ok", worst, viol, T8, mism[0], worst8[0], mism[1], worst8[1]);
+         "int8 fused step == append+decode on %d steps (%d mismatches; static-scratch step %d), exact-value mean "
+         "max err %.3g; dithered int8 fused step == append+decode (%d mismatches; static-scratch step %d), mean max "
+         "err %.3g\n",
+         failures ? "FAILED" : "ok", worst, viol, T8, mism[0], mism_static[0], worst8[0], mism[1], mism_static[1],
+         worst8[1]);
   hipFree(dq8); hipFree(dkt); hipFree(dvt); hipFree(drid);
-  free(k8); free(v8); free(kt); free(vt); free(o0); free(o1);
+  free(k8); free(v8); free(kt); free(vt); free(o0); free(o1); free(o2);
   hipFree(c.k); hipFree(c.v); hipFree(c.pos); hipFree(c.next_position);
   hipFree(dk); hipFree(dv); hipFree(dq); hipFree(dout); hipFree(dviol); hipFree(ws); hipFree(dk1); hipFree(dv1);
   free(hk); free(hv); free(hq); free(out); free(k1); free(v1);
