@@ -152,9 +152,10 @@ __device__ __forceinline__ void decode_rows_wg(int n, const uint4* K, const uint
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * H + h;
   const int len = n < W ? n : W;
-  if (len <= 0) {  // empty cache: zeros, written here or by the merge kernel
-    if constexpr (FINAL) {
-      for (int t = threadIdx.x; t < D; t += NW * 64) out[bh * D + t] = 0.f;
+  if (len <= 0) {  // empty cache: zeros, written here (split 0) or by the merge kernel
+    if constexpr (FINAL || INMERGE) {
+      if (split == 0)
+        for (int t = threadIdx.x; t < D; t += NW * 64) out[bh * D + t] = 0.f;
     }
     return;
   }

@@ -381,3 +381,48 @@ def test_one_workspace_shared_by_caches_of_different_shapes():
         assert torch.equal(cf.pos, cs.pos) and torch.equal(cf.k, cs.k)
         assert not cf.step_sync.any(), "every fused step leaves its counters zero"
         assert swa.validate(cf) == 0
+
+
+@pytest.mark.parametrize("kind,B,H,W", [("bf16", 2, 3, 1024), ("bf16", 16, 32, 64), ("int8", 2, 3, 1024),
+                                        ("int8_dither", 2, 3, 1024)])
+def test_fused_step_with_a_negative_next_position(kind, B, H, W):
+    """A violated precondition forced from the host: next_position of sequence
+    0 set to -5.  The fused step appends nothing to it, leaves its
+    next_position at -5 and writes zeros for its output (bf16 W=1024: splits
+    merged in the step kernel; bf16 W=64: one split; INT8: the merge kernel),
+    exactly as kv_append + the separate decode do on a twin; sequence 1
+    steps normally, and swa_validate reports the bad sequence."""
+    import sliding_window_attention_ring_amd as swa
+    g = torch.Generator(device="cuda").manual_seed(47)
+    n = W - 24
+    k = torch.randn((B, H, n + 1, 128), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, n + 1, 128), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        c = swa.KVCache(kind, B, H, 128, W)
+        for name in ("k", "v", "k_scale", "v_scale", "witness", "k_stage", "v_stage"):
+            if getattr(c, name, None) is not None:
+                getattr(c, name).zero_()
+        swa.kv_append(c, k[:, :, :n].contiguous(), v[:, :, :n].contiguous())
+        c.next_position[0] = -5
+        caches.append(c)
+    cf, cs = caches
+    kn, vn = k[:, :, n:n + 1].contiguous(), v[:, :, n:n + 1].contiguous()
+    if kind == "bf16":
+        got = (swa.decode_step(cf, kn, vn, q),)
+        swa.kv_append(cs, kn, vn)
+        ref = (swa.decode_attn(cs, q),)
+    else:
+        got = swa.decode_step_int8(cf, kn, vn, q, want_tv=True, delta=1e-3)
+        ref = separate(swa, cs, kn, vn, q, 0.2, 1e-3)
+    torch.cuda.synchronize()
+    for a, b_ in zip(got, ref):
+        assert torch.equal(a, b_)
+    assert not got[0][0].any(), "the sequence with the violated precondition gets zeros"
+    assert got[0][1].abs().sum() > 0
+    assert host_bits(cf.next_position).tolist() == [-5, n + 1] + [n + 1] * (B - 2)
+    for name in ("k", "v", "pos"):
+        assert torch.equal(getattr(cf, name), getattr(cs, name)), name
+    assert not cf.step_sync.any(), "every fused step leaves its counters zero"
+    assert swa.validate(cf) > 0
