@@ -227,6 +227,24 @@ int current_scratch(void** out) {
   return SWA_OK;
 }
 
+// Argument checks of the fused INT8 step, common to decode_step_int8 and
+// decode_step_int8_static (everything but the workspace).
+int check_step_int8(const swa_cache* c, const void* k_new, const void* v_new, const void* q, const float* out,
+                    const float* cmax, const float* tv, const int32_t* gate, float tau, float delta) {
+  const int st = check_cache(c);
+  if (st != SWA_OK) return st;
+  if (!is_int8(c->kind)) return SWA_EUNSUPPORTED;
+  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || cmax == nullptr ||
+      c->step_sync == nullptr)
+    return SWA_ENULL;
+  if (gate != nullptr && tv == nullptr) return SWA_ENULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out)) return SWA_EALIGN;
+  if (((uintptr_t)cmax & 3u) || ((uintptr_t)tv & 3u) || ((uintptr_t)gate & 3u)) return SWA_EALIGN;
+  if (!(tau == tau)) return SWA_EINVAL;
+  if (c->kind == SWA_KV_INT8_DITHER && !(delta > 0.f && delta <= 1.f)) return SWA_EINVAL;
+  return SWA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,18 +366,10 @@ int decode_step(const swa_cache* c, const void* k_new, const void* v_new, const 
 int decode_step_int8(const swa_cache* c, const void* k_new, const void* v_new, const void* q, float* out,
                      float* cmax, float* tv, int32_t* gate, float tau, float delta, void* ws, size_t ws_bytes,
                      void* stream) {
-  int st = check_cache(c);
+  int st = check_step_int8(c, k_new, v_new, q, out, cmax, tv, gate, tau, delta);
   if (st != SWA_OK) return st;
-  if (!is_int8(c->kind)) return SWA_EUNSUPPORTED;
-  if (k_new == nullptr || v_new == nullptr || q == nullptr || out == nullptr || cmax == nullptr || ws == nullptr ||
-      c->step_sync == nullptr)
-    return SWA_ENULL;
-  if (gate != nullptr && tv == nullptr) return SWA_ENULL;
-  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) || !aligned16(ws))
-    return SWA_EALIGN;
-  if (((uintptr_t)cmax & 3u) || ((uintptr_t)tv & 3u) || ((uintptr_t)gate & 3u)) return SWA_EALIGN;
-  if (!(tau == tau)) return SWA_EINVAL;
-  if (c->kind == SWA_KV_INT8_DITHER && !(delta > 0.f && delta <= 1.f)) return SWA_EINVAL;
+  if (ws == nullptr) return SWA_ENULL;
+  if (!aligned16(ws)) return SWA_EALIGN;
   if (ws_bytes < swa_workspace_bytes(c)) return SWA_EWORKSPACE;
   const SplitPlan p = plan_decode(*c);
   return launch_decode_step_int8(*c, k_new, v_new, q, out, cmax, tv, gate, tau,
@@ -370,12 +380,11 @@ int decode_step_int8(const swa_cache* c, const void* k_new, const void* v_new, c
 
 int decode_step_int8_static(const swa_cache* c, const void* k_new, const void* v_new, const void* q, float* out,
                             float* cmax, float* tv, int32_t* gate, float tau, float delta, void* stream) {
-  // The checks of decode_step_int8, then the partials' size against the
-  // static scratch; nothing is allocated.
-  const int st = check_cache(c);
+  // The argument checks of decode_step_int8, then the partials' size against
+  // the static scratch, before any HIP call; nothing is allocated.
+  const int st = check_step_int8(c, k_new, v_new, q, out, cmax, tv, gate, tau, delta);
   if (st != SWA_OK) return st;
-  const size_t need = swa_workspace_bytes(c);
-  if (need > kScratchBytes) return SWA_EWORKSPACE;
+  if (swa_workspace_bytes(c) > kScratchBytes) return SWA_EWORKSPACE;
   void* ws = nullptr;
   const int sst = current_scratch(&ws);
   if (sst != SWA_OK) return sst;

@@ -73,6 +73,8 @@ int main(void) {
       EXPECT(decode_step_int8(&c, A, A, A, F, F, NULL, NULL, 0.2f, 0.1f, ws, need - 1, NULL),
              i >= 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
       EXPECT(decode_step(&c, A, A, A, F, ws, need - 1, NULL), i < 2 ? SWA_EWORKSPACE : SWA_EUNSUPPORTED);
+      EXPECT(decode_step_int8_static(&c, NULL, A, A, F, F, NULL, NULL, 0.2f, 0.1f, NULL),
+             i >= 2 ? SWA_ENULL : SWA_EUNSUPPORTED); /* rejected before any HIP call */
       swa_cache ns = c;
       ns.step_sync = NULL; /* the fused steps need the completion counters */
       EXPECT(decode_step(&ns, A, A, A, F, ws, need, NULL), i < 2 ? SWA_ENULL : SWA_EUNSUPPORTED);

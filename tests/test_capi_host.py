@@ -165,3 +165,27 @@ def test_fused_steps_need_the_completion_counters():
     assert L.decode_step_int8(p(i8), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, ws, 1 << 30, None) == -2
     assert L.kv_append(p(d), None, A16, 1, None) == -2                   # the other calls do not need them
     assert L.kv_append(p(desc(step_sync=0xE0002)), None, A16, 1, None) == -3   # misaligned counters
+
+
+def test_static_scratch_step_checks_its_arguments_before_any_hip_call():
+    """decode_step_int8_static rejects bad arguments exactly as
+    decode_step_int8 does, and an oversized shape, before it touches HIP
+    (these calls run on a host without a GPU)."""
+    from sliding_window_attention_ring_amd._capi import lib
+    L = lib()
+    p = ctypes.byref
+    A16, ODD = ctypes.c_void_p(0xA0000), ctypes.c_void_p(0xA0004)
+    st = L.decode_step_int8_static
+    i8, dz = desc(kind=2), desc(kind=3, witness=None, request_id=0xD0000)
+    assert st(None, A16, A16, A16, A16, A16, None, None, 0.2, 0.1, None) == -2
+    assert st(p(desc()), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, None) == -4       # bf16 cache
+    assert st(p(i8), None, A16, A16, A16, A16, None, None, 0.2, 0.1, None) == -2
+    assert st(p(i8), A16, A16, A16, A16, None, None, None, 0.2, 0.1, None) == -2          # cmax NULL
+    assert st(p(desc(kind=2, step_sync=None)), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, None) == -2
+    assert st(p(i8), ODD, A16, A16, A16, A16, None, None, 0.2, 0.1, None) == -3
+    assert st(p(i8), A16, A16, A16, A16, A16, None, A16, 0.2, 0.1, None) == -2            # gate without tv
+    assert st(p(i8), A16, A16, A16, A16, A16, None, None, float("nan"), 0.1, None) == -1
+    assert st(p(dz), A16, A16, A16, A16, A16, None, None, 0.2, 0.0, None) == -1          # Tier B delta
+    big = desc(kind=2, B=65535, H=2, W=16)                                                # 69 MB of partials
+    assert L.swa_workspace_bytes(p(big)) > 16 << 20
+    assert st(p(big), A16, A16, A16, A16, A16, None, None, 0.2, 0.1, None) == -5
