@@ -156,13 +156,17 @@ def test_fused_step_headline_shape_and_graph():
                                                  ("fp32", 1, 2, 16, 4, "ring"), ("bf16", 1, 2, 64, 4096, "ring"),
                                                  ("bf16", 1, 2, 64, 4096, "paged"), ("fp32", 2, 3, 32, 1024, "ring"),
                                                  ("bf16", 2, 3, 16, 2048, "paged"), ("bf16", 3, 2, 32, 96, "ring"),
-                                                 ("fp32", 2, 2, 256, 512, "ring")])
+                                                 ("fp32", 2, 2, 256, 512, "ring"),
+                                                 # 64 heads: too many for the in-kernel merge's counters,
+                                                 # so the several splits go through the merge kernel
+                                                 ("bf16", 1, 64, 128, 4096, "ring")])
 def test_fused_row_step_equals_append_then_decode(kind, B, H, D, W, layout):
     """decode_step (bf16 / fp32 kinds) against kv_append + decode_attn on twin
     caches, bit for bit in the output and the ring state, over 3W ragged
-    steps (at most 40 for long windows); the last three shapes have several
-    splits per (b, h), so the row is written by the split whose slots hold
-    it and a merge launch follows."""
+    steps (at most 40 for long windows).  The shapes with long windows have
+    several splits per (b, h), so the row is written by the split whose slots
+    hold it, and the splits are merged in the step kernel (up to 63 heads) or
+    by the merge launch (64 heads)."""
     import sliding_window_attention_ring_amd as swa
     say("fused row step", kind, B, H, D, W, layout)
     dt = torch.float32 if kind == "fp32" else torch.bfloat16
