@@ -58,12 +58,18 @@ def log(*a):
 
 
 def kernel_source_hash(kind: str) -> str:
+    """Hash of the decode kernel's sources with line comments and blank lines
+    left out, so that a counter summary stays valid across comment edits and
+    lapses with any change to the code."""
     files = (["swa_device.h", "swa_commit.h", "swa_decode_int8.hip"] if kind.startswith("int8")
              else ["swa_device.h", "swa_decode.hip"])
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -26,7 +26,9 @@
 //   each split writes a partial (m, l, acc[D]) and a small second kernel
 //   merges the splits and normalizes.  The kernel boundary makes the
 //   partials visible across the XCDs' separate L2 caches, so no work-group
-//   needs a device-wide fence (each would write back and invalidate its L2).
+//   needs a device-wide fence (each would write back and invalidate its L2);
+//   the fused step with up to 63 heads merges in its own launch instead,
+//   through device-coherent stores and loads (decode_rows_wg, INMERGE).
 #include "swa_device.h"
 #include "swa_launch.h"
 

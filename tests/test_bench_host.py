@@ -96,6 +96,21 @@ def test_traffic_from_another_kernel_source_is_not_reported(tmp_path, monkeypatc
     assert bench.kernel_source_hash("bf16") != bench.kernel_source_hash("int8")
 
 
+def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    """A comment edit keeps a counter summary valid; a code edit retires it."""
+    import shutil
+    for f in ("swa_device.h", "swa_decode.hip"):
+        shutil.copy(os.path.join(bench.CSRC, f), tmp_path / f)
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    h0 = bench.kernel_source_hash("bf16")
+    src = tmp_path / "swa_decode.hip"
+    text = src.read_text()
+    src.write_text("// a new comment line\n\n" + text.replace("namespace swa {", "namespace swa {  // trailing", 1))
+    assert bench.kernel_source_hash("bf16") == h0
+    src.write_text(text.replace("kNegBig = -1e30f", "kNegBig = -1e29f", 1))
+    assert bench.kernel_source_hash("bf16") != h0
+
+
 def test_cpu_baseline_times_ragged_lengths():
     """The oracle leg of the bench runs on a ragged workload too: each sampled
     pair is timed at its own sequence's length, and its bytes follow it."""
