@@ -5,8 +5,9 @@ per sequence is appended and one query per sequence attends to the cache.
 By default a step is one call of the fused entry point (``decode_step_int8``
 for the INT8 workloads, with the witness bound, or with the certificate, TV
 bound and gate for the dithered one; ``decode_step`` otherwise), which
-appends and attends in one launch plus a merge launch when a (b, h) has
-several splits.  ``--no-fuse`` times ``kv_append`` followed by the separate
+appends and attends in one launch.  When a (b, h) has several splits, a
+merge launch follows for the INT8 kinds; the row kinds merge them in the
+step kernel (up to 63 heads).  ``--no-fuse`` times ``kv_append`` followed by the separate
 decode call instead.  The default workload is the INT8 cache with the
 witness bound at 32768 context (B=16, H=32, D=128), prefilled with 32768
 rotary keys.
@@ -291,7 +292,8 @@ def main():
 
     # Call c goes to instance c mod n_inst, as that instance's step c div n_inst.
     # One call per step: kv_append of the token and the decode, fused into
-    # one launch (plus the merge launch when a (b, h) has several splits).
+    # one launch (INT8 kinds: plus the merge launch when a (b, h) has several
+    # splits).
     fuse = not args.no_fuse
     dither = wl.kind == "int8_dither"
 
@@ -417,8 +419,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": read_traffic(wl.name, wl.kind),
-            "kernel": ((("decode_step_int8_kernel" if wl.kind.startswith("int8") else "decode_step_rows_kernel")
-                        + " (the step call; plus the merge kernel when a (b, h) has several splits)") if fuse else
+            "kernel": (("decode_step_int8_kernel (the step call; plus the merge kernel when a (b, h) has several "
+                        "splits)" if wl.kind.startswith("int8") else
+                        "decode_step_rows_kernel (the step call; several splits per (b, h) merge in it up to 63 "
+                        "heads, else in the merge kernel)") if fuse else
                        "decode_int8_kernel" if wl.kind.startswith("int8") else "decode_kernel"),
             "kernel_ms": round(kern_ms, 4),
             "kernel_ms_median": round(kern_median, 4),

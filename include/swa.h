@@ -100,12 +100,16 @@ enum { SWA_LAYOUT_RING = 0, SWA_LAYOUT_PAGED = 1 };
  *  step_sync      [B][64] int32  completion counters of the fused decode step
  *                                (decode_step, decode_step_int8): element
  *                                [b][0] counts the work-groups of sequence b
- *                                that finished the current step (the rest of
- *                                the 256-byte line is padding, so sequences
- *                                never queue on one line).  Zero after
- *                                swa_cache_reset, and every fused step leaves
- *                                it zero.  May be NULL if the fused steps are
- *                                not used (they return SWA_ENULL then).
+ *                                that finished the current step; when
+ *                                decode_step merges several splits in its
+ *                                launch (H <= 63), element [b][1 + h] counts
+ *                                the splits of head h that published their
+ *                                partials.  The rest of the 256-byte line is
+ *                                padding, so sequences never queue on one
+ *                                line.  Zero after swa_cache_reset, and every
+ *                                fused step leaves it zero.  May be NULL if
+ *                                the fused steps are not used (they return
+ *                                SWA_ENULL then).
  */
 typedef struct swa_cache {
   int32_t kind, B, H, D, W;
@@ -239,8 +243,10 @@ int decode_attn_int8_dither(const swa_cache *c, const void *q, float *out, float
  * the decode are one kernel launch: the work-group whose split holds slot
  * next_position mod W of a (b, h) writes the token's rows there, then every
  * work-group decodes its split; the last work-group of a sequence to finish,
- * counted in the cache's step_sync, advances next_position.  A plan with
- * several splits per (b, h) adds the merge launch, as decode_attn does.
+ * counted in the cache's step_sync, advances next_position.  With several
+ * splits per (b, h) and H <= 63, the last split of each (b, h) to finish,
+ * counted in step_sync[b][1 + h], merges the splits in the same launch;
+ * with more heads a merge launch follows, as in decode_attn.
  *  k_new, v_new  [B][H][1][D] in the cache's input dtype
  *  q, out, ws    as for decode_attn
  * Errors: descriptor errors, SWA_EUNSUPPORTED for an INT8 kind, SWA_ENULL
