@@ -256,7 +256,9 @@ const char* swa_status_string(int status) {
     case SWA_ENULL: return "required pointer is NULL";
     case SWA_EALIGN: return "pointer not aligned (16 bytes for K/V/q/out/staging/workspace)";
     case SWA_EUNSUPPORTED: return "kind or head_dim not supported by this entry point";
-    case SWA_EWORKSPACE: return "workspace smaller than swa_workspace_bytes()";
+    case SWA_EWORKSPACE:
+      return "workspace smaller than swa_workspace_bytes() (decode_step_int8_static: the shape needs more "
+             "than its 16 MiB scratch)";
     case SWA_EHIP: return "HIP kernel launch failed";
   }
   return "unknown status";
