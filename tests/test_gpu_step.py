@@ -157,6 +157,8 @@ def test_fused_step_headline_shape_and_graph():
                                                  ("bf16", 1, 2, 64, 4096, "paged"), ("fp32", 2, 3, 32, 1024, "ring"),
                                                  ("bf16", 2, 3, 16, 2048, "paged"), ("bf16", 3, 2, 32, 96, "ring"),
                                                  ("fp32", 2, 2, 256, 512, "ring"),
+                                                 # 63 heads: the last counter of the step_sync line
+                                                 ("bf16", 1, 63, 128, 4096, "paged"),
                                                  # 64 heads: too many for the in-kernel merge's counters,
                                                  # so the several splits go through the merge kernel
                                                  ("bf16", 1, 64, 128, 4096, "ring")])
