@@ -5,6 +5,8 @@ and INT8 caches of both layouts, with one or several splits per (b, h).
 After every operation the ring state is compared bit-exactly and every
 decode output with the oracle."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -76,7 +78,7 @@ def test_mixed_operation_fuzz(kind, layout, W, seed, D):
     for op in range(40):
         r = rng.random()
         if r < 0.45:  # whole-batch append
-            T = int(rng.choice([1, 1, 1, 2, 15, 16, 17, W - 1, W + 5, 2 * W + 3]))
+            T = max(1, int(rng.choice([1, 1, 1, 2, 15, 16, 17, W - 1, W + 5, 2 * W + 3])))  # T >= 1 (W = 1)
             k = torch.randn((B, H, T, D), generator=g).to(torch.bfloat16)
             v = torch.randn((B, H, T, D), generator=g).to(torch.bfloat16)
             swa.kv_append(cache, k.cuda(), v.cuda())
@@ -142,3 +144,36 @@ def test_mixed_operation_fuzz(kind, layout, W, seed, D):
             else:
                 outs = (swa.decode_attn(cache, q.cuda()),)
             check_outputs(op, q, outs, ns, step=False)
+
+
+def random_configurations(seed: int, n: int):
+    """n random (kind, layout, W, seed, D) for the fuzz above: every kind and
+    layout, windows from 1 slot to 2048 (odd ones on bf16 rings), every head
+    dim of the row kinds."""
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        kind = str(rng.choice(["bf16", "int8", "int8_dither"]))
+        layout = str(rng.choice(["ring", "paged"]))
+        if kind == "bf16":
+            D = int(rng.choice([16, 32, 64, 128, 256]))
+            if layout == "ring":
+                W = int(rng.choice([1, 2, 3, 5, 17, 33, 48, 100, 513, 1024, 2047]))
+            else:
+                W = int(rng.choice([16, 32, 48, 64, 96, 160, 512, 1024, 2048]))
+        else:
+            D = 128
+            W = int(rng.choice([16, 32, 48, 64, 96, 160, 512, 1024, 2048]))
+        yield kind, layout, W, int(rng.integers(1000, 10 ** 6)), D
+
+
+def test_random_configuration_fuzz():
+    """The mixed-operation fuzz over random configurations: 8 by default;
+    SWA_FUZZ_CONFIGS=<n> and SWA_FUZZ_SEED=<seed> run a wider campaign
+    (on MI355X: 200 configurations with the default seed, and 222 with
+    seed 777, passed)."""
+    n = int(os.environ.get("SWA_FUZZ_CONFIGS", "8"))
+    seed = int(os.environ.get("SWA_FUZZ_SEED", "20261202"))
+    for i, cfg in enumerate(random_configurations(seed, n)):
+        print(f"fuzz configuration {i}: kind={cfg[0]} layout={cfg[1]} W={cfg[2]} seed={cfg[3]} D={cfg[4]}",
+              flush=True)
+        test_mixed_operation_fuzz(*cfg)
