@@ -131,3 +131,17 @@ def test_stale_next_position_is_a_large_error():
     good = att.masked_attention(q, np.arange(12), k, v, 11, w)
     stale = att.masked_attention(q, np.arange(12) + 4, k, v, 11, w)
     assert np.max(np.abs(good - stale)) > 1e-2
+
+
+def test_empty_visible_set_gives_zeros():
+    """R7: an empty cache (or an empty visible set) answers with the zero
+    vector, through every oracle entry point that can see one."""
+    d = 16
+    q = np.ones(d)
+    empty = np.zeros((0, d))
+    assert not np.any(att.plain_attention(q, empty, empty))
+    assert att.plain_attention(q, empty, empty).shape == (d,)
+    assert not np.any(att.masked_attention(q, np.arange(0), empty, empty, -1, 4))
+    hist = decoder.SequenceHistory(2, d)
+    assert not np.any(hist.attend(np.ones((2, d)), 4))
+    assert not np.any(hist.attend_window(np.ones((2, d)), 4))

@@ -250,6 +250,59 @@ def test_expected_store_values_and_witness_brute_force(n, w, zero_block):
     assert st["staged_positions"] == list(range(16 * nb, n))
 
 
+
+@pytest.mark.parametrize("n,w", [(16 * 3 + 5, 40), (16 * 4, 64), (16 * 6 + 15, 200)])
+def test_int8_decode_against_brute_force_store(n, w):
+    """int8_decode against an independent computation from the brute-force
+    block quantizer: keys AND values read as s * code for positions in
+    complete blocks and exactly for the staged tail, the masked softmax of
+    the window, c_t = (1/sqrt(d)) sum_b ||q_b|| ||r_{t,b}|| per visible token
+    (0 when staged), e_t = |q . r_t| / sqrt(d), and cmax = max_t c_t -- which
+    for random queries lies strictly above max_t e_t."""
+    rng = np.random.default_rng(7 * n + w)
+    d = 32
+    k = (rng.standard_normal((n, d)) * 2).astype(np.float32).astype(np.float64)
+    v = (rng.standard_normal((n, d)) * 0.7).astype(np.float32).astype(np.float64)
+    q = rng.standard_normal(d)
+    res = int8.int8_decode(q, k, v, n, w)
+    nb = n // 16
+    k_hat, v_hat = k.copy(), v.copy()
+    for blk in range(nb):
+        rows = slice(16 * blk, 16 * blk + 16)
+        (sk, ck), (sv, cv) = _brute_block(k[rows].astype(np.float32)), _brute_block(v[rows].astype(np.float32))
+        k_hat[rows] = float(sk) * ck
+        v_hat[rows] = float(sv) * cv
+    ln = min(w, n)
+    vis = np.arange(n - ln, n)
+    sc = k_hat[vis] @ q / np.sqrt(d)
+    p = np.exp(sc - sc.max())
+    out = (p / p.sum()) @ v_hat[vis]
+    np.testing.assert_allclose(res["out"], out, rtol=0, atol=1e-12)
+    r = k[vis] - k_hat[vis]
+    qn = np.sqrt((q.reshape(-1, 8) ** 2).sum(axis=1))
+    c = np.array([sum(qn[b] * np.sqrt((r[i, 8 * b:8 * b + 8] ** 2).sum()) for b in range(d // 8))
+                  for i in range(ln)]) / np.sqrt(d)
+    e = np.abs(r @ q) / np.sqrt(d)
+    np.testing.assert_allclose(res["c"], c, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(res["e"], e, rtol=1e-12, atol=1e-300)
+    assert not np.any(res["c"][vis >= 16 * nb]), "staged tokens are exact"
+    assert res["cmax"] == pytest.approx(c.max(), rel=1e-12)
+    assert res["cmax"] > e.max() * (1 + 1e-6)
+
+
+def test_int8_decode_single_visible_token_is_its_dequantized_value():
+    """A window of one slot whose token sits in a complete block: the output
+    is that token's value row s_V * code exactly (softmax of one logit is 1)."""
+    rng = np.random.default_rng(31)
+    d = 32
+    k = rng.standard_normal((16, d)).astype(np.float32).astype(np.float64)
+    v = rng.standard_normal((16, d)).astype(np.float32).astype(np.float64)
+    res = int8.int8_decode(rng.standard_normal(d), k, v, 16, 1)
+    sv, cv = _brute_block(v.astype(np.float32))
+    np.testing.assert_array_equal(res["out"], float(sv) * cv[15])
+    assert not np.array_equal(res["out"], v[15]), "the value row is read quantized"
+
+
 def test_storage_format(golden):
     g = golden("witcert_witness_format.json")
     d = g["head_dim"]

@@ -132,6 +132,35 @@ MUTATIONS = [
     ("oracle/dither.py", "e = np.abs((k[vis] - k_hat[vis]) @ q) / np.sqrt(d)",
      "e = np.abs((k[vis] - k_hat[vis]) @ q) / d"),
     ("oracle/dither.py", "quantized = vis < nq_all", "quantized = vis <= nq_all"),
+    ("oracle/int8.py", "        return np.zeros(x32.shape, dtype=np.int8)", "        return np.ones(x32.shape, dtype=np.int8)"),
+    ("oracle/int8.py", "out = softmax_weights((k_hat[vis] @ q) / np.sqrt(d)) @ v_hat[vis]",
+     "out = softmax_weights((k_hat[vis] @ q) / np.sqrt(d)) @ v[vis]"),
+    ("oracle/int8.py", "out = softmax_weights((k_hat[vis] @ q) / np.sqrt(d)) @ v_hat[vis]",
+     "out = softmax_weights((k[vis] @ q) / np.sqrt(d)) @ v_hat[vis]"),
+    ("oracle/int8.py", '"cmax": float(np.max(c)) if ln else 0.0', '"cmax": float(np.max(e)) if ln else 0.0'),
+    ("oracle/int8.py", "vis = np.arange(t - ln + 1, t + 1, dtype=np.int64)", "vis = np.arange(t - ln, t, dtype=np.int64)"),
+    ("oracle/int8.py", "return np.sqrt(np.sum(xb * xb, axis=-1))", "return np.sum(np.abs(xb), axis=-1)"),
+    ("oracle/attention.py", "    if k.shape[0] == 0:\n        return np.zeros(v.shape[-1], dtype=np.float64)",
+     "    if k.shape[0] == 0:\n        return np.ones(v.shape[-1], dtype=np.float64)"),
+    ("oracle/attention.py", "    if not np.any(vis):\n        return np.zeros(v.shape[-1], dtype=np.float64)",
+     "    if not np.any(vis):\n        return np.ones(v.shape[-1], dtype=np.float64)"),
+    ("oracle/attention.py", "return (pos >= t - w + 1) & (pos <= t)", "return (pos >= t - w + 1) & (pos < t)"),
+    ("oracle/decoder.py", "attention.masked_attention(q[h], pos, k[h], v[h], t, w)",
+     "attention.masked_attention(q[h], pos, k[h], v[h], t, w + 1)"),
+    ("oracle/decoder.py", "idx = listmodel.last_window(w, list(range(self._n)))",
+     "idx = listmodel.last_window(w - 1, list(range(self._n)))"),
+    ("oracle/decoder.py", "wit[s] = int8.band_norms(r, band)", "wit[s] = int8.band_norms(r, band) * 1.001"),
+    ("oracle/tv.py", "if p < nb * oint8.BLOCK:", "if p < (nb - 1) * oint8.BLOCK:"),
+    ("oracle/tv.py", "p_exact = softmax_weights((k[pos] @ q) / np.sqrt(d))", "p_exact = softmax_weights((k[pos] @ q) / d)"),
+    ("oracle/rope.py", "out[..., 0::2] = a * c - b * s", "out[..., 0::2] = a * c + b * s"),
+    ("oracle/reuse.py", "        if a != b:\n            break", "        if a != b:\n            continue"),
+    ("oracle/listmodel.py", "    if w < len(c2):\n        return c2[1:]", "    if w < len(c2):\n        return c2[:-1]"),
+    ("oracle/listmodel.py", "    return all(pos_of(cell) == base + i for i, cell in enumerate(c))",
+     "    return all(pos_of(cell) >= base for i, cell in enumerate(c))"),
+    ("oracle/philox.py", "    for _ in range(rounds):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> width)",
+     "    for _ in range(rounds - 1):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> width)"),
+    ("oracle/philox.py", "    for _ in range(rounds):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> sh)",
+     "    for _ in range(rounds - 1):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> sh)"),
 ]
 
 
