@@ -21,3 +21,11 @@ def test_bf16_known_patterns():
 def test_to_f64_passes_float_through():
     x = np.array([1.5, -0.25], dtype=np.float32)
     assert bits.to_f64(x).tolist() == [1.5, -0.25]
+
+
+def test_to_f64_reads_uint16_as_bf16_bits():
+    """uint16 arrays are bf16 bit patterns (0x3F80 is 1.0, 0xC040 is -3.0);
+    float arrays widen as they are."""
+    got = bits.to_f64(np.array([0x3F80, 0xC040, 0x0000], dtype=np.uint16))
+    np.testing.assert_array_equal(got, [1.0, -3.0, 0.0])
+    np.testing.assert_array_equal(bits.to_f64(np.array([0.1], dtype=np.float32)), [float(np.float32(0.1))])

@@ -22,9 +22,13 @@ What pins it:
   the logit error over independent dither streams, its coverage (no
   violations at the stated budget) and its tightness (the largest
   error reaches most of the bound), all through int8_dither_decode;
+* the bias term: with a budget that makes the concentration term vanish,
+  the certificate still covers the exact mean logit error over the dither
+  (all 256 values per channel enumerated) where that mean is largest;
 * decode special cases: no complete block -> exact attention and a zero
   certificate; empty history -> zeros; a one-hot query returns its value
-  row within half a step.
+  row within half a step; a one-slot window returns the stored value row
+  s (code - u) exactly.
 """
 
 from fractions import Fraction
@@ -334,3 +338,64 @@ def test_position_offset_is_the_same_history_further_on():
                                   head=1, delta=0.1)
     assert np.array_equal(a["out"], b["out"]) and a["cert"] == b["cert"]
     assert np.array_equal(a["k_codes"][-w:], b["k_codes"][-w:])
+
+
+def test_one_slot_window_returns_the_stored_value_row_exactly():
+    """A one-slot window over a complete block: softmax of one logit is 1, so
+    the output is the stored value row s_V (code - u), with the scale and the
+    codes re-derived here from their definition (absmax / 127 rounded to
+    float32 from exact rationals; the nearest integer, ties to even, of the
+    float32 sum f32(x / s) + u)."""
+    rng = np.random.default_rng(41)
+    d = 32
+    k = rng.standard_normal((16, d)).astype(np.float32).astype(np.float64)
+    v = rng.standard_normal((16, d)).astype(np.float32).astype(np.float64)
+    r = dither.int8_dither_decode(rng.standard_normal(d), k, v, 16, 1, request=5, layer=2, head=1, delta=0.1)
+    u = dither.dither(5, 2, 1, [15], d)[0]
+    v32 = v.astype(np.float32)
+    a = max(abs(Fraction(float(x))) for x in v32.ravel()) / 127
+    s = np.float32(float(a))
+    s = min((s, np.nextafter(s, np.float32(np.inf)), np.nextafter(s, np.float32(-np.inf))),
+            key=lambda c: (abs(Fraction(float(c)) - a), int(np.array(c).view(np.uint32)) & 1))
+    want = np.empty(d)
+    for c in range(d):
+        t = Fraction(float(np.float32(np.float32(v32[15, c] / s) + np.float32(u[c]))))
+        lo = t.numerator // t.denominator
+        rest = t - lo
+        code = lo + 1 if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and lo % 2) else lo
+        want[c] = float(Fraction(float(s)) * (code - Fraction(float(u[c]))))
+    np.testing.assert_array_equal(r["out"], want)
+    assert not np.array_equal(r["out"], v[15]), "the value row is read quantized"
+
+
+def test_certificate_bias_term_covers_the_exact_mean_error():
+    """With delta = 2 n_q the concentration term vanishes (ln 1 = 0) and the
+    certificate is its bias term (s / sqrt(d)) ||q||_1 beta.  It must cover
+    the exact mean of the logit error over the dither, (s / sqrt(d))
+    sum_c q_c mu_c, where mu_c is the mean residual of channel c over all 256
+    dither values (channels are independent, so means add).  Every channel
+    is put at the fractional offset of x / s whose mean residual is largest,
+    and q follows its sign, so the mean error is d times one channel's."""
+    d = 32
+    s0 = 2.0 ** -4                                   # absmax 127 * s0 gives the scale s0 exactly
+    u = dither.dither_values(np.arange(256))
+    best, best_mu = None, 0.0
+    for i in range(512):
+        x = np.float32((10 + i / 512) * s0)
+        z = float(x) / s0                            # exact: dyadic
+        codes = dither.block_codes(np.full(256, x, dtype=np.float32), np.float32(s0), u)
+        mu = float(np.mean(codes.astype(np.float64) - u - z))
+        if abs(mu) > abs(best_mu):
+            best, best_mu = x, mu
+    assert abs(best_mu) > dither.BETA / np.sqrt(d) * 2, "the bias term matters at this offset"
+    assert abs(best_mu) <= dither.BETA
+    block = np.zeros((16, d), dtype=np.float32)
+    block[0, 0] = np.float32(127 * s0)
+    block[15, :] = best
+    assert dither.block_codes(block, int8.block_scale(block), np.zeros((16, d))).any()
+    assert int8.block_scale(block) == np.float32(s0)
+    q = np.full(d, np.sign(best_mu))
+    mean_err = abs(s0 / np.sqrt(d) * float(np.sum(q * best_mu)))
+    bound = float(dither.token_bound(q, np.array([s0]), 1, 2.0)[0])
+    assert bound >= mean_err
+    assert bound == pytest.approx(s0 / np.sqrt(d) * d * dither.BETA, rel=1e-12)

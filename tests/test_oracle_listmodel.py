@@ -157,3 +157,10 @@ def test_exhaustive_small_histories_against_definition():
         hist = cells(n)
         expect = [c for c in hist if pos_of(c) > n - 1 - w]
         assert lm.last_window(w, hist) == expect
+
+
+def test_no_token_means_no_window():
+    """Before the first token (p < 0) the query window is empty."""
+    for w in (1, 4, 7):
+        assert lm.window_positions(w, -1) == []
+        assert lm.window_positions(w, 0) == [0]

@@ -161,6 +161,48 @@ MUTATIONS = [
      "    for _ in range(rounds - 1):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> width)"),
     ("oracle/philox.py", "    for _ in range(rounds):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> sh)",
      "    for _ in range(rounds - 1):\n        p0 = m0 * x0\n        p1 = m1 * x2\n        x0, x1, x2, x3 = ((p1 >> sh)"),
+    ('oracle/dither.py',
+     'out = softmax_weights((k_hat[vis] @ q) / np.sqrt(d)) @ v_hat[vis]\n    return {\n        "out": out,\n        "positions": vis,\n        "e": e,',
+     'out = softmax_weights((k_hat[vis] @ q) / np.sqrt(d)) @ v[vis]\n    return {\n        "out": out,\n        "positions": vis,\n        "e": e,'),
+    ('oracle/dither.py',
+     '+ np.sum(np.abs(q)) * BETA',
+     '+ np.linalg.norm(q) * BETA'),
+    ('oracle/listmodel.py',
+     '    if p < 0:\n        return []',
+     '    if p < 0:\n        return [0]'),
+    ('oracle/reuse.py',
+     '    return max(0, min(n, len(new) - 1))',
+     '    return min(n, len(new) - 1)'),
+    ('oracle/bits.py',
+     '    if x.dtype == np.uint16:\n        return bf16_to_f64(x)',
+     '    if x.dtype == np.uint16:\n        return x.astype(np.float64)'),
+    ('oracle/tv.py',
+     '    if pos.size == 0:\n        return {"tv": 0.0, "bound": 0.0, "cmax": 0.0}',
+     '    if pos.size == 0:\n        return {"tv": 0.0, "bound": 1.0, "cmax": 0.0}'),
+    ('oracle/dither.py',
+     '        "cert": float(np.max(c)) if ln else 0.0,',
+     '        "cert": float(np.max(e)) if ln else 0.0,'),
+    ('oracle/dither.py',
+     '        s_tok[rows] = np.float64(ks[blk])',
+     '        s_tok[rows] = np.float64(vs[blk])'),
+    ('oracle/dither.py',
+     'f = np.linalg.norm(q) * np.sqrt',
+     'f = np.sum(np.abs(q)) * np.sqrt'),
+    ('oracle/dither.py',
+     '    for g in range(groups):\n        for i, p in enumerate(pos):\n            ctr[i, g] = philox_counter(layer, head, int(p), g)',
+     '    for g in range(groups):\n        for i, p in enumerate(pos):\n            ctr[i, g] = philox_counter(layer, head, int(p), 0)'),
+    ('oracle/decoder.py',
+     '        v_codes[s] = vc[j]\n',
+     '        v_codes[s] = vc[j] if j % 16 else kc[j]\n'),
+    ('oracle/tv.py',
+     '    logp = np.log(p)\n',
+     '    logp = np.log(p) * 0.5\n'),
+    ('oracle/rope.py',
+     '    return np.asarray(pos, dtype=np.float64)[..., None] * theta',
+     '    return (np.asarray(pos, dtype=np.float64)[..., None] + 1) * theta'),
+    ('oracle/attention.py',
+     '    return e / np.sum(e, axis=-1, keepdims=True)',
+     '    return e / (np.sum(e, axis=-1, keepdims=True) + 1e-9)'),
 ]
 
 

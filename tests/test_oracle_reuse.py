@@ -50,3 +50,10 @@ def test_int8_rule_matches_block_model():
             rows_ok = reuse.truncation_exact(n, cut, w)
             committed_tail = (cut % 16 != 0) and (cut < 16 * (n // 16))
             assert reuse.truncation_exact(n, cut, w, int8=True) == (rows_ok and not committed_tail)
+
+
+def test_empty_query_reuses_nothing():
+    """An empty new request has no token to recompute and reuses nothing: the
+    cut is 0, never negative."""
+    assert reuse.common_prefix([1, 2, 3], []) == 0
+    assert reuse.common_prefix([], []) == 0

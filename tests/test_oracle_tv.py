@@ -101,3 +101,11 @@ def test_int8_tv_via_one_hot_values():
         r = tv.int8_attention_tv(q, k, v, n, w)
         assert r["tv"] == pytest.approx(tv.tv_distance(pe, pq), abs=1e-12)
         assert r["tv"] > 0
+
+
+def test_empty_history_has_zero_tv_and_bound():
+    """Nothing visible: no attention weights move, so TV and bound are 0."""
+    d = 128
+    z = np.zeros((0, d))
+    r = tv.int8_attention_tv(np.ones(d), z, z, 0, 64)
+    assert r["tv"] == 0.0 and r["bound"] == 0.0 and r["cmax"] == 0.0
