@@ -208,14 +208,16 @@ def _brute_block(x32: np.ndarray):
     return s, codes
 
 
-@pytest.mark.parametrize("n,w,zero_block", [(16 * 9 + 5, 64, None), (40, 64, 1), (16 * 12, 32, 10)])
+@pytest.mark.parametrize("n,w,zero_block", [(16 * 9 + 5, 64, None), (40, 64, 1), (16 * 12, 32, 10),
+                                              (16 * 5 + 15, 64, None)])
 def test_expected_store_values_and_witness_brute_force(n, w, zero_block):
     """Every stored field of ``expected_int8_store`` against brute force from
     exact rationals, slot by slot: the slot's position (newest committed
     position congruent to the slot), the key and value codes and scales of
     the block that position belongs to, and the witness rows (band norms of
     the exact key residual k - s_K code, compared through their squares,
-    exactly).  Covers a wrapped ring, an unfilled one and an all-zero block."""
+    exactly).  Covers a wrapped ring, an unfilled one, an all-zero block and
+    a history one token short of a block commit."""
     rng = np.random.default_rng(n + w)
     d = 32
     k = (rng.standard_normal((n, d)) * 3).astype(np.float32)

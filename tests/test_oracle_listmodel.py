@@ -164,3 +164,13 @@ def test_no_token_means_no_window():
     for w in (1, 4, 7):
         assert lm.window_positions(w, -1) == []
         assert lm.window_positions(w, 0) == [0]
+
+
+def test_valid_compares_contents_not_lengths():
+    """Valid (the cache equals lastWindow) fails for a state of the right
+    length that holds the wrong cells or the right cells in the wrong order."""
+    hist = list(range(10))
+    assert lm.valid(4, hist, [6, 7, 8, 9])
+    assert not lm.valid(4, hist, [9, 8, 7, 6])
+    assert not lm.valid(4, hist, [5, 6, 7, 8])
+    assert not lm.valid(4, hist, [6, 7, 8])

@@ -203,6 +203,54 @@ MUTATIONS = [
     ('oracle/attention.py',
      '    return e / np.sum(e, axis=-1, keepdims=True)',
      '    return e / (np.sum(e, axis=-1, keepdims=True) + 1e-9)'),
+    ('oracle/listmodel.py',
+     '    return list(c) == last_window(w, hs)',
+     '    return len(c) == len(last_window(w, hs))'),
+    ('oracle/listmodel.py',
+     '        c = step(w, c, kv)\n    return c',
+     '        c = step(w, c, kv)\n    return c[::-1] if len(c) > 3 else c'),
+    ('oracle/listmodel.py',
+     '    return [buf[(start + i) % w] for i in range(ln)]',
+     '    return [buf[(start + i + 1) % w] for i in range(ln)]'),
+    ('oracle/reuse.py',
+     '    if int8 and cut % 16 != 0 and cut < 16 * (n // 16):',
+     '    if int8 and cut % 8 != 0 and cut < 16 * (n // 16):'),
+    ('oracle/decoder.py',
+     '    idx = listmodel.ring_state(w, list(int(p) for p in positions), lambda p: p, -1)',
+     '    idx = listmodel.ring_state(w, list(int(p) for p in positions)[:-1], lambda p: p, -1)'),
+    ('oracle/decoder.py',
+     '    nb = n // blk\n    ks, kc = int8.quantize_history(np.asarray(k)[: nb * blk], nb)',
+     '    nb = (n + 1) // blk\n    ks, kc = int8.quantize_history(np.asarray(k)[: nb * blk], nb)'),
+    ('oracle/int8.py',
+     '    for blk in range(nb):\n        rows = slice(blk * BLOCK, (blk + 1) * BLOCK)\n        s, c = quantize_block(x[rows])',
+     '    for blk in range(nb):\n        rows = slice(blk * BLOCK, (blk + 1) * BLOCK)\n        s, c = quantize_block(x[rows][::-1])'),
+    ('oracle/int8.py',
+     '    return np.clip(q, -QMAX, QMAX).astype(np.int8)',
+     '    return np.clip(q, -QMAX + 1, QMAX).astype(np.int8)'),
+    ('oracle/int8.py',
+     '    return np.float64(np.float32(s)) * np.asarray(codes, dtype=np.float64)',
+     '    return np.float64(np.float32(s) * np.float32(1.0000001)) * np.asarray(codes, dtype=np.float64)'),
+    ('oracle/dither.py',
+     '    return np.asarray(words, dtype=np.uint32).astype("<u4").view(np.uint8).reshape(-1, GROUP)',
+     '    return np.asarray(words, dtype=np.uint32)[..., ::-1].astype("<u4").view(np.uint8).reshape(-1, GROUP)'),
+    ('oracle/dither.py',
+     '    return np.clip(np.rint(t), -QMAX, QMAX).astype(np.int8)',
+     '    return np.clip(np.rint(t), -QMAX, QMAX - 1).astype(np.int8)'),
+    ('oracle/dither.py',
+     '    nq_all = nb * BLOCK\n',
+     '    nq_all = nb * BLOCK if nb < 3 else (nb - 1) * BLOCK\n'),
+    ('oracle/tv.py',
+     '    for mask in range(1 << n):',
+     '    for mask in range(1 << (n - 1)):'),
+    ('oracle/philox.py',
+     '    32: (0xD2511F53, 0xCD9E8D57, 0x9E3779B9, 0xBB67AE85),',
+     '    32: (0xD2511F53, 0xCD9E8D57, 0x9E3779B9, 0xBB67AE84),'),
+    ('oracle/attention.py',
+     '    m = np.max(scores, axis=-1, keepdims=True)',
+     '    m = np.max(scores, axis=-1, keepdims=True) * 0 + np.min(np.where(np.isfinite(scores), scores, np.inf), axis=-1, keepdims=True)'),
+    ('oracle/rope.py',
+     '    a, b = x[..., 0::2], x[..., 1::2]\n    out = np.empty_like(x)',
+     '    b, a = x[..., 0::2], x[..., 1::2]\n    out = np.empty_like(x)'),
 ]
 
 

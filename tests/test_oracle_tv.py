@@ -109,3 +109,15 @@ def test_empty_history_has_zero_tv_and_bound():
     z = np.zeros((0, d))
     r = tv.int8_attention_tv(np.ones(d), z, z, 0, 64)
     assert r["tv"] == 0.0 and r["bound"] == 0.0 and r["cmax"] == 0.0
+
+
+@pytest.mark.parametrize("p0", [0.1, 0.9, 0.5, 0.02])
+def test_two_token_worst_case_in_closed_form(p0):
+    """Two tokens: the sign patterns that move anything raise one logit by e
+    and lower the other by e, which multiplies that token's odds by e^(2e);
+    the largest TV over sign patterns is the larger of the two closed forms
+    p' - p with p' = p e^(2e) / (p e^(2e) + 1 - p), whichever token it is."""
+    e = 0.7
+    p = np.array([p0, 1 - p0])
+    want = max(pi * np.exp(2 * e) / (pi * np.exp(2 * e) + 1 - pi) - pi for pi in p)
+    assert tv.max_tv_over_signs(p, e) == pytest.approx(want, rel=1e-12)
