@@ -17,6 +17,7 @@ import torch
 
 from oracle import decoder, dither as odither, int8 as oint8
 from tests.gpu_util import assert_close, check_dither_decode, check_int8_decode, check_ring_rows, oracle_out
+from tests.parity_checks import check_int8_store_arrays
 
 W, H, D = 6, 2, 16
 
@@ -128,3 +129,192 @@ def test_halved_certificate_is_caught():
     check_dither_decode(res["out"], cert, 0, 0, q, k, v, n, w, 9, 0, 1e-3)
     with pytest.raises(AssertionError):
         check_dither_decode(res["out"], 0.5 * cert, 0, 0, q, k, v, n, w, 9, 0, 1e-3)
+
+
+# Each assertion of the INT8, Tier B and ring comparisons rejects a state or
+# output that differs from the oracle's in that one respect.  The "GPU"
+# state is built from the oracle the way the kernels store it (witness
+# rounded up to fp16, bounds padded), the comparison must accept it, and
+# each planted difference must be rejected.
+
+def _bf16_rows(rng, n, d):
+    """n rows of bf16 bit patterns (finite) and their float64 values."""
+    f32 = rng.standard_normal((n, d)).astype(np.float32)
+    bits16 = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    return bits16, (bits16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _fp16_up(x):
+    """Nonnegative float64 -> nearest fp16 at or above it, as float64."""
+    h = x.astype(np.float16)
+    below = h.astype(np.float64) < x
+    h[below] = np.nextafter(h[below], np.float16(np.inf))
+    return h.astype(np.float64)
+
+
+class Int8State:
+    def __init__(self, n=16 * 5 + 7, w=48, seed=5):
+        rng = np.random.default_rng(seed)
+        self.n, self.w = n, w
+        self.kbits, self.k64 = _bf16_rows(rng, n, 128)
+        self.vbits, self.v64 = _bf16_rows(rng, n, 128)
+        st = decoder.expected_int8_store(self.k64, self.v64, n, w)
+        self.kc, self.vc = st["k_codes"].copy(), st["v_codes"].copy()
+        self.ks, self.vs = st["k_scale"].copy(), st["v_scale"].copy()
+        self.exact_wit = st["witness"]
+        self.wit = _fp16_up(st["witness"])
+        self.pos = st["slot_pos"].copy()
+        self.ksg = np.zeros((16, 128), dtype=np.uint16)
+        self.vsg = np.zeros((16, 128), dtype=np.uint16)
+        self.staged = st["staged_positions"]
+        for p in self.staged:
+            self.ksg[p % 16], self.vsg[p % 16] = self.kbits[p], self.vbits[p]
+        self.live = np.nonzero(self.pos >= 0)[0]
+
+    def check(self):
+        check_int8_store_arrays(self.kc, self.vc, self.ks, self.vs, self.wit, self.pos, self.ksg, self.vsg,
+                                self.k64, self.v64, self.n, self.w)
+
+
+def test_int8_store_comparison_accepts_the_oracle_state():
+    Int8State().check()
+
+
+@pytest.mark.parametrize("field", ["witness_below", "witness_loose", "k_codes", "v_codes", "k_scale", "v_scale",
+                                   "k_stage", "v_stage", "pos"])
+def test_int8_store_comparison_rejects_each_field(field):
+    s = Int8State()
+    slot = s.live[len(s.live) // 2]
+    if field == "witness_below":
+        # one band rounded down instead of up: below the exact norm
+        b = int(np.argmax(s.wit[slot] > s.exact_wit[slot]))
+        s.wit[slot, b] = np.nextafter(np.float16(s.wit[slot, b]), np.float16(0)).astype(np.float64)
+        assert s.wit[slot, b] < s.exact_wit[slot, b]
+    elif field == "witness_loose":
+        s.wit[slot, 3] *= 1.01
+    elif field == "k_codes":
+        s.kc[slot, 7] += 1 if s.kc[slot, 7] < 127 else -1
+    elif field == "v_codes":
+        s.vc[slot, 7] += 1 if s.vc[slot, 7] < 127 else -1
+    elif field == "k_scale":
+        s.ks[slot // 16] = np.nextafter(s.ks[slot // 16], np.float32(np.inf))
+    elif field == "v_scale":
+        s.vs[slot // 16] = np.nextafter(s.vs[slot // 16], np.float32(np.inf))
+    elif field == "k_stage":
+        s.ksg[s.staged[-1] % 16, 5] ^= 1
+    elif field == "v_stage":
+        s.vsg[s.staged[-1] % 16, 5] ^= 1
+    elif field == "pos":
+        s.pos[slot] += s.w  # same slot, the wrong absolute position
+    with pytest.raises(AssertionError):
+        s.check()
+
+
+class Int8Decode:
+    def __init__(self, n=16 * 3 + 9, w=64, seed=8):
+        rng = np.random.default_rng(seed)
+        self.n, self.w = n, w
+        self.k64 = rng.standard_normal((n, 128))
+        self.v64 = rng.standard_normal((n, 128))
+        self.q64 = rng.standard_normal(128)
+        res = oint8.int8_decode(self.q64, self.k64, self.v64, n, w)
+        self.res = res
+        self.out = res["out"].copy()
+        self.cmax = res["cmax"] * (1 + 2.0 ** -12)
+        self.quant = res["positions"] < 16 * (n // 16)
+        self.slots = res["positions"] % w
+        self.c_all = np.zeros(w)
+        self.c_all[self.slots[self.quant]] = res["c"][self.quant] * (1 + 2.0 ** -12)
+
+    def check(self):
+        check_int8_decode(self.out, self.cmax, self.c_all, 0, 0, self.q64, self.k64, self.v64, self.n, self.w)
+
+
+def test_int8_decode_comparison_accepts_the_oracle_outputs():
+    Int8Decode().check()
+
+
+@pytest.mark.parametrize("field", ["out", "cmax_loose", "c_below_error", "c_loose", "c_on_staged", "c_on_empty_slot"])
+def test_int8_decode_comparison_rejects_each_output(field):
+    d = Int8Decode()
+    assert d.n < d.w and not d.quant.all()   # unwritten slots and staged tokens exist
+    t = int(np.argmax(np.where(d.quant, d.res["e"], -1)))   # the quantized token with the largest error
+    if field == "out":
+        d.out[3] += 4e-3
+    elif field == "cmax_loose":
+        d.cmax *= 1.01
+    elif field == "c_below_error":
+        d.c_all[d.slots[t]] = d.res["e"][t] * 0.99
+    elif field == "c_loose":
+        d.c_all[d.slots[t]] *= 1.01
+    elif field == "c_on_staged":
+        d.c_all[d.slots[~d.quant][0]] = 0.1
+    elif field == "c_on_empty_slot":
+        d.c_all[d.w - 1] = 0.1
+    with pytest.raises(AssertionError):
+        d.check()
+
+
+class DitherDecode:
+    def __init__(self, n=60, w=32, seed=4, tau=0.2):
+        rng = np.random.default_rng(seed)
+        self.n, self.w, self.tau = n, w, tau
+        self.k64 = rng.standard_normal((n, 128)).astype(np.float32).astype(np.float64)
+        self.v64 = rng.standard_normal((n, 128)).astype(np.float32).astype(np.float64)
+        self.q64 = rng.standard_normal(128)
+        self.delta = 1e-3
+        res = odither.int8_dither_decode(self.q64, self.k64, self.v64, n, w, 9, 0, 0,
+                                         float(np.float32(self.delta)))
+        self.out = res["out"].copy()
+        self.cert = res["cert"] * (1 + 2.0 ** -12)
+        self.tv = min(float(np.tanh(self.cert / 2)) * (1 + 2.0 ** -20), 1.0)
+        self.gate = int(self.tv > tau)
+
+    def check(self):
+        check_dither_decode(self.out, self.cert, 0, 0, self.q64, self.k64, self.v64, self.n, self.w, 9, 0,
+                            self.delta, self.tv, self.gate, tau=self.tau)
+
+
+def test_dither_decode_comparison_accepts_the_oracle_outputs():
+    DitherDecode().check()
+
+
+@pytest.mark.parametrize("field", ["out", "cert_loose", "tv_below", "tv_loose", "gate"])
+def test_dither_decode_comparison_rejects_each_output(field):
+    d = DitherDecode()
+    if field == "out":
+        d.out[0] -= 4e-3
+    elif field == "cert_loose":  # with tv and gate consistent with it, so only the tightness check can object
+        d.cert *= 1.01
+        d.tv = min(float(np.tanh(d.cert / 2)) * (1 + 2.0 ** -20), 1.0)
+        d.gate = int(d.tv > d.tau)
+    elif field == "tv_below":
+        d.tv *= 1 - 1e-4
+    elif field == "tv_loose":
+        d.tv *= 1 + 1e-4
+    elif field == "gate":
+        d.gate = 1 - d.gate
+    with pytest.raises(AssertionError):
+        d.check()
+
+
+def test_ring_comparison_rejects_a_wrong_position_record():
+    """Rows in the right slots, but a slot's recorded absolute position is off
+    by the window (the same slot, another lap)."""
+    n = 9
+    k, v = data(n)
+    bad = Ring(k, v, n)
+    bad.pos[0, (n - 1) % W] += W
+    with pytest.raises(AssertionError):
+        check_ring_rows(bad, k, v, np.array([n]))
+
+
+def test_ring_comparison_rejects_a_wrong_value_row():
+    """Keys and positions right; one slot holds another token's value row."""
+    n = 9
+    k, v = data(n)
+    bad = Ring(k, v, n)
+    s = (n - 1) % W
+    bad.v[0, :, s] = torch.from_numpy(v[0, :, n - 2].view(np.int16)).view(torch.bfloat16)
+    with pytest.raises(AssertionError):
+        check_ring_rows(bad, k, v, np.array([n]))

@@ -6,8 +6,11 @@ fix.  This test checks that those pins have teeth: for each entry below it
 copies ``oracle/`` and the pin tests into a temporary directory, plants one
 plausible mistake in the copy (a dropped scale, an off-by-one in the window or
 the ring, a swapped operand, a wrong rounding rule, a wrong Philox round...),
-runs the pins there, and requires them to fail.  The unmodified copy must
-pass, so a failure is the planted bug's doing.  The repository itself is
+runs the pins there, and requires them to fail.  The same is done for the
+comparisons the GPU parity tests use (``tests/parity_checks.py`` and the
+ring check of ``tests/gpu_util.py``): with any one assertion taken out, a
+negative control in ``tests/test_negative_controls.py`` must fail.  The
+unmodified copy must pass, so a failure is the planted bug's doing.  The repository itself is
 never modified, and nothing here touches the HIP library or a GPU.
 
 Following [Lean-SWA] §6.4 (the specification serves as the oracle, and the
@@ -251,6 +254,53 @@ MUTATIONS = [
     ('oracle/rope.py',
      '    a, b = x[..., 0::2], x[..., 1::2]\n    out = np.empty_like(x)',
      '    b, a = x[..., 0::2], x[..., 1::2]\n    out = np.empty_like(x)'),
+    # The comparisons the GPU parity tests use (tests/parity_checks.py, tests/gpu_util.py): each assertion
+    # taken out must let a planted difference through a negative control.
+    ('tests/parity_checks.py',
+     '    assert np.all(wg >= we), f"{what}: stored witness below the exact band norm"',
+     '    pass'),
+    ('tests/parity_checks.py',
+     '    assert np.all(wg <= we * (1 + 2.0 ** -9) + 2.0 ** -24), f"{what}: stored witness not tight"',
+     '    pass'),
+    ('tests/parity_checks.py',
+     '    np.testing.assert_array_equal(vc[live], st["v_codes"][live], err_msg=f"{what} value codes")',
+     '    pass'),
+    ('tests/parity_checks.py',
+     '    np.testing.assert_array_equal(vs[lb], st["v_scale"][lb], err_msg=f"{what} value scales")',
+     '    pass'),
+    ('tests/parity_checks.py',
+     '        np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])\n\n\ndef fp16',
+     '        pass\n\n\ndef fp16'),
+    ('tests/parity_checks.py',
+     '    assert cmax <= (res["cmax"] + slack) * (1 + 2.0 ** -9), (cmax, res["cmax"])',
+     '    pass'),
+    ('tests/parity_checks.py',
+     '        assert np.all(cg >= e), "per-token bound below the true logit error"',
+     '        pass'),
+    ('tests/parity_checks.py',
+     '        assert np.all(cg <= (c + slack) * (1 + 2.0 ** -9)), "per-token bound not tight"',
+     '        pass'),
+    ('tests/parity_checks.py',
+     '        assert not np.any(np.asarray(c_all)[~vis]), "slots without a visible quantized token must be 0"',
+     '        pass'),
+    ('tests/parity_checks.py',
+     '    assert cert <= ref * (1 + 2.0 ** -10) + 1e-30, (what, b, h, cert, ref)',
+     '    pass'),
+    ('tests/parity_checks.py',
+     '        assert t <= tv <= min(t * (1 + 2.0 ** -18) + 1e-30, 1.0), (tv, t)',
+     '        pass'),
+    ('tests/parity_checks.py',
+     '            assert int(gate) == int(tv > tau)',
+     '            pass'),
+    ('tests/gpu_util.py',
+     '        np.testing.assert_array_equal(pos[b], exp)',
+     '        pass'),
+    ('tests/gpu_util.py',
+     '        np.testing.assert_array_equal(vv[b][:, live], v_in[b][:, exp[live]])',
+     '        pass'),
+    ('tests/gpu_util.py',
+     '        assert npos[b] == n[b], (b, npos[b], n[b])',
+     '        pass'),
 ]
 
 
@@ -268,7 +318,8 @@ def _copy_tree(dst: str) -> None:
 _FIRST = {"attention": ["test_oracle_attention.py"], "int8": ["test_oracle_int8.py"],
           "decoder": ["test_oracle_int8.py", "test_oracle_attention.py"], "rope": ["test_oracle_int8.py"],
           "listmodel": ["test_oracle_listmodel.py"], "bits": ["test_oracle_bits.py"], "tv": ["test_oracle_tv.py"],
-          "reuse": ["test_oracle_reuse.py"], "philox": ["test_oracle_dither.py"], "dither": ["test_oracle_dither.py"]}
+          "reuse": ["test_oracle_reuse.py"], "philox": ["test_oracle_dither.py"], "dither": ["test_oracle_dither.py"],
+          "parity_checks": ["test_negative_controls.py"], "gpu_util": ["test_negative_controls.py"]}
 
 
 def _order(mutation) -> list:
