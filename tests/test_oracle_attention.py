@@ -145,3 +145,20 @@ def test_empty_visible_set_gives_zeros():
     hist = decoder.SequenceHistory(2, d)
     assert not np.any(hist.attend(np.ones((2, d)), 4))
     assert not np.any(hist.attend_window(np.ones((2, d)), 4))
+
+
+def test_masking_is_exact_at_large_logit_magnitudes():
+    """Invisible rows get exactly zero weight however large the visible
+    logits are in magnitude: with every visible logit near -1e4 (or +1e4) and
+    invisible rows present, the masked attention equals plain attention over
+    the visible rows alone."""
+    rng = np.random.default_rng(12)
+    d, n, w = 16, 12, 4
+    for sign in (-1.0, 1.0):
+        q = np.ones(d) * 100.0
+        k = rng.standard_normal((n, d)) * 0.01 + sign * 25.0   # q.k/sqrt(d) ~ sign * 1e4
+        v = rng.standard_normal((n, d))
+        t = n - 1
+        got = att.masked_attention(q, np.arange(n), k, v, t, w)
+        want = att.plain_attention(q, k[t - w + 1:], v[t - w + 1:])
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)

@@ -344,3 +344,22 @@ def test_rope_angle_from_definition():
     e0[0] = 1.0
     y0 = rope.rope_interleaved(e0, 3)
     assert y0[0] == pytest.approx(np.cos(3.0), abs=1e-15) and y0[1] == pytest.approx(np.sin(3.0), abs=1e-15)
+
+
+def test_rope_half_split_is_the_interleaved_rotation_on_reordered_dims():
+    """The half-split form rotates the pairs (i, i + D/2) by the same angles
+    that the interleaved form applies to (2i, 2i + 1): reorder the dims so
+    those pairs become adjacent and the two agree exactly; both preserve the
+    norm of the whole vector."""
+    rng = np.random.default_rng(21)
+    d = 32
+    x = rng.standard_normal((5, d))
+    pos = np.array([0, 1, 7, 100, 32767])
+    h = d // 2
+    perm = np.empty(d, dtype=np.int64)
+    perm[0::2], perm[1::2] = np.arange(h), np.arange(h) + h      # y[2i] = x[i], y[2i+1] = x[i + D/2]
+    got = rope.rope_half_split(x, pos)
+    want = np.empty_like(x)
+    want[:, perm] = rope.rope_interleaved(x[:, perm], pos)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)

@@ -254,6 +254,51 @@ MUTATIONS = [
     ('oracle/rope.py',
      '    a, b = x[..., 0::2], x[..., 1::2]\n    out = np.empty_like(x)',
      '    b, a = x[..., 0::2], x[..., 1::2]\n    out = np.empty_like(x)'),
+    ('oracle/listmodel.py',
+     '    lhs = (list(xs) + [kv])[max(n + 1 - w, 0):]\n    rhs = list(xs)[max(n + 1 - w, 0):] + [kv]',
+     '    lhs = (list(xs) + [kv])[max(n + 1 - w, 0):]\n    rhs = list(xs)[max(n + 2 - w, 0):] + [kv]'),
+    ('oracle/listmodel.py',
+     '    lhs = (list(xs) + [kv])[max(n + 1 - w, 0):]\n    rhs = list(xs)[max(n - w, 0):] + [kv]',
+     '    lhs = (list(xs) + [kv])[max(n + 1 - w, 0):]\n    rhs = list(xs)[max(n + 1 - w, 0):] + [kv]'),
+    ('oracle/decoder.py',
+     '            self._cache = (np.arange(self._n, dtype=np.int64), k, v)',
+     '            self._cache = (np.arange(1, self._n + 1, dtype=np.int64), k, v)'),
+    ('oracle/decoder.py',
+     '        return np.stack([attention.masked_attention(q[h], pos, k[h], v[h], t, w)',
+     '        return np.stack([attention.masked_attention(q[0], pos, k[h], v[h], t, w)'),
+    ('oracle/attention.py',
+     '    scores = np.where(vis, (k @ q) / np.sqrt(d), -np.inf)',
+     '    scores = np.where(vis, (k @ q) / np.sqrt(d), -1e3)'),
+    ('oracle/int8.py',
+     '    xb = x.reshape(x.shape[:-1] + (d // band, band))\n    return',
+     '    xb = x.reshape(x.shape[:-1] + (d // band, band))[..., ::-1, :]\n    return'),
+    ('oracle/int8.py',
+     '    nq = band_norms(q, band)\n',
+     '    nq = band_norms(q, band)[::-1]\n'),
+    ('oracle/int8.py',
+     '    r = k[:n] - k_hat  # exact residual',
+     '    r = k[:n] - k_hat * 1.0  # exact residual\n    r[-1] = 0'),
+    ('oracle/philox.py',
+     '    64: (0xD2E7470EE14C6C93, 0xCA5A826395121157, 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B),',
+     '    64: (0xD2E7470EE14C6C93, 0xCA5A826395121157, 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73A),'),
+    ('oracle/dither.py',
+     '    return group_bytes(words.reshape(-1, 4)).reshape(pos.size, d)',
+     '    return group_bytes(words.reshape(-1, 4)[::-1]).reshape(pos.size, d)'),
+    ('oracle/dither.py',
+     '    assert 0 <= r < 1 << 64\n    return np.array([r & 0xFFFFFFFF, r >> 32], dtype=np.uint64)',
+     '    assert 0 <= r < 1 << 64\n    return np.array([r & 0xFFFFFFFF, (r >> 32) ^ 1], dtype=np.uint64)'),
+    ('oracle/dither.py',
+     '        k_hat[rows] = dequantize(kc[rows], ks[blk], u[rows])',
+     '        k_hat[rows] = dequantize(kc[rows], ks[blk], u[rows][::-1])'),
+    ('oracle/tv.py',
+     '    p_quant = softmax_weights((k_hat @ q) / np.sqrt(d))',
+     '    p_quant = softmax_weights((k_hat @ q) / np.sqrt(d) * 1.0001)'),
+    ('oracle/reuse.py',
+     '    if n > w and cut not in (0, n):\n        return False',
+     '    if n > w + 1 and cut not in (0, n):\n        return False'),
+    ('oracle/rope.py',
+     '    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)',
+     '    return np.concatenate([a * c - b * s, a * s - b * c], axis=-1)'),
     # The comparisons the GPU parity tests use (tests/parity_checks.py, tests/gpu_util.py): each assertion
     # taken out must let a planted difference through a negative control.
     ('tests/parity_checks.py',
