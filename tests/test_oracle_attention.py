@@ -20,6 +20,7 @@ import workloads
 from workloads import gen
 from oracle import attention as att
 from oracle import bits, decoder, listmodel
+from oracle import int8 as oint8
 
 
 def sdpa_reference(q, pos, k, v, t, w):
@@ -145,6 +146,8 @@ def test_empty_visible_set_gives_zeros():
     hist = decoder.SequenceHistory(2, d)
     assert not np.any(hist.attend(np.ones((2, d)), 4))
     assert not np.any(hist.attend_window(np.ones((2, d)), 4))
+    empty128 = np.zeros((0, 128))
+    assert not np.any(oint8.int8_decode(np.ones(128), empty128, empty128, 0, 16)["out"])
 
 
 def test_masking_is_exact_at_large_logit_magnitudes():

@@ -399,3 +399,51 @@ def test_certificate_bias_term_covers_the_exact_mean_error():
     bound = float(dither.token_bound(q, np.array([s0]), 1, 2.0)[0])
     assert bound >= mean_err
     assert bound == pytest.approx(s0 / np.sqrt(d) * d * dither.BETA, rel=1e-12)
+
+
+def _nearest_int_even(t: Fraction) -> int:
+    lo = t.numerator // t.denominator
+    rest = t - lo
+    return lo + 1 if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and lo % 2) else lo
+
+
+def test_decode_errors_and_bounds_against_a_brute_force_store():
+    """Through int8_dither_decode, at a budget delta = 2 n_q that zeroes the
+    concentration term: every visible token's true logit error
+    |q . (k - k_hat)| / sqrt(d) and bound (s_K / sqrt(d)) ||q||_1 beta (0 for
+    the exact staged tokens), n_q and the certificate (their maximum), with
+    k_hat = s (code - u) re-derived here from the definitions of the scale
+    and the codes (exact rationals; float32 steps as the method fixes them)
+    and u from the Philox stream."""
+    rng = np.random.default_rng(55)
+    n, w, d = 16 * 3 + 5, 40, 32
+    req, layer, head = 77, 3, 1
+    k = (rng.standard_normal((n, d)) * 2).astype(np.float32).astype(np.float64)
+    v = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    q = rng.standard_normal(d)
+    vis = np.arange(n - w, n)
+    quant = vis < 16 * (n // 16)
+    n_q = int(quant.sum())
+    res = dither.int8_dither_decode(q, k, v, n, w, req, layer, head, delta=2.0 * n_q)
+    assert res["n_q"] == n_q
+    u = dither.dither(req, layer, head, np.arange(16 * (n // 16)), d)
+    k_hat = k.copy()
+    s_tok = np.zeros(n)
+    for blk in range(n // 16):
+        rows = slice(16 * blk, 16 * blk + 16)
+        x32 = k[rows].astype(np.float32)
+        a = max(abs(Fraction(float(x))) for x in x32.ravel()) / 127
+        s = np.float32(float(a))
+        s = min((s, np.nextafter(s, np.float32(np.inf)), np.nextafter(s, np.float32(-np.inf))),
+                key=lambda c: (abs(Fraction(float(c)) - a), int(np.array(c).view(np.uint32)) & 1))
+        for i in range(16):
+            for c in range(d):
+                t = Fraction(float(np.float32(np.float32(x32[i, c] / s) + np.float32(u[16 * blk + i, c]))))
+                code = max(-127, min(127, _nearest_int_even(t)))
+                k_hat[16 * blk + i, c] = float(Fraction(float(s)) * (code - Fraction(float(u[16 * blk + i, c]))))
+        s_tok[rows] = float(s)
+    e = np.abs((k[vis] - k_hat[vis]) @ q) / np.sqrt(d)
+    c = np.where(quant, s_tok[vis] / np.sqrt(d) * np.sum(np.abs(q)) * dither.BETA, 0.0)
+    np.testing.assert_allclose(res["e"], e, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(res["c"], c, rtol=1e-12, atol=0)
+    assert res["cert"] == pytest.approx(c.max(), rel=1e-12)

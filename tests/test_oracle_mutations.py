@@ -299,6 +299,36 @@ MUTATIONS = [
     ('oracle/rope.py',
      '    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)',
      '    return np.concatenate([a * c - b * s, a * s - b * c], axis=-1)'),
+    ('oracle/dither.py',
+     '    assert position0 % BLOCK == 0 and position0 >= 0\n',
+     '    assert position0 % BLOCK == 0 and position0 >= 0\n    position0 = 0\n'),
+    ('oracle/dither.py',
+     '    c = np.where(quantized, token_bound(q, s_tok[vis], n_q, delta), 0.0)',
+     '    c = np.where(quantized, token_bound(q, s_tok[vis], n_q + 1, delta), 0.0)'),
+    ('oracle/dither.py',
+     '    c = np.where(quantized, token_bound(q, s_tok[vis], n_q, delta), 0.0)',
+     '    c = np.where(quantized, token_bound(q, s_tok[vis], n_q, delta * 2), 0.0)'),
+    ('oracle/dither.py',
+     '    c = np.where(quantized, token_bound(q, s_tok[vis], n_q, delta), 0.0)',
+     '    c = np.where(quantized, token_bound(q, np.full(ln, s_tok[vis].max() if ln else 0.0), n_q, delta), 0.0)'),
+    ('oracle/dither.py',
+     '    e = np.abs((k[vis] - k_hat[vis]) @ q) / np.sqrt(d)',
+     '    e = np.abs((k[vis] - k_hat[vis]) @ np.abs(q)) / np.sqrt(d)'),
+    ('oracle/dither.py',
+     '    return np.float64(np.float32(s)) * (np.asarray(codes, dtype=np.float64) - np.asarray(u, dtype=np.float64))',
+     '    return np.float64(np.float32(s)) * (np.asarray(codes, dtype=np.float64) - np.asarray(u, dtype=np.float32).astype(np.float64) * (1 + 2.0 ** -20))'),
+    ('oracle/dither.py',
+     '    groups = d // GROUP\n',
+     '    groups = d // GROUP\n    pos = pos + (pos >= 1000)\n'),
+    ('oracle/int8.py',
+     '    if ln == 0:\n        out = np.zeros(v.shape[-1], dtype=np.float64)',
+     '    if ln == 0:\n        out = np.ones(v.shape[-1], dtype=np.float64)'),
+    ('oracle/dither.py',
+     '    if ln == 0:\n        out = np.zeros(v.shape[-1], dtype=np.float64)',
+     '    if ln == 0:\n        out = np.ones(v.shape[-1], dtype=np.float64)'),
+    ('oracle/dither.py',
+     '        "n_q": n_q,',
+     '        "n_q": ln,'),
     # The comparisons the GPU parity tests use (tests/parity_checks.py, tests/gpu_util.py): each assertion
     # taken out must let a planted difference through a negative control.
     ('tests/parity_checks.py',
