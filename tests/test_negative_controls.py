@@ -16,7 +16,8 @@ import pytest
 import torch
 
 from oracle import decoder, dither as odither, int8 as oint8
-from tests.gpu_util import assert_close, check_dither_decode, check_int8_decode, check_ring_rows, oracle_out
+from tests.gpu_util import (assert_close, check_dither_decode, check_dither_store, check_int8_decode, check_ring_rows,
+                            oracle_out)
 from tests.parity_checks import check_int8_store_arrays
 
 W, H, D = 6, 2, 16
@@ -318,3 +319,69 @@ def test_ring_comparison_rejects_a_wrong_value_row():
     bad.v[0, :, s] = torch.from_numpy(v[0, :, n - 2].view(np.int16)).view(torch.bfloat16)
     with pytest.raises(AssertionError):
         check_ring_rows(bad, k, v, np.array([n]))
+
+
+class DitherCache:
+    """A Tier B ring cache (B = 1, H = 1) as CPU tensors, filled from the
+    oracle's own quantization: the layout check_dither_store reads."""
+
+    def __init__(self, n=16 * 4 + 6, w=48, seed=6, req=21, layer=2):
+        rng = np.random.default_rng(seed)
+        self.W, self.B, self.layer, self.layout = w, 1, layer, "ring"
+        self.n = n
+        self.kbits, self.k64 = _bf16_rows(rng, n, 128)
+        self.vbits, self.v64 = _bf16_rows(rng, n, 128)
+        self.request_id = torch.tensor([req], dtype=torch.int64)
+        nb = n // 16
+        k = np.zeros((1, 1, w, 128), dtype=np.int8)
+        v = np.zeros_like(k)
+        ks = np.zeros((1, 1, w // 16), dtype=np.float32)
+        vs = np.zeros_like(ks)
+        pos = np.full((1, w), -1, dtype=np.int32)
+        for kb in range(max(0, nb - w // 16), nb):
+            rows = np.arange(16 * kb, 16 * kb + 16)
+            u = odither.dither(req, layer, 0, rows, 128)
+            sk, ck = odither.quantize_block(self.k64[rows], u)
+            sv, cv = odither.quantize_block(self.v64[rows], u)
+            s0 = (16 * kb) % w
+            k[0, 0, s0:s0 + 16], v[0, 0, s0:s0 + 16] = ck, cv
+            ks[0, 0, s0 // 16], vs[0, 0, s0 // 16] = sk, sv
+            pos[0, s0:s0 + 16] = rows
+        ksg = np.zeros((1, 1, 16, 128), dtype=np.uint16)
+        vsg = np.zeros_like(ksg)
+        for p in range(16 * nb, n):
+            ksg[0, 0, p % 16], vsg[0, 0, p % 16] = self.kbits[p], self.vbits[p]
+        self.k, self.v = torch.from_numpy(k), torch.from_numpy(v)
+        self.k_scale, self.v_scale = torch.from_numpy(ks), torch.from_numpy(vs)
+        self.pos = torch.from_numpy(pos)
+        self.k_stage = torch.from_numpy(ksg.view(np.int16)).view(torch.bfloat16)
+        self.v_stage = torch.from_numpy(vsg.view(np.int16)).view(torch.bfloat16)
+
+    def check(self):
+        check_dither_store(self, 0, 0, self.k64, self.v64, self.n)
+
+
+def test_dither_store_comparison_accepts_the_oracle_state():
+    DitherCache().check()
+
+
+@pytest.mark.parametrize("field", ["k_codes", "v_codes", "k_scale", "v_scale", "pos", "k_stage", "v_stage"])
+def test_dither_store_comparison_rejects_each_field(field):
+    c = DitherCache()
+    slot = 20
+    if field == "k_codes":
+        c.k[0, 0, slot, 3] += 1 if c.k[0, 0, slot, 3] < 127 else -1
+    elif field == "v_codes":
+        c.v[0, 0, slot, 3] += 1 if c.v[0, 0, slot, 3] < 127 else -1
+    elif field == "k_scale":
+        c.k_scale[0, 0, slot // 16] *= 1.5
+    elif field == "v_scale":
+        c.v_scale[0, 0, slot // 16] *= 1.5
+    elif field == "pos":
+        c.pos[0, slot] += c.W
+    elif field == "k_stage":
+        c.k_stage.view(torch.int16)[0, 0, (c.n - 1) % 16, 9] ^= 1
+    elif field == "v_stage":
+        c.v_stage.view(torch.int16)[0, 0, (c.n - 1) % 16, 9] ^= 1
+    with pytest.raises(AssertionError):
+        c.check()

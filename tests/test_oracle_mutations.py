@@ -376,6 +376,27 @@ MUTATIONS = [
     ('tests/gpu_util.py',
      '        assert npos[b] == n[b], (b, npos[b], n[b])',
      '        pass'),
+    ('tests/gpu_util.py',
+     '        np.testing.assert_array_equal(kc[slot0:slot0 + 16], ck, err_msg=f"key codes b={b} h={h} block {kb}")',
+     '        pass'),
+    ('tests/gpu_util.py',
+     '        np.testing.assert_array_equal(vc[slot0:slot0 + 16], cv, err_msg=f"value codes b={b} h={h} block {kb}")',
+     '        pass'),
+    ('tests/gpu_util.py',
+     '        assert ks[slot0 // 16] == sk and vs[slot0 // 16] == sv, (kb, ks[slot0 // 16], sk)',
+     '        assert ks[slot0 // 16] == sk, (kb, ks[slot0 // 16], sk)'),
+    ('tests/gpu_util.py',
+     '        assert ks[slot0 // 16] == sk and vs[slot0 // 16] == sv, (kb, ks[slot0 // 16], sk)',
+     '        assert vs[slot0 // 16] == sv, (kb, ks[slot0 // 16], sk)'),
+    ('tests/gpu_util.py',
+     '    np.testing.assert_array_equal(pos, exp_pos)\n    ksg',
+     '    pass\n    ksg'),
+    ('tests/gpu_util.py',
+     '        np.testing.assert_array_equal(bits.to_f64(ksg[p % 16]), k64[p])\n        np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])',
+     '        np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])'),
+    ('tests/gpu_util.py',
+     '        np.testing.assert_array_equal(bits.to_f64(ksg[p % 16]), k64[p])\n        np.testing.assert_array_equal(bits.to_f64(vsg[p % 16]), v64[p])',
+     '        np.testing.assert_array_equal(bits.to_f64(ksg[p % 16]), k64[p])'),
 ]
 
 
