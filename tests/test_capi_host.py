@@ -75,6 +75,22 @@ def test_argument_checks_return_codes():
     assert L.kv_append(p(d), None, A16, 1, None) == -2
     assert L.kv_append(p(d), A16, A16, -1, None) == -1
     assert L.kv_append(p(d), A16, A16, 0, None) == -1                       # T < 1
+    # every descriptor field is checked on its own
+    assert L.kv_append(p(desc(H=0)), A16, A16, 1, None) == -1               # H < 1
+    assert L.kv_append(p(desc(W=0)), A16, A16, 1, None) == -1               # W < 1
+    assert L.kv_append(p(desc(B=65536)), A16, A16, 1, None) == -1           # grid limits
+    assert L.kv_append(p(desc(H=65536)), A16, A16, 1, None) == -1
+    assert L.kv_append(p(desc(D=256, W=8388608)), None, A16, 1, None) == -1  # one (b, h) region reaches 4 GiB
+    assert L.kv_append(p(desc(v=0x20004)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(pos=0x30002)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(next_position=0x40002)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(kind=2, k_stage=0x80004)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(kind=2, v_stage=0x90004)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(kind=2, k_scale=0x50002)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(kind=2, v_scale=0x60002)), A16, A16, 1, None) == -3
+    assert L.kv_append(p(desc(kind=2, witness=0x70004)), A16, A16, 1, None) == -3
+    assert L.kv_truncate(p(d), A16, ctypes.c_void_p(0xA0002), None) == -3    # ok misaligned
+    assert L.kv_truncate(p(d), ctypes.c_void_p(0xA0002), None, None) == -3   # cut misaligned
     need = L.swa_workspace_bytes(p(d))
     assert need > 0 and L.swa_workspace_bytes(p(desc(D=100))) == 0
     assert L.decode_attn(p(d), A16, A16, ws, need - 1, None) == -5           # small workspace
@@ -87,6 +103,11 @@ def test_argument_checks_return_codes():
     assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, A16, A16, float("nan"), None, ws, 1 << 30,
                                          None) == -1
     assert L.decode_attn_int8_witness_tv(p(d), A16, A16, A16, A16, A16, 0.2, None, ws, 1 << 30, None) == -4
+    O2 = ctypes.c_void_p(0xA0002)
+    assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, O2, None, None, 0.2, None, ws, 1 << 30, None) == -3
+    assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, None, None, 0.2, O2, ws, 1 << 30, None) == -3
+    assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, O2, None, 0.2, None, ws, 1 << 30, None) == -3
+    assert L.decode_attn_int8_witness_tv(p(i8), A16, A16, A16, A16, O2, 0.2, None, ws, 1 << 30, None) == -3
     # Tier B kind: no witness needed, request ids required, delta in (0, 1]
     dz = desc(kind=3, witness=None, request_id=0xD0000)
     nz = L.swa_workspace_bytes(p(dz))
