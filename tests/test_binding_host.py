@@ -70,3 +70,42 @@ def test_workspace_must_be_gpu_memory():
         cache.workspace_init(torch.zeros(64, dtype=torch.uint8))
     with pytest.raises(ValueError, match="GPU tensor"):
         cache._workspace(None, torch.zeros(64, dtype=torch.uint8))
+
+
+class _FakeArg(_FakeCuda):
+    def dim(self):
+        return len(self.shape)
+
+
+def test_every_entry_point_checks_its_tensor_shapes(monkeypatch):
+    """A tensor of the wrong shape never reaches the C ABI, which sees only
+    pointers: each entry point of the binding rejects one (the shapes follow
+    the cache: B, H, D, W; one new token per fused step)."""
+    import types
+    import sliding_window_attention_ring_amd as swa
+    from sliding_window_attention_ring_amd import cache as cmod
+    monkeypatch.setattr(cmod.torch, "Tensor", _FakeCuda)
+    bf = torch.bfloat16
+    rows = types.SimpleNamespace(B=2, H=3, D=64, W=32, kind="bf16", input_dtype=bf)
+    i8 = types.SimpleNamespace(B=2, H=3, D=128, W=32, kind="int8", input_dtype=bf)
+    cases = [
+        lambda: swa.kv_append(rows, _FakeArg((2, 3, 5, 64), bf), _FakeArg((2, 3, 4, 64), bf)),
+        lambda: swa.kv_append(rows, _FakeArg((2, 3, 5, 32), bf), _FakeArg((2, 3, 5, 32), bf)),
+        lambda: swa.decode_attn(rows, _FakeArg((2, 3, 32), bf)),
+        lambda: swa.decode_attn(rows, _FakeArg((2, 3, 64), torch.float32)),
+        lambda: swa.decode_attn_int8_witness(i8, _FakeArg((2, 3, 64), bf)),
+        lambda: swa.decode_attn_int8_witness_tv(i8, _FakeArg((3, 2, 128), bf)),
+        lambda: swa.decode_attn_int8_dither(i8, _FakeArg((2, 3, 127), bf), 1e-3),
+        lambda: swa.decode_step(rows, _FakeArg((2, 3, 2, 64), bf), _FakeArg((2, 3, 2, 64), bf),
+                                _FakeArg((2, 3, 64), bf)),
+        lambda: swa.decode_step(rows, _FakeArg((2, 3, 1, 64), bf), _FakeArg((2, 3, 1, 64), bf),
+                                _FakeArg((2, 3, 63), bf)),
+        lambda: swa.decode_step_int8(i8, _FakeArg((2, 3, 1, 128), bf), _FakeArg((2, 2, 1, 128), bf),
+                                     _FakeArg((2, 3, 128), bf)),
+        lambda: swa.decode_step_int8_static(i8, _FakeArg((2, 3, 1, 128), bf), _FakeArg((2, 3, 1, 128), bf),
+                                            _FakeArg((2, 3, 128), torch.float32)),
+        lambda: swa.kv_truncate(rows, _FakeArg((3,), torch.int32)),
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises(ValueError, match="expected"):
+            call()
