@@ -73,6 +73,10 @@ class KVCache:
         if paged:
             if W % 16:
                 raise ValueError("a paged cache needs W % 16 == 0")
+            if block_table is not None and (not isinstance(block_table, torch.Tensor)
+                                            or tuple(block_table.shape) != (B, W // 16)):
+                # the kernels index the table as [B][W/16]: a smaller one would be read past its end
+                raise ValueError(f"block_table must be a tensor of shape [B, W/16] = [{B}, {W // 16}]")
             self.num_pages = B * (W // 16) if num_pages is None else int(num_pages)
             rows = (self.num_pages, H, 16)
         else:

@@ -22,6 +22,27 @@ def test_cache_refuses_host_memory():
         swa.KVCache("bf16", 1, 1, 64, 16, layout="tree")
 
 
+def test_paged_cache_checks_its_block_table_shape(monkeypatch):
+    """The kernels read the table as [B][W/16]; a table of another shape is
+    refused before any device memory is allocated (allocation is stubbed
+    out here, so a table of the right shape stops there)."""
+    import sliding_window_attention_ring_amd as swa
+    from sliding_window_attention_ring_amd import cache as cmod
+
+    class Stop(Exception):
+        pass
+
+    def no_gpu(*a, **k):
+        raise Stop()
+
+    monkeypatch.setattr(cmod.torch, "empty", no_gpu)
+    for shape in [(2, 3), (2, 5), (8,), (1, 4)]:
+        with pytest.raises((ValueError, Stop)) as e:
+            swa.KVCache("bf16", 2, 1, 64, 64, layout="paged", num_pages=16,
+                        block_table=torch.zeros(shape, dtype=torch.int32))
+        assert e.type is ValueError or shape == (2, 4)
+
+
 def test_tensor_checks():
     from sliding_window_attention_ring_amd.cache import _need
     t = torch.zeros((2, 3), dtype=torch.float32)
