@@ -1,7 +1,7 @@
 """Seeded fuzz of mixed operations against per-sequence oracle histories:
 appends of random sizes (whole batch or one sequence through a view),
-truncations (exact or fallback), fused decode steps and decodes, on bf16
-and INT8 caches of both layouts, with one or several splits per (b, h).
+truncations (exact or fallback), fused decode steps and decodes, on bf16,
+fp32 and INT8 caches of both layouts, with one or several splits per (b, h).
 After every operation the ring state is compared bit-exactly and every
 decode output with the oracle."""
 
@@ -35,15 +35,18 @@ def _gpu():
                                                   # the other head dims of the row kinds (32 rows per wave load
                                                   # over two pages at D = 16; 4 and 32 splits at D = 32 and 256)
                                                   ("bf16", "paged", 96, 13, 16), ("bf16", "ring", 1024, 14, 32),
-                                                  ("bf16", "ring", 1024, 15, 256)])
+                                                  ("bf16", "ring", 1024, 15, 256),
+                                                  # fp32 rows: one split on an odd ring, several on a paged pool
+                                                  ("fp32", "ring", 33, 16, 64), ("fp32", "paged", 1024, 17, 128)])
 def test_mixed_operation_fuzz(kind, layout, W, seed, D):
     import sliding_window_attention_ring_amd as swa
     rng = np.random.default_rng(seed)
     g = torch.Generator().manual_seed(seed)
     B, H = 3, 2
     cache = swa.KVCache(kind, B, H, D, W, layout=layout)
-    hist_k = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
-    hist_v = [torch.empty((H, 0, D), dtype=torch.bfloat16) for _ in range(B)]
+    dt = torch.float32 if kind == "fp32" else torch.bfloat16  # the cache's input dtype
+    hist_k = [torch.empty((H, 0, D), dtype=dt) for _ in range(B)]
+    hist_v = [torch.empty((H, 0, D), dtype=dt) for _ in range(B)]
 
     def check_outputs(op, q, outs, ns, step):
         """Every (b, h) output (and bound) of a decode or fused step against the oracle."""
@@ -79,8 +82,8 @@ def test_mixed_operation_fuzz(kind, layout, W, seed, D):
         r = rng.random()
         if r < 0.45:  # whole-batch append
             T = max(1, int(rng.choice([1, 1, 1, 2, 15, 16, 17, W - 1, W + 5, 2 * W + 3])))  # T >= 1 (W = 1)
-            k = torch.randn((B, H, T, D), generator=g).to(torch.bfloat16)
-            v = torch.randn((B, H, T, D), generator=g).to(torch.bfloat16)
+            k = torch.randn((B, H, T, D), generator=g).to(dt)
+            v = torch.randn((B, H, T, D), generator=g).to(dt)
             swa.kv_append(cache, k.cuda(), v.cuda())
             for b in range(B):
                 hist_k[b] = torch.cat([hist_k[b], k[b]], dim=1)
@@ -88,16 +91,16 @@ def test_mixed_operation_fuzz(kind, layout, W, seed, D):
         elif r < 0.7:  # one sequence through a view
             b = int(rng.integers(B))
             T = int(rng.integers(1, 2 * W))
-            k = torch.randn((1, H, T, D), generator=g).to(torch.bfloat16)
-            v = torch.randn((1, H, T, D), generator=g).to(torch.bfloat16)
+            k = torch.randn((1, H, T, D), generator=g).to(dt)
+            v = torch.randn((1, H, T, D), generator=g).to(dt)
             swa.kv_append(cache.seq_view(b), k.cuda(), v.cuda())
             hist_k[b] = torch.cat([hist_k[b], k[0]], dim=1)
             hist_v[b] = torch.cat([hist_v[b], v[0]], dim=1)
         elif r < 0.8 and rng.random() < 0.5:  # fused decode step: one token per sequence, then the decode
-            k = torch.randn((B, H, 1, D), generator=g).to(torch.bfloat16)
-            v = torch.randn((B, H, 1, D), generator=g).to(torch.bfloat16)
-            q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
-            if kind == "bf16":
+            k = torch.randn((B, H, 1, D), generator=g).to(dt)
+            v = torch.randn((B, H, 1, D), generator=g).to(dt)
+            q = torch.randn((B, H, D), generator=g).to(dt)
+            if kind in ("bf16", "fp32"):
                 outs = (swa.decode_step(cache, k.cuda(), v.cuda(), q.cuda()),)
             elif kind == "int8":
                 outs = swa.decode_step_int8(cache, k.cuda(), v.cuda(), q.cuda(), want_tv=True)
@@ -129,14 +132,14 @@ def test_mixed_operation_fuzz(kind, layout, W, seed, D):
                     check_dither_store(cache, b, h, f64(hist_k[b][h]), f64(hist_v[b][h]), ns[b])
         else:
             N = max(max(ns), 1)
-            kb = np.zeros((B, H, N, D), dtype=np.uint16)
+            kb = np.zeros((B, H, N, D), dtype=np.float32 if kind == "fp32" else np.uint16)
             vb = np.zeros_like(kb)
             for b in range(B):
                 kb[b, :, :ns[b]] = host_bits(hist_k[b])
                 vb[b, :, :ns[b]] = host_bits(hist_v[b])
             check_ring_rows(cache, kb, vb, np.array(ns))
         if rng.random() < 0.6:  # decode
-            q = torch.randn((B, H, D), generator=g).to(torch.bfloat16)
+            q = torch.randn((B, H, D), generator=g).to(dt)
             if kind == "int8_dither":
                 outs = swa.decode_attn_int8_dither(cache, q.cuda(), delta=1e-3)
             elif kind == "int8":
